@@ -1,0 +1,29 @@
+"""CPU oracle of the MOSS-Image DiT denoising step -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+this package. It is independent of the HIP path: it imports nothing from
+``diffusion_transformer_text_amd`` and shares no kernels, tables, constants or helpers with it.
+
+Parity status of each function (pins in tests/test_oracle_pins.py):
+  bf16_round, from_bf16_bits  pinned: torch's bfloat16 cast (a library routine), hand bit patterns
+  sigmas, slg_active          pinned: closed-form hand fractions, endpoints, "first step at full CFG"
+  time_features               pinned: hand values (sigma 0, t = 500 at k = 0 and k = 64)
+  modulation                  pinned: zero weights, chunk order via scalar brute force
+  patchify, unpatchify        pinned: hand-placed elements, mutual inverse, 4,096 tokens at 1024^2
+  layernorm, ln_modulate      pinned: statistics.pstdev (library), constant and +-a rows
+  rope_angles, apply_rope,    pinned: hand angles (1 rad, 0.02 rad), norm preservation, identity at
+  rope_rows                   (0, 0), relative-position invariance, row/column halves
+  attention                   pinned: scalar brute force, S = 1 -> V, equal keys -> mean(V), a
+                              hand 3:1 softmax split that fixes the 1/sqrt(d) scale
+  block                       pinned: scalar brute-force block on a tiny shape, gate = 0 identity,
+                              taps consistency
+  embed, final_layer,         pinned: all-gates-zero forward equals embed -> final closed form,
+  forward                     skip == zeroed gate rows (bitwise), per-sample independence
+  cfg_combine, euler_step,    pinned: CFG identities, telescoping under constant v, point-mass field
+  sample_step                 lands exactly on x*, cfg = 1 runs no negative pass
+"""
+from .moss_oracle import *  # noqa: F401,F403
+from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, embed, euler_step,  # noqa
+                          final_layer, forward, from_bf16_bits, layernorm, ln_modulate, modulation,
+                          patchify, rope_angles, apply_rope, rope_rows, sample_step, sigmas, silu,
+                          slg_active, time_features, unpatchify, weights_to_f64)

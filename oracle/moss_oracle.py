@@ -1,0 +1,407 @@
+"""CPU oracle of one MOSS-Image denoising step (single-stream DiT + FP32 CFG/SLG + Euler).
+
+TEST INFRASTRUCTURE ONLY. Only the test-suite, the package's smoke check and the benchmark's
+``cpu_baseline`` leg may import this module. The product path never calls it and shares no code with
+it: this file imports nothing but numpy.
+
+Plain, slow and obviously correct: numpy float64, one step of the method after another, in the
+pages' order and notation. A library matmul/exp serves as a step; nothing is blocked, fused or
+reordered. ``mirror_bf16=True`` rounds (float64 -> float32 -> bfloat16, round-to-nearest-even) at the
+points where a bf16 DiT stores a tensor between operations; everything else stays float64.
+
+Pages (titles as published):
+  [SG]  "MOSS-Image" -- SGLang diffusion cookbook, section 3 "Guidance and precision".
+  [WP]  "MOSS-Image: specs, settings, VRAM and text rendering tested" -- sections "Architecture and
+        specs" and "Recommended settings".
+  [IV]  InvokeAI user guide "MOSS-Image" -- sections "Transformer formats", "Generation settings",
+        "Skip layers".
+  [QI]  "Qwen-Image 2.1" -- SGLang cookbook, sections "Lossless RoPE fusion", "Lossless MLP and
+        residual fusion", "Lossless LayerNorm modulation" (fused-op idioms of a single-stream DiT).
+
+Where the pages leave a step open the plainest reading is taken; each such reading is named at the
+function that makes it. Pins: every function here is checked in tests/test_oracle_pins.py against
+closed forms, hand values, library routines, invariants and an independent scalar brute force.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence, Set
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------------------------
+# numbers and rounding
+# ----------------------------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """float64 -> float32 (RNE) -> bfloat16 (RNE), returned as float64 values.
+
+    The bf16 DiT keeps weights and activations in bfloat16 while latents, guidance and the scheduler
+    stay float32 ([SG] "Guidance and precision")."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(x32), np.nan, out)
+
+
+def from_bf16_bits(bits) -> np.ndarray:
+    """uint16 bfloat16 bit patterns -> float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _store(x, mirror: bool):
+    return bf16_round(x) if mirror else np.asarray(x, dtype=np.float64)
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+# ----------------------------------------------------------------------------------------------
+# configuration
+# ----------------------------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Config:
+    """[WP] "Architecture and specs": 42 joint blocks, hidden 3072, 24 heads of 128, FFN 8192,
+    32 latent channels, 2x2 latent patches. temb_dim, rope_theta, norm_eps and flow_multiplier are
+    readings (the pages do not give them)."""
+    num_layers: int = 42
+    hidden: int = 3072
+    num_heads: int = 24
+    head_dim: int = 128
+    ffn_hidden: int = 8192
+    latent_channels: int = 32
+    patch: int = 2
+    temb_dim: int = 256
+    rope_theta: float = 1.0e4
+    norm_eps: float = 1.0e-6
+    flow_multiplier: float = 1000.0
+
+    @property
+    def patch_dim(self) -> int:
+        return self.latent_channels * self.patch * self.patch
+
+
+# ----------------------------------------------------------------------------------------------
+# A1  sigma schedule and skip-layer-guidance window
+# ----------------------------------------------------------------------------------------------
+
+def sigmas(num_steps: int, shift: float = 5.0) -> np.ndarray:
+    """Flow-matching Euler schedule with shift ([SG] "Guidance and precision": 50 steps, flow shift 5;
+    [IV] "Generation settings": the model's own Euler schedule).
+
+    s_i = (N - i)/N for i = 0..N, sigma_i = shift*s_i / (1 + (shift-1)*s_i); sigma_0 = 1, sigma_N = 0.
+    Reading: the grid is uniform in s and computed as a ratio, not by accumulating a step."""
+    if num_steps < 1:
+        raise ValueError("num_steps must be >= 1")
+    s = np.array([(num_steps - i) / num_steps for i in range(num_steps + 1)], dtype=np.float64)
+    return shift * s / (1.0 + (shift - 1.0) * s)
+
+
+def slg_active(step: int, num_steps: int, slg_start: float = 0.01, slg_stop: float = 1.0) -> bool:
+    """Whether the unconditional pass skips its layers at this step ([SG] "Guidance and precision":
+    the window slg_start=0.01 .. slg_stop=1.0 leaves the first step at full CFG; slg_start=0.0 starts
+    at zero). Reading: progress p = step/num_steps, inclusive at both ends."""
+    p = step / num_steps
+    return slg_start <= p <= slg_stop
+
+
+# ----------------------------------------------------------------------------------------------
+# A2  timestep embedding and modulation
+# ----------------------------------------------------------------------------------------------
+
+def time_features(sigma: float, cfg: Config) -> np.ndarray:
+    """Sinusoidal features of t = flow_multiplier*sigma: e = [cos(t f_k) | sin(t f_k)], k = 0..127,
+    f_k = exp(-ln(1e4) k / 128). Reading (the pages name a flow multiplier but no embedding)."""
+    half = cfg.temb_dim // 2
+    t = cfg.flow_multiplier * float(sigma)
+    f = np.exp(-math.log(1.0e4) * np.arange(half, dtype=np.float64) / half)
+    return np.concatenate([np.cos(t * f), np.sin(t * f)])
+
+
+def modulation(sigma: float, W: Dict, cfg: Config, mirror: bool = False):
+    """Time MLP and per-block modulation ([IV] "Transformer formats" lists the time-embedding and
+    modulation layers). Reading: temb = W_t2 SiLU(W_t1 e), u = SiLU(temb); block l gets
+    m_l = W_mod,l u = (shift1, scale1, gate1, shift2, scale2, gate2), each of size D; the final layer
+    gets m_f = W_fmod u = (shift_f, scale_f). No biases anywhere (the pages mention none).
+
+    Returns (m [L, 6, D], m_f [2, D])."""
+    D = cfg.hidden
+    e = _store(time_features(sigma, cfg), mirror)
+    a1 = _store(silu(W["t_w1"] @ e), mirror)
+    temb = _store(W["t_w2"] @ a1, mirror)
+    u = _store(silu(temb), mirror)
+    m = np.stack([_store(W["mod_w"][l] @ u, mirror).reshape(6, D) for l in range(cfg.num_layers)])
+    m_f = _store(W["final_mod_w"] @ u, mirror).reshape(2, D)
+    return m, m_f
+
+
+# ----------------------------------------------------------------------------------------------
+# A3 / A11  patchify, unpatchify
+# ----------------------------------------------------------------------------------------------
+
+def patchify(latent: np.ndarray, p: int = 2) -> np.ndarray:
+    """[C, h, w] -> [N, C*p*p]: 2x2 latent patches, one token per 16x16 pixels ([WP] "Architecture and
+    specs"). Token n = r*(w/p) + c for grid cell (r, c), row-major; feature j = ch*p*p + dy*p + dx
+    holds latent[ch, p*r+dy, p*c+dx] (reading: channel-major within a patch)."""
+    C, h, w = latent.shape
+    gh, gw = h // p, w // p
+    out = np.zeros((gh * gw, C * p * p), dtype=np.float64)
+    for r in range(gh):
+        for c in range(gw):
+            n = r * gw + c
+            for ch in range(C):
+                for dy in range(p):
+                    for dx in range(p):
+                        out[n, ch * p * p + dy * p + dx] = latent[ch, p * r + dy, p * c + dx]
+    return out
+
+
+def unpatchify(tokens: np.ndarray, C: int, h: int, w: int, p: int = 2) -> np.ndarray:
+    """Inverse of :func:`patchify`: [N, C*p*p] -> [C, h, w]."""
+    gw = w // p
+    out = np.zeros((C, h, w), dtype=np.float64)
+    for n in range(tokens.shape[0]):
+        r, c = divmod(n, gw)
+        for ch in range(C):
+            for dy in range(p):
+                for dx in range(p):
+                    out[ch, p * r + dy, p * c + dx] = tokens[n, ch * p * p + dy * p + dx]
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# A4 / A8  LayerNorm + modulation
+# ----------------------------------------------------------------------------------------------
+
+def layernorm(x: np.ndarray, eps: float) -> np.ndarray:
+    """Affine-free LayerNorm over the last axis: (x - mean) / sqrt(var + eps), population variance
+    ([QI] "Lossless LayerNorm modulation" describes this affine-free form)."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def ln_modulate(x: np.ndarray, shift: np.ndarray, scale: np.ndarray, eps: float) -> np.ndarray:
+    """LN(x) * (1 + scale) + shift."""
+    return layernorm(x, eps) * (1.0 + scale) + shift
+
+
+# ----------------------------------------------------------------------------------------------
+# RoPE (inside A6)
+# ----------------------------------------------------------------------------------------------
+
+def rope_angles(pos_r: int, pos_c: int, head_dim: int, theta: float) -> np.ndarray:
+    """Angles of the 2-D axial rotary embedding for image token (pos_r, pos_c): dims [0, d/2) use the
+    grid row, dims [d/2, d) the grid column; within each half, pair (2k, 2k+1), k = 0..d/4-1, turns by
+    pos * theta^(-k/(d/4)). Reading (the pages name a complex rotary multiplication, [QI] "Lossless
+    RoPE fusion", and the attention workload ropes image positions of a 64x64 grid)."""
+    quarter = head_dim // 4
+    k = np.arange(quarter, dtype=np.float64)
+    inv = theta ** (-k / quarter)
+    return np.concatenate([pos_r * inv, pos_c * inv])          # [d/2] angles, pair index order
+
+
+def apply_rope(v: np.ndarray, angles: np.ndarray) -> np.ndarray:
+    """Rotate interleaved pairs (v[2k], v[2k+1]) by angles[k]."""
+    out = v.astype(np.float64).copy()
+    a = v[..., 0::2]
+    b = v[..., 1::2]
+    cs, sn = np.cos(angles), np.sin(angles)
+    out[..., 0::2] = a * cs - b * sn
+    out[..., 1::2] = a * sn + b * cs
+    return out
+
+
+def rope_rows(x: np.ndarray, text_len: int, grid_w: int, head_dim: int, theta: float,
+              rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Apply RoPE per head to the image rows of x [S, H*d]; text rows (the first text_len) stay as
+    they are. ``rows`` gives the sequence index of each row of x (default: 0..S-1)."""
+    S, HD = x.shape
+    H = HD // head_dim
+    rows = range(S) if rows is None else rows
+    out = x.astype(np.float64).copy()
+    for i, s in enumerate(rows):
+        if s < text_len:
+            continue
+        pr, pc = divmod(s - text_len, grid_w)
+        ang = rope_angles(pr, pc, head_dim, theta)
+        for h in range(H):
+            sl = slice(h * head_dim, (h + 1) * head_dim)
+            out[i, sl] = apply_rope(x[i, sl], ang)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# A6  attention
+# ----------------------------------------------------------------------------------------------
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, num_heads: int, head_dim: int) -> np.ndarray:
+    """Exact softmax attention per head over all keys, no mask, scale 1/sqrt(d) ([WP] "Architecture
+    and specs": single-stream joint blocks attend over text and image tokens together).
+    q [Sq, H*d], k/v [Sk, H*d] -> [Sq, H*d]."""
+    out = np.zeros((q.shape[0], num_heads * head_dim), dtype=np.float64)
+    scale = 1.0 / math.sqrt(head_dim)
+    for h in range(num_heads):
+        sl = slice(h * head_dim, (h + 1) * head_dim)
+        s = (q[:, sl] @ k[:, sl].T) * scale
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        out[:, sl] = (p @ v[:, sl]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# A4..A10  one joint block
+# ----------------------------------------------------------------------------------------------
+
+def block(x: np.ndarray, m: np.ndarray, W: Dict, l: int, cfg: Config, text_len: int, grid_w: int,
+          mirror: bool = False, rows: Optional[Sequence[int]] = None, taps: Optional[Dict] = None):
+    """One single-stream joint block on one sample ([WP] "Architecture and specs").
+
+    x [S, D] (the residual stream, bf16 values), m [6, D] = (shift1, scale1, gate1, shift2, scale2,
+    gate2). Reading: pre-norm; attention branch then SwiGLU FFN branch, each gated into the residual:
+        A  = LN(x)(1+scale1) + shift1;  [Q|K|V] = A W_qkv^T;  RoPE on image rows of Q, K
+        x += gate1 * (softmax(Q K^T/sqrt d) V) W_o^T
+        A2 = LN(x)(1+scale2) + shift2;  x += gate2 * (SiLU(A2 W_g^T) * (A2 W_u^T)) W_down^T
+    with W_qkv rows [q | k | v] ([IV] "Transformer formats": a fused qkv weight splits into three)
+    and W_gate_up rows [gate | up]. FFN width 8192 = 8/3 of 3072 reads as SwiGLU.
+
+    ``rows``: compute only these output rows (K and V still use every row). Returns x' for those rows.
+    ``taps``: dict that receives the branch outputs before the residual add (fp64, for tests)."""
+    D, F, H, d = cfg.hidden, cfg.ffn_hidden, cfg.num_heads, cfg.head_dim
+    eps, theta = cfg.norm_eps, cfg.rope_theta
+    S = x.shape[0]
+    rows = list(range(S)) if rows is None else list(rows)
+    shift1, scale1, gate1, shift2, scale2, gate2 = m
+    r = lambda t: _store(t, mirror)
+
+    a_all = r(ln_modulate(x, shift1, scale1, eps))
+    wqkv = W["qkv_w"][l]
+    kv = r(a_all @ wqkv[D:3 * D].T)                      # K | V for every row
+    k_all = r(rope_rows(kv[:, :D], text_len, grid_w, d, theta))
+    v_all = kv[:, D:]
+    q = r(a_all[rows] @ wqkv[:D].T)
+    q = r(rope_rows(q, text_len, grid_w, d, theta, rows=rows))
+    o = r(attention(q, k_all, v_all, H, d))
+    attn_out = o @ W["out_w"][l].T
+    x1 = r(x[rows] + gate1 * attn_out)
+    a2 = r(ln_modulate(x1, shift2, scale2, eps))
+    wgu = W["gate_up_w"][l]
+    g = a2 @ wgu[:F].T
+    u = a2 @ wgu[F:].T
+    hf = r(silu(g) * u)
+    ffn_out = hf @ W["down_w"][l].T
+    x2 = r(x1 + gate2 * ffn_out)
+    if taps is not None:
+        taps.update(dict(a=a_all[rows], q=q, k=k_all, v=v_all, o=o, attn_out=attn_out, x1=x1,
+                         a2=a2, h=hf, ffn_out=ffn_out))
+    return x2
+
+
+# ----------------------------------------------------------------------------------------------
+# A3..A11  one DiT forward
+# ----------------------------------------------------------------------------------------------
+
+def embed(latent: np.ndarray, text: np.ndarray, W: Dict, cfg: Config, mirror: bool = False):
+    """Sequence [text (T rows) | image tokens (N rows)] of one sample. text [T, D] stands in for the
+    text refiner's output; the image tokens are patch features times W_x^T (no bias)."""
+    p = _store(patchify(latent, cfg.patch), mirror)
+    z = _store(p @ W["x_embed_w"].T, mirror)
+    return np.concatenate([_store(text, mirror), z], axis=0)
+
+
+def final_layer(x_img: np.ndarray, m_f: np.ndarray, W: Dict, cfg: Config, mirror: bool = False):
+    """Image rows only: Y = (LN(x)(1+scale_f) + shift_f) W_f^T, kept in float32/64 (latents are FP32,
+    [SG] "Guidance and precision"). Returns Y [N, C*p*p]."""
+    shift_f, scale_f = m_f
+    a = _store(ln_modulate(x_img, shift_f, scale_f, cfg.norm_eps), mirror)
+    return a @ W["final_w"].T
+
+
+def forward(latents: np.ndarray, text: np.ndarray, sigma: Sequence[float], W: Dict, cfg: Config,
+            skip: Optional[Sequence[Set[int]]] = None, mirror: bool = False,
+            taps: Optional[List] = None) -> np.ndarray:
+    """DiT velocity for a batch. latents [B, C, h, w], text [B, T, D], sigma [B]; skip[b] = the
+    blocks sample b leaves out ([IV] "Skip layers": the listed blocks are skipped by that pass, which
+    reads as the identity on that sample's residual stream). Returns v [B, C, h, w] (float64)."""
+    B, C, h, w = latents.shape
+    T = text.shape[1]
+    gw = w // cfg.patch
+    skip = [set() for _ in range(B)] if skip is None else [set(s) for s in skip]
+    out = np.zeros((B, C, h, w), dtype=np.float64)
+    for b in range(B):
+        m, m_f = modulation(sigma[b], W, cfg, mirror)
+        x = embed(latents[b], text[b], W, cfg, mirror)
+        per_layer = []
+        for l in range(cfg.num_layers):
+            if l in skip[b]:
+                per_layer.append(None)
+                continue
+            x = block(x, m[l], W, l, cfg, T, gw, mirror)
+            per_layer.append(x)
+        y = final_layer(x[T:], m_f, W, cfg, mirror)
+        out[b] = unpatchify(y, C, h, w, cfg.patch)
+        if taps is not None:
+            taps.append(per_layer)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# A12  guidance and Euler
+# ----------------------------------------------------------------------------------------------
+
+def cfg_combine(v_cond: np.ndarray, v_uncond: Optional[np.ndarray], cfg_scale: float) -> np.ndarray:
+    """Classifier-free guidance as the ordinary linear combination ([QI] "5. Runtime features" names
+    it for a sibling single-stream DiT): v = v_u + cfg (v_c - v_u). CFG 1 turns guidance off and
+    runs no negative pass ([IV] "Generation settings"), so v = v_c exactly; CFG < 1 is refused."""
+    if cfg_scale < 1.0:
+        raise ValueError("CFG scale below 1 is not accepted")
+    if cfg_scale == 1.0:
+        return np.asarray(v_cond, dtype=np.float64)
+    return v_uncond + cfg_scale * (v_cond - v_uncond)
+
+
+def euler_step(x: np.ndarray, v: np.ndarray, sigma: float, sigma_next: float) -> np.ndarray:
+    """Flow-matching Euler update x_{i+1} = x_i + (sigma_{i+1} - sigma_i) v."""
+    return x + (sigma_next - sigma) * v
+
+
+def sample_step(x: np.ndarray, text_cond: np.ndarray, text_uncond: Optional[np.ndarray], W: Dict,
+                cfg: Config, step: int, sigma_table: np.ndarray, cfg_scale: float = 3.0,
+                uncond_skip_layers: Sequence[int] = (22,), slg_start: float = 0.01,
+                slg_stop: float = 1.0, mirror: bool = False, velocities: Optional[List] = None):
+    """One denoising step: DiT(cond), DiT(uncond, skipping uncond_skip_layers inside the SLG window),
+    CFG combine, Euler. x [1, C, h, w]. The negative pass runs only when CFG > 1 ([IV] "Skip layers":
+    the setting has no effect at CFG 1)."""
+    N = len(sigma_table) - 1
+    s, s_next = float(sigma_table[step]), float(sigma_table[step + 1])
+    if cfg_scale == 1.0:
+        v_c = forward(x, text_cond, [s], W, cfg, mirror=mirror)
+        v = cfg_combine(v_c, None, 1.0)
+        v_u = None
+    else:
+        skip_u = set(uncond_skip_layers) if slg_active(step, N, slg_start, slg_stop) else set()
+        lat = np.concatenate([x, x], axis=0)
+        txt = np.concatenate([text_cond, text_uncond], axis=0)
+        vv = forward(lat, txt, [s, s], W, cfg, skip=[set(), skip_u], mirror=mirror)
+        v_c, v_u = vv[0:1], vv[1:2]
+        v = cfg_combine(v_c, v_u, cfg_scale)
+    if velocities is not None:
+        velocities.append((v_c, v_u))
+    return euler_step(x, v, s, s_next)
+
+
+def weights_to_f64(w) -> Dict:
+    """bf16 bit-pattern weights (an object with the C ABI's field names) -> float64 arrays."""
+    get = (lambda k: w[k]) if isinstance(w, dict) else (lambda k: getattr(w, k))
+    out = {k: from_bf16_bits(get(k)) for k in ("t_w1", "t_w2", "x_embed_w", "final_mod_w", "final_w")}
+    for k in ("mod_w", "qkv_w", "out_w", "gate_up_w", "down_w"):
+        out[k] = [from_bf16_bits(a) for a in get(k)]
+    return out

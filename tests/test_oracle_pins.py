@@ -1,0 +1,496 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (runs without a GPU).
+
+Each test names the passage or the mathematical fact it checks. The brute-force references below are
+scalar Python loops written from the definition, not calls of the oracle's own routines, so a dropped
+term, a wrong sign or index, or a transposed operand in the oracle fails one of them.
+"""
+import json
+import math
+import os
+import statistics
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------------------------------------
+# bfloat16 rounding
+# ------------------------------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1.0, -1.0, 65504.0, 3.0e38, 1e-40, -1e-42]])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_round(x32), ref)
+
+
+def test_bf16_round_hand_ties():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa wins -> 1.
+    assert O.bf16_round(1.0 + 2.0 ** -8) == 1.0
+    # 1 + 3*2^-8 is a tie between 1 + 2^-7 (odd) and 1 + 2^-6 (even) -> 1 + 2^-6.
+    assert O.bf16_round(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert O.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert O.from_bf16_bits(np.array([0x3F80, 0xC000, 0x0000], dtype=np.uint16)).tolist() == [1.0, -2.0, 0.0]
+
+
+# ------------------------------------------------------------------------------------------------
+# A1: schedule and SLG window
+# ------------------------------------------------------------------------------------------------
+
+def test_sigmas_hand_fractions_shift5():
+    # sigma = 5 s / (1 + 4 s) on s = 1, 3/4, 1/2, 1/4, 0 (fractions worked by hand)
+    np.testing.assert_allclose(O.sigmas(4, 5.0), [1.0, 15 / 16, 5 / 6, 5 / 8, 0.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.sigmas(2, 5.0), [1.0, 5 / 6, 0.0], rtol=0, atol=1e-15)
+
+
+def test_sigmas_endpoints_monotone_and_shift1_linear():
+    g = golden()["defaults"]
+    s = O.sigmas(g["num_steps"], g["shift"])
+    assert len(s) == g["num_steps"] + 1 and s[0] == 1.0 and s[-1] == 0.0
+    assert np.all(np.diff(s) < 0)
+    np.testing.assert_allclose(O.sigmas(10, 1.0), np.linspace(1, 0, 11), atol=1e-15)
+    # the shift only warps time: s recovered by the inverse map is the uniform grid
+    s_back = s / (g["shift"] - (g["shift"] - 1) * s)
+    np.testing.assert_allclose(s_back, np.linspace(1, 0, g["num_steps"] + 1), atol=1e-14)
+
+
+def test_slg_window_first_step_full_cfg():
+    # "skips unconditional layer 22 inside the slg_start=0.01, slg_stop=1.0 window. It leaves the first
+    # step at full CFG"; "set slg_start=0.0 ... for the start-at-zero behavior" (SGLang cookbook, 3).
+    g = golden()["defaults"]
+    N = g["num_steps"]
+    active = [i for i in range(N) if O.slg_active(i, N, g["slg_start"], g["slg_stop"])]
+    assert active == list(range(1, N))
+    assert [i for i in range(N) if O.slg_active(i, N, 0.0, 1.0)] == list(range(N))
+    assert [O.slg_active(i, 2) for i in range(2)] == [False, True]
+
+
+# ------------------------------------------------------------------------------------------------
+# A12: guidance and Euler
+# ------------------------------------------------------------------------------------------------
+
+def test_cfg_identities():
+    rng = np.random.default_rng(2)
+    vc, vu = rng.standard_normal(100), rng.standard_normal(100)
+    np.testing.assert_array_equal(O.cfg_combine(vc, vu, 1.0), vc)
+    np.testing.assert_array_equal(O.cfg_combine(vc, vc, 4.5), vc)
+    np.testing.assert_allclose(O.cfg_combine(vc, vu, 3.0), 3 * vc - 2 * vu, atol=1e-14)
+    with pytest.raises(ValueError):
+        O.cfg_combine(vc, vu, 0.5)
+
+
+def test_euler_constant_velocity_telescopes():
+    sig = O.sigmas(50, 5.0)
+    rng = np.random.default_rng(3)
+    x0, v = rng.standard_normal(64), rng.standard_normal(64)
+    x = x0.copy()
+    for i in range(50):
+        x = O.euler_step(x, v, sig[i], sig[i + 1])
+    np.testing.assert_allclose(x, x0 - v, atol=1e-12)
+
+
+def test_euler_point_mass_field_lands_on_target():
+    # v(x, sigma) = (x - x*)/sigma gives x_{i+1} - x* = (x_i - x*) sigma_{i+1}/sigma_i -> x_N = x*.
+    sig = O.sigmas(50, 5.0)
+    rng = np.random.default_rng(4)
+    xs, x = rng.standard_normal(64), rng.standard_normal(64)
+    x_mid = None
+    for i in range(50):
+        x = O.euler_step(x, (x - xs) / sig[i], sig[i], sig[i + 1])
+        if i == 24:
+            x_mid = x.copy()
+    np.testing.assert_allclose(x, xs, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------
+# A2: time features and modulation
+# ------------------------------------------------------------------------------------------------
+
+def test_time_features_hand_values():
+    cfg = O.Config()
+    e0 = O.time_features(0.0, cfg)
+    np.testing.assert_array_equal(e0, [1.0] * 128 + [0.0] * 128)
+    e = O.time_features(0.5, cfg)           # t = 1000 * 0.5 = 500
+    assert e[0] == pytest.approx(math.cos(500.0), abs=1e-12)
+    assert e[128] == pytest.approx(math.sin(500.0), abs=1e-12)
+    # k = 64 -> f = 10^4^(-1/2) = 0.01 -> angle 5
+    assert e[64] == pytest.approx(math.cos(5.0), abs=1e-12)
+    assert e[192] == pytest.approx(math.sin(5.0), abs=1e-12)
+
+
+def test_modulation_chunk_order_scalar_bruteforce():
+    cfg = O.Config(num_layers=2, hidden=8, temb_dim=256)
+    rng = np.random.default_rng(5)
+    W = {"t_w1": rng.standard_normal((256, 256)) * 0.05, "t_w2": rng.standard_normal((256, 256)) * 0.05,
+         "mod_w": [rng.standard_normal((48, 256)) for _ in range(2)], "final_mod_w": rng.standard_normal((16, 256))}
+    sigma = 0.3
+    m, mf = O.modulation(sigma, W, cfg)
+    # scalar re-derivation
+    t = 1000.0 * sigma
+    e = [math.cos(t * math.exp(-math.log(1e4) * k / 128)) for k in range(128)] + \
+        [math.sin(t * math.exp(-math.log(1e4) * k / 128)) for k in range(128)]
+    sl = lambda z: z / (1 + math.exp(-z))
+    a1 = [sl(sum(W["t_w1"][i][j] * e[j] for j in range(256))) for i in range(256)]
+    temb = [sum(W["t_w2"][i][j] * a1[j] for j in range(256)) for i in range(256)]
+    u = [sl(z) for z in temb]
+    for l in range(2):
+        for chunk in range(6):
+            for dd in range(8):
+                row = chunk * 8 + dd
+                ref = sum(W["mod_w"][l][row][j] * u[j] for j in range(256))
+                assert m[l, chunk, dd] == pytest.approx(ref, rel=1e-10, abs=1e-12)
+    assert mf[1, 3] == pytest.approx(sum(W["final_mod_w"][8 + 3][j] * u[j] for j in range(256)), rel=1e-10)
+
+
+# ------------------------------------------------------------------------------------------------
+# A3 / A11: patchify
+# ------------------------------------------------------------------------------------------------
+
+def test_patchify_hand_element_and_inverse():
+    lat = np.zeros((32, 6, 8))
+    lat[3, 5, 2] = 1.0          # grid (r, c) = (2, 1), (dy, dx) = (1, 0) -> n = 2*4 + 1, j = 3*4 + 2
+    tok = O.patchify(lat)
+    assert tok.shape == (12, 128)
+    assert tok[9, 14] == 1.0 and tok.sum() == 1.0
+    rng = np.random.default_rng(6)
+    lat = rng.standard_normal((32, 6, 8))
+    np.testing.assert_array_equal(O.unpatchify(O.patchify(lat), 32, 6, 8), lat)
+
+
+def test_token_count_at_1024():
+    g = golden()["architecture"]
+    side = 1024 // g["vae_downsample"]                       # latent side 128
+    assert (side // g["patch"]) ** 2 == g["image_tokens_at_1024"]
+    assert g["vae_downsample"] * g["patch"] == g["pixels_per_token_side"]
+
+
+# ------------------------------------------------------------------------------------------------
+# A4 / A8: LayerNorm modulation
+# ------------------------------------------------------------------------------------------------
+
+def test_layernorm_against_statistics_module():
+    rng = np.random.default_rng(7)
+    row = rng.standard_normal(3072) * 3 + 1.5
+    mu, var = statistics.fmean(row), statistics.pvariance(row)
+    ref = [(v - mu) / math.sqrt(var + 1e-6) for v in row]
+    np.testing.assert_allclose(O.layernorm(row[None], 1e-6)[0], ref, atol=1e-12)
+
+
+def test_ln_modulate_special_rows():
+    D = 64
+    rng = np.random.default_rng(8)
+    shift, scale = rng.standard_normal(D), rng.standard_normal(D)
+    np.testing.assert_allclose(O.ln_modulate(np.full((1, D), 2.5), shift, scale, 1e-6)[0], shift, atol=1e-12)
+    np.testing.assert_allclose(O.ln_modulate(np.zeros((1, D)), shift, scale, 1e-6)[0], shift, atol=1e-12)
+    a = 3.0
+    row = np.array([a, -a] * (D // 2))
+    n = a / math.sqrt(a * a + 1e-6)
+    ref = np.array([n, -n] * (D // 2)) * (1 + scale) + shift
+    np.testing.assert_allclose(O.ln_modulate(row[None], shift, scale, 1e-6)[0], ref, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------
+# RoPE
+# ------------------------------------------------------------------------------------------------
+
+def test_rope_hand_angles():
+    a = O.rope_angles(1, 0, 128, 1e4)
+    assert a.shape == (64,) and a[0] == 1.0 and a[32] == 0.0
+    assert O.rope_angles(2, 0, 128, 1e4)[16] == pytest.approx(0.02, rel=1e-14)   # 2 * 1e4^(-1/2)
+    assert O.rope_angles(0, 3, 128, 1e4)[32 + 8] == pytest.approx(0.3, rel=1e-14)  # 3 * 1e4^(-1/4)
+
+
+def test_rope_rows_rotates_right_halves():
+    d = 128
+    x = np.zeros((3, 2 * d))
+    x[:, 0] = 1.0            # head 0, dim 0 (row half)
+    x[:, 64] = 1.0           # head 0, dim 64 (column half)
+    x[:, d + 65] = 1.0       # head 1, dim 65 (column half, odd element)
+    # sequence: 1 text row, then image tokens at (0,0) and (0,1) on a 2-wide grid
+    y = O.rope_rows(x, text_len=1, grid_w=2, head_dim=d, theta=1e4)
+    np.testing.assert_array_equal(y[0], x[0])                 # text row untouched
+    np.testing.assert_array_equal(y[1], x[1])                 # position (0,0) is the identity
+    c, s = math.cos(1.0), math.sin(1.0)
+    assert y[2, 0] == 1.0 and y[2, 1] == 0.0                  # row position 0: dims 0,1 fixed
+    assert y[2, 64] == pytest.approx(c) and y[2, 65] == pytest.approx(s)
+    assert y[2, d + 64] == pytest.approx(-s) and y[2, d + 65] == pytest.approx(c)
+
+
+def test_rope_preserves_norm_and_relative_positions():
+    rng = np.random.default_rng(9)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    ang = lambda r, c: O.rope_angles(r, c, 128, 1e4)
+    qr = O.apply_rope(q, ang(5, 7))
+    assert np.linalg.norm(qr) == pytest.approx(np.linalg.norm(q), rel=1e-13)
+    s1 = O.apply_rope(q, ang(5, 7)) @ O.apply_rope(k, ang(2, 30))
+    s2 = O.apply_rope(q, ang(5 + 11, 7 + 4)) @ O.apply_rope(k, ang(2 + 11, 30 + 4))
+    assert s1 == pytest.approx(s2, rel=1e-10)
+    s3 = O.apply_rope(q, ang(5, 8)) @ O.apply_rope(k, ang(2, 30))
+    assert abs(s3 - s1) > 1e-6
+
+
+# ------------------------------------------------------------------------------------------------
+# A6: attention
+# ------------------------------------------------------------------------------------------------
+
+def _attn_bruteforce(q, k, v, H, d):
+    Sq, Sk = len(q), len(k)
+    out = [[0.0] * (H * d) for _ in range(Sq)]
+    for h in range(H):
+        base = h * d
+        for i in range(Sq):
+            sc = [sum(q[i][base + t] * k[j][base + t] for t in range(d)) / math.sqrt(d) for j in range(Sk)]
+            mx = max(sc)
+            w = [math.exp(s - mx) for s in sc]
+            z = sum(w)
+            for t in range(d):
+                out[i][base + t] = sum(w[j] * v[j][base + t] for j in range(Sk)) / z
+    return np.array(out)
+
+
+@pytest.mark.parametrize("S,H", [(1, 1), (7, 2), (12, 1)])
+def test_attention_vs_scalar_bruteforce(S, H):
+    rng = np.random.default_rng(10 + S)
+    q, k, v = (rng.standard_normal((S, H * 128)) for _ in range(3))
+    np.testing.assert_allclose(O.attention(q, k, v, H, 128), _attn_bruteforce(q.tolist(), k.tolist(), v.tolist(), H, 128),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((1, 256))
+    np.testing.assert_allclose(O.attention(rng.standard_normal((3, 256)), rng.standard_normal((1, 256)), v, 2, 128),
+                               np.repeat(v, 3, axis=0), atol=1e-14)
+    k = np.repeat(rng.standard_normal((1, 128)), 5, axis=0)
+    v = rng.standard_normal((5, 128))
+    np.testing.assert_allclose(O.attention(rng.standard_normal((2, 128)), k, v, 1, 128),
+                               np.repeat(v.mean(0, keepdims=True), 2, axis=0), atol=1e-13)
+    # hand 3:1 split: scores ln 3 and 0 after the 1/sqrt(128) scale
+    q = np.zeros((1, 128)); q[0, 0] = math.sqrt(128) * math.log(3.0)
+    k = np.zeros((2, 128)); k[0, 0] = 1.0
+    v = rng.standard_normal((2, 128))
+    np.testing.assert_allclose(O.attention(q, k, v, 1, 128)[0], 0.75 * v[0] + 0.25 * v[1], atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------------------
+# A4..A10: one block, against a scalar brute force
+# ------------------------------------------------------------------------------------------------
+
+def _block_bruteforce(x, m, Wqkv, Wo, Wgu, Wd, T, gw, D, H, d, F, eps, theta):
+    S = len(x)
+    sl = lambda z: z / (1 + math.exp(-z))
+
+    def ln_mod(rowv, sh, sc):
+        mu = sum(rowv) / D
+        var = sum((a - mu) ** 2 for a in rowv) / D
+        return [(rowv[i] - mu) / math.sqrt(var + eps) * (1 + sc[i]) + sh[i] for i in range(D)]
+
+    def lin(vec, Wm, rows, cols):
+        return [sum(Wm[o][i] * vec[i] for i in range(cols)) for o in range(rows)]
+
+    def rope(vec, s):
+        if s < T:
+            return vec
+        pr, pc = divmod(s - T, gw)
+        out = list(vec)
+        for h in range(H):
+            for i in range(0, d, 2):
+                half, pair = divmod(i, d // 2)
+                pos = pr if half == 0 else pc
+                kk = pair // 2
+                phi = pos * theta ** (-kk / (d // 4))
+                a, b = vec[h * d + i], vec[h * d + i + 1]
+                out[h * d + i] = a * math.cos(phi) - b * math.sin(phi)
+                out[h * d + i + 1] = a * math.sin(phi) + b * math.cos(phi)
+        return out
+
+    sh1, sc1, g1, sh2, sc2, g2 = [list(c) for c in m]
+    A = [ln_mod(x[s], sh1, sc1) for s in range(S)]
+    QKV = [lin(A[s], Wqkv, 3 * D, D) for s in range(S)]
+    Q = [rope(QKV[s][:D], s) for s in range(S)]
+    K = [rope(QKV[s][D:2 * D], s) for s in range(S)]
+    V = [QKV[s][2 * D:] for s in range(S)]
+    Oh = _attn_bruteforce(Q, K, V, H, d).tolist()
+    x1 = []
+    for s in range(S):
+        ao = lin(Oh[s], Wo, D, D)
+        x1.append([x[s][i] + g1[i] * ao[i] for i in range(D)])
+    x2 = []
+    for s in range(S):
+        a2 = ln_mod(x1[s], sh2, sc2)
+        gu = lin(a2, Wgu, 2 * F, D)
+        hf = [sl(gu[j]) * gu[F + j] for j in range(F)]
+        fo = lin(hf, Wd, D, F)
+        x2.append([x1[s][i] + g2[i] * fo[i] for i in range(D)])
+    return np.array(x2)
+
+
+def test_block_vs_scalar_bruteforce():
+    H, d, F = 2, 128, 32
+    D = H * d
+    cfg = O.Config(num_layers=1, hidden=D, num_heads=H, head_dim=d, ffn_hidden=F)
+    rng = np.random.default_rng(12)
+    T, gw = 2, 2
+    S = T + 4                                   # 2x2 image grid
+    x = rng.standard_normal((S, D))
+    m = rng.standard_normal((6, D)) * 0.5
+    W = {"qkv_w": [rng.standard_normal((3 * D, D)) * 0.06], "out_w": [rng.standard_normal((D, D)) * 0.06],
+         "gate_up_w": [rng.standard_normal((2 * F, D)) * 0.06], "down_w": [rng.standard_normal((D, F)) * 0.06]}
+    got = O.block(x, m, W, 0, cfg, T, gw)
+    ref = _block_bruteforce(x.tolist(), m.tolist(), W["qkv_w"][0].tolist(), W["out_w"][0].tolist(),
+                            W["gate_up_w"][0].tolist(), W["down_w"][0].tolist(), T, gw, D, H, d, F, 1e-6, 1e4)
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-10)
+    # computing a subset of rows gives the same rows
+    sub = O.block(x, m, W, 0, cfg, T, gw, rows=[1, 4])
+    np.testing.assert_allclose(sub, got[[1, 4]], rtol=1e-12, atol=1e-13)
+
+
+def test_block_zero_gates_is_identity_and_mirror_rounds_residual():
+    H, d, F = 1, 128, 64
+    D = H * d
+    cfg = O.Config(num_layers=1, hidden=D, num_heads=H, head_dim=d, ffn_hidden=F)
+    rng = np.random.default_rng(13)
+    x = O.bf16_round(rng.standard_normal((5, D)))
+    m = rng.standard_normal((6, D))
+    m[2] = 0.0
+    m[5] = 0.0
+    W = {"qkv_w": [rng.standard_normal((3 * D, D)) * 0.05], "out_w": [rng.standard_normal((D, D)) * 0.05],
+         "gate_up_w": [rng.standard_normal((2 * F, D)) * 0.05], "down_w": [rng.standard_normal((D, F)) * 0.05]}
+    np.testing.assert_array_equal(O.block(x, m, W, 0, cfg, 1, 2, mirror=True), x)
+    m[2] = 0.3
+    taps = {}
+    y = O.block(x, m, W, 0, cfg, 1, 2, mirror=True, taps=taps)
+    np.testing.assert_array_equal(O.bf16_round(y), y)
+    np.testing.assert_allclose(taps["x1"], O.bf16_round(x + m[2] * taps["attn_out"]), atol=0)
+
+
+# ------------------------------------------------------------------------------------------------
+# forward and sampling step
+# ------------------------------------------------------------------------------------------------
+
+def _tiny_cfg():
+    return O.Config(num_layers=2, hidden=128, num_heads=1, head_dim=128, ffn_hidden=64)
+
+
+def _tiny_weights(cfg, rng, gate_zero=False):
+    D, F, E, P = cfg.hidden, cfg.ffn_hidden, cfg.temb_dim, cfg.patch_dim
+    W = {"t_w1": rng.standard_normal((E, 256)) * 0.05, "t_w2": rng.standard_normal((E, E)) * 0.05,
+         "x_embed_w": rng.standard_normal((D, P)) * 0.05,
+         "mod_w": [rng.standard_normal((6 * D, E)) for _ in range(cfg.num_layers)],
+         "qkv_w": [rng.standard_normal((3 * D, D)) * 0.05 for _ in range(cfg.num_layers)],
+         "out_w": [rng.standard_normal((D, D)) * 0.05 for _ in range(cfg.num_layers)],
+         "gate_up_w": [rng.standard_normal((2 * F, D)) * 0.05 for _ in range(cfg.num_layers)],
+         "down_w": [rng.standard_normal((D, F)) * 0.05 for _ in range(cfg.num_layers)],
+         "final_mod_w": rng.standard_normal((2 * D, E)), "final_w": rng.standard_normal((P, D)) * 0.05}
+    if gate_zero:
+        for l in range(cfg.num_layers):
+            W["mod_w"][l][2 * D:3 * D] = 0.0
+            W["mod_w"][l][5 * D:6 * D] = 0.0
+    return W
+
+
+def test_forward_with_all_gates_zero_is_embed_then_final_bruteforce():
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(14)
+    W = _tiny_weights(cfg, rng, gate_zero=True)
+    C, h, w, T, D = 32, 4, 4, 3, cfg.hidden
+    lat = rng.standard_normal((1, C, h, w))
+    txt = rng.standard_normal((1, T, D))
+    v = O.forward(lat, txt, [0.7], W, cfg)
+    # scalar brute force of: patch -> embed -> (blocks are identities) -> LN-mod final -> W_f -> place
+    _, mf = O.modulation(0.7, W, cfg)
+    ref = np.zeros((C, h, w))
+    for r in range(h // 2):
+        for c in range(w // 2):
+            feat = [lat[0, ch, 2 * r + dy, 2 * c + dx] for ch in range(C) for dy in range(2) for dx in range(2)]
+            z = [sum(W["x_embed_w"][o][j] * feat[j] for j in range(128)) for o in range(D)]
+            mu = sum(z) / D
+            var = sum((a - mu) ** 2 for a in z) / D
+            a = [(z[i] - mu) / math.sqrt(var + 1e-6) * (1 + mf[1][i]) + mf[0][i] for i in range(D)]
+            y = [sum(W["final_w"][o][i] * a[i] for i in range(D)) for o in range(128)]
+            for ch in range(C):
+                for dy in range(2):
+                    for dx in range(2):
+                        ref[ch, 2 * r + dy, 2 * c + dx] = y[ch * 4 + dy * 2 + dx]
+    np.testing.assert_allclose(v[0], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_skip_equals_zeroed_gate_rows_bitwise():
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(15)
+    W = _tiny_weights(cfg, rng)
+    lat = O.bf16_round(rng.standard_normal((1, 32, 4, 4)))
+    txt = rng.standard_normal((1, 3, cfg.hidden))
+    v_skip = O.forward(lat, txt, [0.4], W, cfg, skip=[{1}], mirror=True)
+    W0 = {k: (list(v) if isinstance(v, list) else v) for k, v in W.items()}
+    mw = W["mod_w"][1].copy()
+    mw[2 * cfg.hidden:3 * cfg.hidden] = 0.0
+    mw[5 * cfg.hidden:] = 0.0
+    W0["mod_w"] = [W["mod_w"][0], mw]
+    np.testing.assert_array_equal(O.forward(lat, txt, [0.4], W0, cfg, mirror=True), v_skip)
+    assert not np.array_equal(O.forward(lat, txt, [0.4], W, cfg, mirror=True), v_skip)
+
+
+def test_sample_step_guidance_paths():
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(16)
+    W = _tiny_weights(cfg, rng)
+    x = rng.standard_normal((1, 32, 4, 4))
+    tc = rng.standard_normal((1, 3, cfg.hidden))
+    tu = np.zeros_like(tc)
+    sig = O.sigmas(2, 5.0)
+    # cfg = 1: no negative pass, x1 = x + dsigma * v_c
+    vel = []
+    x1 = O.sample_step(x, tc, None, W, cfg, 0, sig, cfg_scale=1.0, velocities=vel)
+    assert vel[0][1] is None
+    np.testing.assert_array_equal(x1, x + (sig[1] - sig[0]) * O.forward(x, tc, [sig[0]], W, cfg))
+    # step 0 is outside the default window: the skip list does not matter there
+    a = O.sample_step(x, tc, tu, W, cfg, 0, sig, 3.0, (1,))
+    b = O.sample_step(x, tc, tu, W, cfg, 0, sig, 3.0, ())
+    np.testing.assert_array_equal(a, b)
+    # step 1 is inside: skipping block 1 changes the result; [] is ordinary CFG
+    vel = []
+    a = O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, (1,), velocities=vel)
+    vel2 = []
+    b = O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, (), velocities=vel2)
+    assert not np.allclose(a, b)
+    np.testing.assert_array_equal(vel[0][0], vel2[0][0])     # the cond pass never skips
+    v_ref = vel2[0][1] + 3.0 * (vel2[0][0] - vel2[0][1])
+    np.testing.assert_allclose(b, x + (sig[2] - sig[1]) * v_ref, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------------
+# dimension pins (the SwiGLU / shape readings against the pages' printed sizes)
+# ------------------------------------------------------------------------------------------------
+
+def test_page_dimensions():
+    g = golden()
+    a = g["architecture"]
+    cfg = O.Config()
+    assert (cfg.num_layers, cfg.hidden, cfg.num_heads, cfg.head_dim, cfg.ffn_hidden, cfg.latent_channels,
+            cfg.patch) == (a["num_layers"], a["hidden"], a["num_heads"], a["head_dim"], a["ffn_hidden"],
+                           a["latent_channels"], a["patch"])
+    assert cfg.num_heads * cfg.head_dim == cfg.hidden
+    # q is a D x D projection: 42 * 3072^2 * 2 bytes ~ 0.74 GiB
+    q_gib = cfg.num_layers * cfg.hidden ** 2 * 2 / 2 ** 30
+    assert abs(q_gib - g["q_projection_memory"]["total_gib_about"]) < 0.005
+    # SwiGLU blocks + modulation: ~5B parameters, ~10 GB in bf16
+    D, F = cfg.hidden, cfg.ffn_hidden
+    per_block = 4 * D * D + 3 * D * F + 6 * D * cfg.temb_dim
+    params = cfg.num_layers * per_block + D * cfg.patch_dim + cfg.patch_dim * D + 2 * D * cfg.temb_dim
+    assert round(params / 1e9) == a["dit_params_billion"]
+    assert round(params * 2 / 1e9) == a["dit_bf16_gb_about"]
+    # a two-matrix GELU FFN of 8192 would give ~3.9B: the SwiGLU reading is the one that reaches 5B
+    assert round(cfg.num_layers * (4 * D * D + 2 * D * F) / 1e9) != a["dit_params_billion"]
