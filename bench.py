@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the MOSS-Image DiT denoising step on one MI355X.
+
+Workload (default): the full 42-block DiT at 1024^2 -- a [1, 32, 128, 128] fp32 latent patched to
+4,096 image tokens plus 256 synthetic text tokens (dim 3072), random-init bf16 weights ~N(0, 0.02),
+batch 2 per step (the conditional row and the unconditional row, which skips block 22 inside the
+skip-layer-guidance window), followed by the FP32 CFG (scale 3) + Euler (shift 5) update. One
+timed step = one moss_sample_step call = two DiT forward passes ("each step runs the transformer
+twice", MOSS-Image: specs, settings, VRAM and text rendering tested -- "Recommended settings").
+
+Prints ONE JSON line on stdout. Progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--image-steps 50] [--cpu-baseline-blocks 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "DiT forwards/sec at 1024² (4096 img tok, 1 MI355X); s/image 50 steps CFG3"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def block_linear_flops(M, D, F):
+    return 2.0 * M * (4 * D * D + 3 * D * F)
+
+
+def attention_flops(nb, S, D):
+    return 4.0 * nb * S * S * D
+
+
+def class_work(cls, L, D, F, S, N, T, B, skipped, lat_elems, mod_rows, P):
+    """Algorithmic work of one profiled class over ONE sampling step: (flops, bytes)."""
+    runs = [B] * L
+    for l in skipped:
+        runs[l] -= 1
+    rows = [r * S for r in runs]
+    if cls == "gemm_qkv_rope":
+        return sum(2.0 * M * 3 * D * D for M in rows), 0
+    if cls == "gemm_out_residual":
+        return sum(2.0 * M * D * D for M in rows), 0
+    if cls == "gemm_gate_up_swiglu":
+        return sum(2.0 * M * 2 * F * D for M in rows), 0
+    if cls == "gemm_down_residual":
+        return sum(2.0 * M * D * F for M in rows), 0
+    if cls == "attention":
+        return sum(attention_flops(r, S, D) for r in runs), 0
+    if cls == "ln_mod":
+        return 0, sum(2 * (2.0 * M * D * 2) for M in rows)          # read x, write a; twice per block
+    if cls == "modulation":
+        return 2.0 * B * mod_rows * 256, mod_rows * 256 * 2.0
+    if cls == "embed":
+        return 2.0 * B * N * P * D, B * (T * D * 4.0 + T * D * 2 + lat_elems * 4 + N * P * 2 * 2 + N * D * 2)
+    if cls == "final_layer":
+        return 2.0 * B * N * D * P, B * (N * D * 2 * 2 + N * D * 2 + lat_elems * 4)
+    if cls == "cfg_euler":
+        return 0, 16.0 * lat_elems
+    return 0, 0
+
+
+def _host_f64(t):
+    import numpy as np
+    import torch
+    import oracle as O
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return O.from_bf16_bits(bits)
+
+
+def run_cpu_baseline(weights, nblocks, S, T, gw):
+    """The oracle as it stands, on a bounded sample of the same workload: `nblocks` joint blocks of
+    one sample at the 1024^2 sequence length, float64 numpy with the bf16 storage points mirrored."""
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = O.Config()
+    W = {"t_w1": _host_f64(weights["t_w1"]), "t_w2": _host_f64(weights["t_w2"]),
+         "final_mod_w": _host_f64(weights["final_mod_w"])}
+    for k in ("mod_w", "qkv_w", "out_w", "gate_up_w", "down_w"):
+        W[k] = [_host_f64(weights[k][l]) if l < nblocks else None for l in range(cfg.num_layers)]
+    rng = np.random.default_rng(0)
+    x = O.from_bf16_bits(synth.bf16_normal_bits(rng, (S, cfg.hidden)))
+    Wm = dict(W)
+    Wm["mod_w"] = [W["mod_w"][l] if l < nblocks else np.zeros((6 * cfg.hidden, 256)) for l in range(cfg.num_layers)]
+    t0 = time.perf_counter()
+    m, _ = O.modulation(0.5, Wm, cfg, mirror=True)
+    for l in range(nblocks):
+        x = O.block(x, m[l], W, l, cfg, T, gw, mirror=True)
+    el = time.perf_counter() - t0
+    per_block = el / nblocks
+    fwd_s = cfg.num_layers * per_block
+    return {"value": 1.0 / fwd_s, "unit": "DiT forwards/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{nblocks} of 42 joint blocks (+ the modulation MLP) of one sample at 1024^2 "
+                       f"(S = {S}: {T} text + {S - T} image tokens), float64 numpy with bf16 storage points "
+                       f"mirrored; {el:.1f} s wall; forwards/s = 1 / (42 x {per_block:.2f} s per block)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--image-steps", type=int, default=50, help="steps of the full-image timing (0 = skip)")
+    ap.add_argument("--cpu-baseline-blocks", type=int, default=1, help="oracle blocks for cpu_baseline (0 = skip)")
+    ap.add_argument("--profile-steps", type=int, default=3, help="steps of the per-kernel event pass")
+    ap.add_argument("--text-len", type=int, default=256)
+    ap.add_argument("--latent", type=int, default=128, help="latent side (1024 px / 8)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU: the denoising step runs on one MI355X and this build has no multi-GPU "
+            "path (CFG-parallel / Ulysses sharding is a design note only). Run it with --gpus 1.")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import diffusion_transformer_text_amd as dt
+    import synth
+
+    torch.cuda.set_device(0)
+    L, D, F, H = 42, 3072, 8192, 24
+    lat_side, T = args.latent, args.text_len
+    gw = lat_side // 2
+    N = gw * gw
+    S = T + N
+    P = 128
+    lat_elems = 32 * lat_side * lat_side
+    mod_rows = L * 6 * D + 2 * D
+
+    t0 = time.time()
+    log(f"[bench] drawing random bf16 weights (42 blocks, hidden 3072, FFN 8192) on the GPU")
+    weights = synth.torch_weights(synth.FULL, seed=0, device="cuda")
+    cfg = dt.moss_dit_config_init()
+    model = dt.MossDiT(cfg, weights)
+    log(f"[bench] model created in {time.time() - t0:.1f} s")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    text_cond = torch.randn((1, T, D), generator=g, device="cuda", dtype=torch.float32)
+    text_uncond = torch.zeros_like(text_cond)
+    x0 = torch.randn((1, 32, lat_side, lat_side), generator=g, device="cuda", dtype=torch.float32)
+    sig = dt.moss_sigmas(50, 5.0)
+    x = x0.clone()
+
+    def step(k):
+        # steps 1..49 lie inside the 0.01..1.0 window: the unconditional row skips block 22
+        model.moss_sample_step(x, text_cond, text_uncond, sig, 1 + (k % 49), cfg_scale=3.0,
+                               uncond_skip_layers=[22], slg_start=0.01, slg_stop=1.0)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(k)
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    fwd_per_s = 2.0 * 1000.0 / ms_step
+    step_flops = (2 * L - 1) * (block_linear_flops(S, D, F) + attention_flops(1, S, D)) + \
+        2 * (2.0 * N * P * D) * 2 + 2.0 * 2 * mod_rows * 256
+    mfma_frac = step_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+    log(f"[bench] {ms_step:.2f} ms/step, {fwd_per_s:.2f} forwards/s, whole-step MFMA fraction {mfma_frac:.3f}")
+
+    # ---- per-kernel-class event timing (separate pass over the same steps) ----
+    model.moss_dit_profile_enable(True)
+    for k in range(args.profile_steps):
+        step(k)
+    prof = model.moss_dit_profile_read()
+    model.moss_dit_profile_enable(False)
+    kernels = {}
+    for cls, (ms, n) in prof.items():
+        if n == 0:
+            continue
+        fl, by = class_work(cls, L, D, F, S, N, T, 2, [22], lat_elems, mod_rows, P)
+        ms_s = ms / args.profile_steps
+        e = {"ms_per_step": round(ms_s, 4), "launches_per_step": n // args.profile_steps}
+        if fl and (cls.startswith("gemm") or cls == "attention"):
+            e["tflops"] = round(fl / (ms_s * 1e-3) / 1e12, 1)
+            e["frac_mfma_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        elif by:
+            e["gbs"] = round(by / (ms_s * 1e-3) / 1e9, 1)
+            e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[cls] = e
+    dom = max(kernels, key=lambda c: kernels[c]["ms_per_step"])
+    fl, by = class_work(dom, L, D, F, S, N, T, 2, [22], lat_elems, mod_rows, P)
+    launches = kernels[dom]["launches_per_step"]
+    if dom.startswith("gemm") or dom == "attention":
+        roof = {"bound": "mfma", "achieved": kernels[dom]["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": kernels[dom]["frac_mfma_peak"], "traffic": None, "kernel": dom,
+                "flops_per_launch": fl / launches, "avg_launch_ms": kernels[dom]["ms_per_step"] / launches}
+    else:
+        roof = {"bound": "hbm", "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": kernels[dom]["frac_hbm_peak"], "traffic": None, "kernel": dom,
+                "bytes_per_launch": by / launches, "avg_launch_ms": kernels[dom]["ms_per_step"] / launches}
+    log(f"[bench] per-kernel: {json.dumps(kernels)}")
+
+    # ---- one full 50-step image (step 0 runs full CFG, steps 1..49 skip block 22 in the negative pass) ----
+    s_image = None
+    if args.image_steps > 0:
+        x.copy_(x0)
+        sig_i = dt.moss_sigmas(args.image_steps, 5.0)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.image_steps):
+            model.moss_sample_step(x, text_cond, text_uncond, sig_i, i, cfg_scale=3.0, uncond_skip_layers=[22])
+        end.record()
+        end.synchronize()
+        s_image = start.elapsed_time(end) / 1000.0
+        assert torch.isfinite(x).all().item()
+        log(f"[bench] {args.image_steps}-step image: {s_image:.2f} s (DiT + guidance only)")
+
+    cpu = None
+    if args.cpu_baseline_blocks > 0:
+        log(f"[bench] cpu_baseline: oracle on {args.cpu_baseline_blocks} block(s) of one sample")
+        cpu = run_cpu_baseline(weights, args.cpu_baseline_blocks, S, T, gw)
+        log(f"[bench] cpu_baseline {cpu['value']:.5f} forwards/s ({cpu['cores']} threads)")
+
+    out = {
+        "metric": METRIC, "value": round(fwd_per_s, 3), "unit": "DiT forwards/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"MOSS-Image DiT sampling step at {lat_side * 8}^2: 42 blocks, hidden 3072, 24x128 "
+                               f"heads, FFN 8192, {N} image + {T} text tokens, batch 2 (cond + uncond skipping block "
+                               f"22), CFG 3, Euler shift 5",
+                   "global_batch": 2, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "s_per_image": round(s_image, 3) if s_image else None,
+        "image_steps": args.image_steps,
+        "mfma_fraction_step": round(mfma_frac, 4),
+        "step_tflop": round(step_flops / 1e12, 2),
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    model.close()
+
+
+if __name__ == "__main__":
+    main()

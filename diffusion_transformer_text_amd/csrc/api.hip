@@ -1,0 +1,1005 @@
+// C ABI and host executor of the MOSS-Image DiT denoising step.
+//
+// The executor enqueues, per forward pass: the timestep MLP and the modulation GEMV of every block
+// (one read of all modulation weights for the whole batch), the text cast and the patch embedding
+// GEMM, the 42 joint blocks (LN1-mod, QKV GEMM + RoPE, attention, out GEMM + gated residual,
+// LN2-mod, gate/up GEMM + SiLU*mul, down GEMM + gated residual), and the final LN-mod + output GEMM
+// that scatters the velocity back to latent layout. A sampling step adds the fused FP32 CFG + Euler
+// kernel. Skip-layer guidance runs a skipped block only on the samples that keep it: the kernels are
+// row-independent, so a sample's result does not depend on which other samples share the launch.
+//
+// Argument conventions (struct_size, *_init, status codes, a dead handle after a device error,
+// user-facing validation messages) follow the C API rules of the MossInfer integration guide.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "moss_dit.h"
+#include "moss_dit_ops.h"
+
+using namespace moss;
+
+namespace {
+
+thread_local std::string g_thread_error;
+
+constexpr int kMaxLatentSide = 512;           // 4096 px / 8
+constexpr double kMaxPixels = 4.2e6;          // 4.2 megapixels
+constexpr int kMaxTextLen = 4096;
+constexpr int kSinusoidDim = 256;
+
+std::string fmt(const char* f, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, f);
+  vsnprintf(buf, sizeof buf, f, ap);
+  va_end(ap);
+  return buf;
+}
+
+void copy_msg(const std::string& m, char* msg, int32_t len) {
+  if (msg && len > 0) {
+    strncpy(msg, m.c_str(), (size_t)len - 1);
+    msg[len - 1] = 0;
+  }
+}
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+// ---- RoPE tables: cos/sin of pos * theta^(-k/32), pos < 256, k < 32, fp64 rounded to fp32 ----
+std::mutex g_rope_mu;
+std::map<std::pair<int, float>, float*> g_rope;   // (device, theta) -> [2][256][32], process lifetime
+
+hipError_t rope_table(float theta, float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_rope_mu);
+  auto it = g_rope.find({dev, theta});
+  if (it != g_rope.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  const int Q = kHeadDim / 4;
+  std::vector<float> host(2 * kRopeMaxPos * Q);
+  for (int pos = 0; pos < kRopeMaxPos; ++pos)
+    for (int k = 0; k < Q; ++k) {
+      const double ang = (double)pos * std::pow((double)theta, -(double)k / Q);
+      host[pos * Q + k] = (float)std::cos(ang);
+      host[kRopeMaxPos * Q + pos * Q + k] = (float)std::sin(ang);
+    }
+  float* d = nullptr;
+  e = hipMalloc(&d, host.size() * sizeof(float));
+  if (e != hipSuccess) return e;
+  e = hipMemcpy(d, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    hipFree(d);
+    return e;
+  }
+  g_rope[{dev, theta}] = d;
+  *out = d;
+  return hipSuccess;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// =============================================================================================
+// handle
+// =============================================================================================
+struct moss_dit {
+  moss_dit_config cfg{};
+  int device = 0;
+  bool dead = false;
+  std::string err;
+  uint16_t* wbuf = nullptr;
+  uint16_t *t_w1 = nullptr, *t_w2 = nullptr, *x_embed = nullptr, *mod_all = nullptr, *final_w = nullptr;
+  std::vector<uint16_t*> qkv, out, gu, down;
+  float* rope = nullptr;   // [2][256][32]
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  // per-class event timing (moss_dit_profile_enable)
+  bool prof_on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[MOSS_PROF_CLASSES];
+  size_t prof_used[MOSS_PROF_CLASSES] = {};
+  long mod_rows() const {
+    return (long)cfg.num_layers * 6 * cfg.hidden + 2L * cfg.hidden;
+  }
+};
+
+namespace {
+
+int fail(moss_dit* h, int status, const std::string& msg) {
+  if (h) {
+    h->err = msg;
+    if (status == MOSS_ERR_DEVICE) h->dead = true;
+  } else {
+    g_thread_error = msg;
+  }
+  return status;
+}
+
+#define HIP_TRY(h, expr)                                                                          \
+  do {                                                                                            \
+    hipError_t e_ = (expr);                                                                       \
+    if (e_ != hipSuccess) return fail((h), MOSS_ERR_DEVICE, fmt("%s failed: %s", #expr, hipGetErrorString(e_))); \
+  } while (0)
+
+enum ProfClass { PC_MOD = 0, PC_EMBED, PC_LN, PC_QKV, PC_ATTN, PC_OUT, PC_GATE_UP, PC_DOWN, PC_FINAL, PC_CFG };
+
+// Brackets the launches of one class with events when profiling is on.
+struct ProfScope {
+  moss_dit* h;
+  int cls;
+  hipStream_t st;
+  hipEvent_t end = nullptr;
+  ProfScope(moss_dit* h_, int cls_, hipStream_t st_) : h(h_), cls(cls_), st(st_) {
+    if (!h || !h->prof_on) return;
+    auto& pool = h->prof_ev[cls];
+    size_t& used = h->prof_used[cls];
+    if (used == pool.size()) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+      pool.push_back({a, b});
+    }
+    (void)hipEventRecord(pool[used].first, st);
+    end = pool[used].second;
+    ++used;
+  }
+  ~ProfScope() {
+    if (end) (void)hipEventRecord(end, st);
+  }
+};
+
+hipError_t dev_alloc(void** p, size_t bytes) {
+  if (env_flag("MOSS_DIT_FAIL_ALLOC")) return hipErrorOutOfMemory;
+  return hipMalloc(p, bytes);
+}
+
+int check_config(const moss_dit_config* c, std::string& msg) {
+  if (!c) {
+    msg = "config is NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (c->struct_size != sizeof(moss_dit_config)) {
+    msg = fmt("moss_dit_config.struct_size %u, this library expects %zu (fill it with moss_dit_config_init)",
+              c->struct_size, sizeof(moss_dit_config));
+    return MOSS_ERR_ABI_MISMATCH;
+  }
+  if (c->num_layers < 1 || c->hidden < 1 || c->num_heads < 1 || c->head_dim < 1 || c->ffn_hidden < 1 ||
+      c->latent_channels < 1 || c->patch < 1 || c->temb_dim < 1 || !(c->norm_eps > 0.f) ||
+      !(c->rope_theta > 1.f) || !std::isfinite(c->flow_multiplier)) {
+    msg = "config values must be positive";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (c->head_dim != kHeadDim || c->hidden != c->num_heads * c->head_dim || c->hidden % 256 != 0 ||
+      c->hidden > 4096 || c->ffn_hidden % 64 != 0 || c->temb_dim != kSinusoidDim || c->patch != 2 ||
+      c->num_layers > 64 || c->qk_norm != 0 || c->latent_channels * 4 % 128 != 0) {
+    msg = fmt("unsupported configuration (need head_dim 128, hidden = heads*128, hidden %% 256 == 0 and <= 4096, "
+              "ffn %% 64 == 0, temb 256, patch 2, channels*4 %% 128 == 0, <= 64 layers, no qk_norm)");
+    return MOSS_ERR_NOT_SUPPORTED;
+  }
+  return MOSS_OK;
+}
+
+int check_latent(int32_t lh, int32_t lw, std::string& msg) {
+  if (lh <= 0 || lw <= 0 || lh % 2 || lw % 2) {
+    msg = "Height and width must be positive multiples of 16.";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (lh > kMaxLatentSide || lw > kMaxLatentSide) {
+    msg = "Height and width must be at most 4096.";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (64.0 * lh * lw > kMaxPixels) {
+    msg = "The image must be at most 4.2 megapixels.";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  return MOSS_OK;
+}
+
+int check_text_len(int32_t t, std::string& msg) {
+  if (t < 1 || t > kMaxTextLen) {
+    msg = fmt("text_len %d out of range [1, %d]", t, kMaxTextLen);
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  return MOSS_OK;
+}
+
+int validate_forward(const moss_dit_config* c, const moss_forward_args* a, std::string& msg) {
+  int s = check_config(c, msg);
+  if (s) return s;
+  if (!a) {
+    msg = "args is NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (a->struct_size != sizeof(moss_forward_args)) {
+    msg = fmt("moss_forward_args.struct_size %u, this library expects %zu", a->struct_size, sizeof(moss_forward_args));
+    return MOSS_ERR_ABI_MISMATCH;
+  }
+  if (a->batch < 1 || a->batch > kMaxBatch) {
+    msg = fmt("batch %d out of range [1, %d]", a->batch, kMaxBatch);
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if ((s = check_latent(a->latent_h, a->latent_w, msg))) return s;
+  if ((s = check_text_len(a->text_len, msg))) return s;
+  if (!a->latents || !a->text || !a->sigma || !a->velocity) {
+    msg = "latents, text, sigma and velocity must not be NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  for (int b = 0; b < a->batch; ++b) {
+    if (!(a->sigma[b] >= 0.f && a->sigma[b] <= 1.f)) {
+      msg = fmt("sigma[%d] = %g outside [0, 1]", b, (double)a->sigma[b]);
+      return MOSS_ERR_INVALID_ARGUMENT;
+    }
+    if (a->skip_mask && c->num_layers < 64 && (a->skip_mask[b] >> c->num_layers)) {
+      msg = fmt("skip_mask[%d] names a block >= num_layers (%d)", b, c->num_layers);
+      return MOSS_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return MOSS_OK;
+}
+
+int validate_step(const moss_dit_config* c, const moss_step_args* a, std::string& msg) {
+  int s = check_config(c, msg);
+  if (s) return s;
+  if (!a) {
+    msg = "args is NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (a->struct_size != sizeof(moss_step_args)) {
+    msg = fmt("moss_step_args.struct_size %u, this library expects %zu", a->struct_size, sizeof(moss_step_args));
+    return MOSS_ERR_ABI_MISMATCH;
+  }
+  if ((s = check_latent(a->latent_h, a->latent_w, msg))) return s;
+  if ((s = check_text_len(a->text_len, msg))) return s;
+  if (a->num_steps < 1) {
+    msg = "num_steps must be at least 1";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (a->step < 0 || a->step >= a->num_steps) {
+    msg = fmt("step %d out of range [0, %d)", a->step, a->num_steps);
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (!std::isfinite(a->cfg_scale) || a->cfg_scale < 1.f) {
+    msg = "CFG scale must be at least 1.0.";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (!std::isfinite(a->slg_start) || !std::isfinite(a->slg_stop)) {
+    msg = "slg_start and slg_stop must be finite";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (!a->x || !a->text_cond || !a->sigmas) {
+    msg = "x, text_cond and sigmas must not be NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (a->cfg_scale > 1.f && !a->text_uncond) {
+    msg = "text_uncond must not be NULL when cfg_scale > 1";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (a->n_skip < 0 || a->n_skip > c->num_layers || (a->n_skip > 0 && !a->uncond_skip_layers)) {
+    msg = fmt("n_skip %d invalid", a->n_skip);
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  for (int i = 0; i < a->n_skip; ++i) {
+    const int l = a->uncond_skip_layers[i];
+    if (l < 0 || l >= c->num_layers) {
+      msg = fmt("Skip layers must be block numbers from 0 to %d (got %d).", c->num_layers - 1, l);
+      return MOSS_ERR_INVALID_ARGUMENT;
+    }
+  }
+  for (int i = 0; i <= a->num_steps; ++i) {
+    if (!std::isfinite(a->sigmas[i])) {
+      msg = fmt("sigmas[%d] is not finite", i);
+      return MOSS_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return MOSS_OK;
+}
+
+// ---- workspace carve ----
+struct Carve {
+  uint16_t *x, *a, *qkv, *o, *h, *tokens, *mod;
+  float *u, *vel;
+};
+
+size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, Carve* c) {
+  const moss_dit_config& k = H->cfg;
+  const size_t D = k.hidden, F = k.ffn_hidden, P = (size_t)k.latent_channels * 4;
+  const size_t M = (size_t)B * S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  Carve t;
+  t.x = (uint16_t*)take(M * D * 2);
+  t.a = (uint16_t*)take(M * D * 2);
+  t.qkv = (uint16_t*)take(M * 3 * D * 2);
+  t.o = (uint16_t*)take(M * D * 2);
+  t.h = (uint16_t*)take(M * F * 2);
+  t.tokens = (uint16_t*)take((size_t)B * N * P * 2);
+  t.mod = (uint16_t*)take((size_t)B * H->mod_rows() * 2);
+  t.u = (float*)take((size_t)B * k.temb_dim * 4);
+  t.vel = (float*)take((size_t)2 * lat_elems * 4);
+  if (c) *c = t;
+  return off;
+}
+
+int ensure_ws(moss_dit* H, size_t bytes) {
+  if (bytes <= H->ws_bytes) return MOSS_OK;
+  if (H->ws) {
+    HIP_TRY(H, hipDeviceSynchronize());
+    HIP_TRY(H, hipFree(H->ws));
+    H->ws = nullptr;
+    H->ws_bytes = 0;
+  }
+  void* p = nullptr;
+  const hipError_t e = dev_alloc(&p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(H, MOSS_ERR_OUT_OF_MEMORY, fmt("workspace allocation of %zu bytes failed", bytes));
+  }
+  H->ws = p;
+  H->ws_bytes = bytes;
+  return MOSS_OK;
+}
+
+GemmArgs gemm_args(const uint16_t* A, const uint16_t* W, int M, int N, int K, void* out, long ldo) {
+  GemmArgs g;
+  memset(&g, 0, sizeof g);
+  g.A = A;
+  g.W = W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = K;
+  g.ldw = K;
+  g.out = out;
+  g.ldo = ldo;
+  g.seg = M > 0 ? M : 1;
+  g.seg_stride = 0;
+  g.seg_off = 0;
+  g.rows_per_sample = 1;
+  return g;
+}
+
+LnModArgs ln_args(const uint16_t* x, uint16_t* out, int rows, int D, int rows_per_sample, const uint16_t* shift,
+                  const uint16_t* scale, long mod_stride, float eps) {
+  LnModArgs l;
+  l.x = x;
+  l.out = out;
+  l.rows = rows;
+  l.D = D;
+  l.seg = rows > 0 ? rows : 1;
+  l.seg_stride = 0;
+  l.seg_off = 0;
+  l.rows_per_sample = rows_per_sample;
+  l.shift = shift;
+  l.scale = scale;
+  l.mod_stride = mod_stride;
+  l.eps = eps;
+  return l;
+}
+
+// One joint block on nb consecutive samples of a residual stream x [nb*S, D].
+int run_block(moss_dit* H, int l, uint16_t* x, int nb, int T, int gw, int S, const uint16_t* mod, long mod_stride,
+              const Carve& c, const moss_block_taps* taps, hipStream_t st) {
+  const moss_dit_config& k = H->cfg;
+  const int D = k.hidden, F = k.ffn_hidden, M = nb * S;
+  const uint16_t* m = mod + (long)l * 6 * D;
+  auto tap_copy = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
+    if (!taps || !dst) return hipSuccess;
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+  };
+  // A4: LN1 + modulation
+  {
+    ProfScope ps(H, PC_LN, st);
+    HIP_TRY(H, launch_ln_mod(ln_args(x, c.a, M, D, S, m, m + D, mod_stride, k.norm_eps), st));
+  }
+  HIP_TRY(H, tap_copy(taps ? taps->a : nullptr, c.a, (size_t)M * D * 2));
+  // A5: QKV projection, RoPE on image rows of q and k
+  GemmArgs g = gemm_args(c.a, H->qkv[l], M, 3 * D, D, c.qkv, 3 * D);
+  g.rope_cos = H->rope;
+  g.rope_sin = H->rope + kRopeMaxPos * (kHeadDim / 4);
+  g.S = S;
+  g.T = T;
+  g.grid_w = gw;
+  g.rope_cols = 2 * D;
+  {
+    ProfScope ps(H, PC_QKV, st);
+    HIP_TRY(H, launch_gemm(g, EPI_QKV_ROPE, st));
+  }
+  HIP_TRY(H, tap_copy(taps ? taps->qkv : nullptr, c.qkv, (size_t)M * 3 * D * 2));
+  // A6: attention
+  AttnArgs at;
+  at.qkv = c.qkv;
+  at.out = c.o;
+  at.B = nb;
+  at.S = S;
+  at.H = k.num_heads;
+  at.ld_qkv = 3L * D;
+  at.ld_out = D;
+  at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+  {
+    ProfScope ps(H, PC_ATTN, st);
+    HIP_TRY(H, launch_attention(at, st));
+  }
+  HIP_TRY(H, tap_copy(taps ? taps->o : nullptr, c.o, (size_t)M * D * 2));
+  // A7: out projection + gated residual
+  if (taps && taps->attn) HIP_TRY(H, launch_gemm(gemm_args(c.o, H->out[l], M, D, D, taps->attn, D), EPI_F32, st));
+  g = gemm_args(c.o, H->out[l], M, D, D, x, D);
+  g.gate = m + 2 * D;
+  g.rows_per_sample = S;
+  g.gate_stride = mod_stride;
+  {
+    ProfScope ps(H, PC_OUT, st);
+    HIP_TRY(H, launch_gemm(g, EPI_GATED_RES, st));
+  }
+  HIP_TRY(H, tap_copy(taps ? taps->x1 : nullptr, x, (size_t)M * D * 2));
+  // A8: LN2 + modulation
+  {
+    ProfScope ps(H, PC_LN, st);
+    HIP_TRY(H, launch_ln_mod(ln_args(x, c.a, M, D, S, m + 3 * D, m + 4 * D, mod_stride, k.norm_eps), st));
+  }
+  HIP_TRY(H, tap_copy(taps ? taps->a2 : nullptr, c.a, (size_t)M * D * 2));
+  // A9: gate/up projection + SiLU * mul
+  {
+    ProfScope ps(H, PC_GATE_UP, st);
+    HIP_TRY(H, launch_gemm(gemm_args(c.a, H->gu[l], M, 2 * F, D, c.h, F), EPI_SWIGLU, st));
+  }
+  HIP_TRY(H, tap_copy(taps ? taps->h : nullptr, c.h, (size_t)M * F * 2));
+  // A10: down projection + gated residual
+  if (taps && taps->ffn) HIP_TRY(H, launch_gemm(gemm_args(c.h, H->down[l], M, D, F, taps->ffn, D), EPI_F32, st));
+  g = gemm_args(c.h, H->down[l], M, D, F, x, D);
+  g.gate = m + 5 * D;
+  g.rows_per_sample = S;
+  g.gate_stride = mod_stride;
+  {
+    ProfScope ps(H, PC_DOWN, st);
+    HIP_TRY(H, launch_gemm(g, EPI_GATED_RES, st));
+  }
+  return MOSS_OK;
+}
+
+int run_modulation(moss_dit* H, const float* sigma, int B, const Carve& c, hipStream_t st) {
+  const moss_dit_config& k = H->cfg;
+  SigmaBatch sb;
+  for (int b = 0; b < kMaxBatch; ++b) sb.s[b] = b < B ? sigma[b] : 0.f;
+  ProfScope ps(H, PC_MOD, st);
+  HIP_TRY(H, launch_time_mlp(sb, B, H->t_w1, H->t_w2, k.temb_dim, k.flow_multiplier, c.u, st));
+  HIP_TRY(H, launch_mod_gemv(H->mod_all, (int)H->mod_rows(), k.temb_dim, c.u, B, c.mod, H->mod_rows(), st));
+  return MOSS_OK;
+}
+
+struct FwdPlan {
+  int B, lat_h, lat_w, T;
+  PtrBatch lat, txt;
+  float sigma[kMaxBatch];
+  uint64_t skip[kMaxBatch];
+  float* vel;     // [B, C, lat_h, lat_w]
+  uint16_t* dump; // optional [L + 1, B, S, D]
+};
+
+int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st) {
+  const moss_dit_config& k = H->cfg;
+  const int D = k.hidden, L = k.num_layers, P = k.latent_channels * 4;
+  const int gh = p.lat_h / 2, gw = p.lat_w / 2, N = gh * gw, S = p.T + N, B = p.B;
+  const long mstride = H->mod_rows();
+  int s;
+  // A2: timestep embedding + modulation of every block for every sample
+  if ((s = run_modulation(H, p.sigma, B, c, st))) return s;
+  // A3: text rows (fp32 -> bf16) and patch embedding of the image rows
+  GemmArgs g = gemm_args(c.tokens, H->x_embed, B * N, D, P, c.x, D);
+  g.seg = N;
+  g.seg_stride = S;
+  g.seg_off = p.T;
+  {
+    ProfScope ps(H, PC_EMBED, st);
+    HIP_TRY(H, launch_text_cast(p.txt, B, p.T, D, S, c.x, st));
+    HIP_TRY(H, launch_patchify(p.lat, B, k.latent_channels, p.lat_h, p.lat_w, c.tokens, st));
+    HIP_TRY(H, launch_gemm(g, EPI_BF16, st));
+  }
+  const size_t stream_bytes = (size_t)B * S * D * 2;
+  if (p.dump) HIP_TRY(H, hipMemcpyAsync(p.dump, c.x, stream_bytes, hipMemcpyDeviceToDevice, st));
+  // A4..A10 x L, skipped blocks leave their samples' rows untouched
+  for (int l = 0; l < L; ++l) {
+    int b = 0;
+    while (b < B) {
+      if ((p.skip[b] >> l) & 1ULL) {
+        ++b;
+        continue;
+      }
+      int e = b;
+      while (e < B && !((p.skip[e] >> l) & 1ULL)) ++e;
+      if ((s = run_block(H, l, c.x + (size_t)b * S * D, e - b, p.T, gw, S, c.mod + (size_t)b * mstride, mstride, c,
+                         nullptr, st)))
+        return s;
+      b = e;
+    }
+    if (p.dump)
+      HIP_TRY(H, hipMemcpyAsync(p.dump + (size_t)(l + 1) * B * S * D, c.x, stream_bytes, hipMemcpyDeviceToDevice, st));
+  }
+  // A11: final LN-mod on the image rows, output projection, unpatchify to fp32 velocity
+  LnModArgs ln = ln_args(c.x, c.a, B * N, D, N, c.mod + (long)L * 6 * D, c.mod + (long)L * 6 * D + D, mstride,
+                         k.norm_eps);
+  ln.seg = N;
+  ln.seg_stride = S;
+  ln.seg_off = p.T;
+  g = gemm_args(c.a, H->final_w, B * N, P, D, p.vel, 0);
+  g.C = k.latent_channels;
+  g.lat_h = p.lat_h;
+  g.lat_w = p.lat_w;
+  g.n_img = N;
+  {
+    ProfScope ps(H, PC_FINAL, st);
+    HIP_TRY(H, launch_ln_mod(ln, st));
+    HIP_TRY(H, launch_gemm(g, EPI_F32_UNPATCH, st));
+  }
+  return MOSS_OK;
+}
+
+int enter(moss_dit* H) {
+  if (!H) {
+    g_thread_error = "handle is NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (H->dead) return fail(H, MOSS_ERR_DEVICE, "the handle hit a device error earlier; destroy it");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != H->device) {
+    if (hipSetDevice(H->device) != hipSuccess) return fail(H, MOSS_ERR_DEVICE, "cannot select the handle's device");
+  }
+  return MOSS_OK;
+}
+
+}  // namespace
+
+// =============================================================================================
+// exported functions
+// =============================================================================================
+extern "C" {
+
+int moss_dit_abi_version(void) { return MOSS_DIT_ABI_VERSION; }
+
+const char* moss_status_string(int s) {
+  switch (s) {
+    case MOSS_OK: return "ok";
+    case MOSS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOSS_ERR_NOT_SUPPORTED: return "not supported";
+    case MOSS_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case MOSS_ERR_DEVICE: return "device error";
+    case MOSS_ERR_ABI_MISMATCH: return "ABI mismatch";
+    default: return "unknown status";
+  }
+}
+
+const char* moss_dit_last_error(const moss_dit* h) { return h ? h->err.c_str() : g_thread_error.c_str(); }
+
+void moss_dit_config_init(moss_dit_config* c, uint32_t size) {
+  if (!c) return;
+  moss_dit_config d;
+  d.struct_size = size;
+  d.num_layers = 42;
+  d.hidden = 3072;
+  d.num_heads = 24;
+  d.head_dim = 128;
+  d.ffn_hidden = 8192;
+  d.latent_channels = 32;
+  d.patch = 2;
+  d.temb_dim = 256;
+  d.qk_norm = 0;
+  d.rope_theta = 1.0e4f;
+  d.norm_eps = 1.0e-6f;
+  d.flow_multiplier = 1000.f;
+  memcpy(c, &d, size < sizeof d ? size : sizeof d);
+}
+
+void moss_dit_weights_init(moss_dit_weights* w, uint32_t size) {
+  if (!w) return;
+  moss_dit_weights d;
+  memset(&d, 0, sizeof d);
+  d.struct_size = size;
+  memcpy(w, &d, size < sizeof d ? size : sizeof d);
+}
+
+void moss_forward_args_init(moss_forward_args* a, uint32_t size) {
+  if (!a) return;
+  moss_forward_args d;
+  memset(&d, 0, sizeof d);
+  d.struct_size = size;
+  d.batch = 1;
+  d.latent_h = d.latent_w = 128;
+  d.text_len = 256;
+  memcpy(a, &d, size < sizeof d ? size : sizeof d);
+}
+
+static const int32_t kDefaultSkip[1] = {22};
+
+void moss_step_args_init(moss_step_args* a, uint32_t size) {
+  if (!a) return;
+  moss_step_args d;
+  memset(&d, 0, sizeof d);
+  d.struct_size = size;
+  d.latent_h = d.latent_w = 128;
+  d.text_len = 256;
+  d.num_steps = 50;
+  d.step = 0;
+  d.cfg_scale = 3.0f;
+  d.slg_start = 0.01f;
+  d.slg_stop = 1.0f;
+  d.uncond_skip_layers = kDefaultSkip;
+  d.n_skip = 1;
+  memcpy(a, &d, size < sizeof d ? size : sizeof d);
+}
+
+void moss_block_taps_init(moss_block_taps* t, uint32_t size) {
+  if (!t) return;
+  moss_block_taps d;
+  memset(&d, 0, sizeof d);
+  d.struct_size = size;
+  memcpy(t, &d, size < sizeof d ? size : sizeof d);
+}
+
+int moss_sigmas(int32_t num_steps, float shift, float* sigmas) {
+  if (num_steps < 1 || !sigmas || !(shift > 0.f) || !std::isfinite(shift)) {
+    g_thread_error = "num_steps must be >= 1, shift > 0 and sigmas non-NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  for (int i = 0; i <= num_steps; ++i) {
+    const double s = (double)(num_steps - i) / (double)num_steps;
+    sigmas[i] = (float)((double)shift * s / (1.0 + ((double)shift - 1.0) * s));
+  }
+  return MOSS_OK;
+}
+
+int moss_validate_forward_args(const moss_dit_config* cfg, const moss_forward_args* a, char* msg, int32_t msg_len) {
+  std::string m;
+  const int s = validate_forward(cfg, a, m);
+  copy_msg(s ? m : std::string("ok"), msg, msg_len);
+  return s;
+}
+
+int moss_validate_step_args(const moss_dit_config* cfg, const moss_step_args* a, char* msg, int32_t msg_len) {
+  std::string m;
+  const int s = validate_step(cfg, a, m);
+  copy_msg(s ? m : std::string("ok"), msg, msg_len);
+  return s;
+}
+
+int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int weights_on_device, void* stream,
+                    moss_dit** out) {
+  if (!out) {
+    g_thread_error = "out is NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  *out = nullptr;
+  std::string msg;
+  int s = check_config(cfg, msg);
+  if (s) return fail(nullptr, s, msg);
+  if (!w || w->struct_size != sizeof(moss_dit_weights))
+    return fail(nullptr, w ? MOSS_ERR_ABI_MISMATCH : MOSS_ERR_INVALID_ARGUMENT,
+                "moss_dit_weights missing or struct_size mismatch (fill it with moss_dit_weights_init)");
+  const int L = cfg->num_layers;
+  if (!w->t_w1 || !w->t_w2 || !w->x_embed_w || !w->mod_w || !w->qkv_w || !w->out_w || !w->gate_up_w || !w->down_w ||
+      !w->final_mod_w || !w->final_w)
+    return fail(nullptr, MOSS_ERR_INVALID_ARGUMENT, "a weight pointer is NULL");
+  for (int l = 0; l < L; ++l)
+    if (!w->mod_w[l] || !w->qkv_w[l] || !w->out_w[l] || !w->gate_up_w[l] || !w->down_w[l])
+      return fail(nullptr, MOSS_ERR_INVALID_ARGUMENT, fmt("a weight pointer of block %d is NULL", l));
+
+  moss_dit* H = new moss_dit();
+  H->cfg = *cfg;
+  hipStream_t st = (hipStream_t)stream;
+  auto bail = [&](int status, const std::string& m) {
+    if (H->wbuf) hipFree(H->wbuf);
+    delete H;
+    return fail(nullptr, status, m);
+  };
+  if (hipGetDevice(&H->device) != hipSuccess) return bail(MOSS_ERR_DEVICE, "hipGetDevice failed");
+
+  const size_t D = cfg->hidden, F = cfg->ffn_hidden, E = cfg->temb_dim, P = (size_t)cfg->latent_channels * 4;
+  const size_t n_t1 = E * kSinusoidDim, n_t2 = E * E, n_xe = D * P, n_mod = (size_t)H->mod_rows() * E, n_fin = P * D;
+  const size_t n_layer = 3 * D * D + D * D + 2 * F * D + D * F;
+  const size_t total = n_t1 + n_t2 + n_xe + n_mod + n_fin + (size_t)L * n_layer;
+  void* p = nullptr;
+  hipError_t e = dev_alloc(&p, total * 2);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return bail(MOSS_ERR_OUT_OF_MEMORY, fmt("weight allocation of %zu bytes failed", total * 2));
+  }
+  H->wbuf = (uint16_t*)p;
+  uint16_t* cur = H->wbuf;
+  auto next = [&](size_t n) {
+    uint16_t* r = cur;
+    cur += n;
+    return r;
+  };
+  H->t_w1 = next(n_t1);
+  H->t_w2 = next(n_t2);
+  H->x_embed = next(n_xe);
+  H->mod_all = next(n_mod);
+  H->final_w = next(n_fin);
+  for (int l = 0; l < L; ++l) {
+    H->qkv.push_back(next(3 * D * D));
+    H->out.push_back(next(D * D));
+    H->gu.push_back(next(2 * F * D));
+    H->down.push_back(next(D * F));
+  }
+  const hipMemcpyKind kind = weights_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+  auto cp = [&](void* dst, const void* src, size_t n) { return hipMemcpyAsync(dst, src, n * 2, kind, st); };
+#define CREATE_TRY(expr)                                                                   \
+  do {                                                                                     \
+    hipError_t e2 = (expr);                                                                \
+    if (e2 != hipSuccess) return bail(MOSS_ERR_DEVICE, fmt("%s failed: %s", #expr, hipGetErrorString(e2))); \
+  } while (0)
+  CREATE_TRY(cp(H->t_w1, w->t_w1, n_t1));
+  CREATE_TRY(cp(H->t_w2, w->t_w2, n_t2));
+  CREATE_TRY(cp(H->x_embed, w->x_embed_w, n_xe));
+  for (int l = 0; l < L; ++l) CREATE_TRY(cp(H->mod_all + (size_t)l * 6 * D * E, w->mod_w[l], 6 * D * E));
+  CREATE_TRY(cp(H->mod_all + (size_t)L * 6 * D * E, w->final_mod_w, 2 * D * E));
+  CREATE_TRY(cp(H->final_w, w->final_w, n_fin));
+  // gate/up rows are interleaved in 32-row groups for the SwiGLU epilogue; host weights go through
+  // a staging buffer (the workspace allocation, freed below).
+  uint16_t* stage = nullptr;
+  if (!weights_on_device) {
+    void* sp = nullptr;
+    if (dev_alloc(&sp, 2 * F * D * 2) != hipSuccess) {
+      (void)hipGetLastError();
+      return bail(MOSS_ERR_OUT_OF_MEMORY, "staging allocation failed");
+    }
+    stage = (uint16_t*)sp;
+  }
+  for (int l = 0; l < L; ++l) {
+    CREATE_TRY(cp(H->qkv[l], w->qkv_w[l], 3 * D * D));
+    CREATE_TRY(cp(H->out[l], w->out_w[l], D * D));
+    CREATE_TRY(cp(H->down[l], w->down_w[l], D * F));
+    const uint16_t* src = (const uint16_t*)w->gate_up_w[l];
+    if (stage) {
+      CREATE_TRY(cp(stage, src, 2 * F * D));
+      src = stage;
+    }
+    CREATE_TRY(launch_interleave_gate_up(src, H->gu[l], (int)F, (int)D, st));
+    if (stage) CREATE_TRY(hipStreamSynchronize(st));   // the staging buffer is reused next layer
+  }
+  CREATE_TRY(hipStreamSynchronize(st));
+  if (stage) hipFree(stage);
+  CREATE_TRY(rope_table(cfg->rope_theta, &H->rope));
+#undef CREATE_TRY
+  *out = H;
+  return MOSS_OK;
+}
+
+void moss_dit_destroy(moss_dit* h) {
+  if (!h) return;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(h->device);
+  (void)hipDeviceSynchronize();
+  if (h->ws) (void)hipFree(h->ws);
+  if (h->wbuf) (void)hipFree(h->wbuf);
+  for (auto& pool : h->prof_ev)
+    for (auto& e : pool) {
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
+    }
+  if (prev >= 0) (void)hipSetDevice(prev);
+  delete h;
+}
+
+int moss_dit_forward(moss_dit* h, const moss_forward_args* a, void* stream) {
+  int s = enter(h);
+  if (s) return s;
+  std::string msg;
+  if ((s = validate_forward(&h->cfg, a, msg))) return fail(h, s, msg);
+  const moss_dit_config& k = h->cfg;
+  const int B = a->batch, N = (a->latent_h / 2) * (a->latent_w / 2), S = a->text_len + N;
+  const int lat = k.latent_channels * a->latent_h * a->latent_w;
+  if ((s = ensure_ws(h, carve(h, B, S, N, lat, nullptr, nullptr)))) return s;
+  Carve c;
+  carve(h, B, S, N, lat, (char*)h->ws, &c);
+  FwdPlan p;
+  memset(&p, 0, sizeof p);
+  p.B = B;
+  p.lat_h = a->latent_h;
+  p.lat_w = a->latent_w;
+  p.T = a->text_len;
+  for (int b = 0; b < B; ++b) {
+    p.lat.p[b] = a->latents + (size_t)b * lat;
+    p.txt.p[b] = a->text + (size_t)b * a->text_len * k.hidden;
+    p.sigma[b] = a->sigma[b];
+    p.skip[b] = a->skip_mask ? a->skip_mask[b] : 0;
+  }
+  p.vel = a->velocity;
+  p.dump = (uint16_t*)a->residual_dump;
+  return run_forward(h, p, c, (hipStream_t)stream);
+}
+
+int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream) {
+  int s = enter(h);
+  if (s) return s;
+  std::string msg;
+  if ((s = validate_step(&h->cfg, a, msg))) return fail(h, s, msg);
+  const moss_dit_config& k = h->cfg;
+  const bool guided = a->cfg_scale > 1.f;
+  const int B = guided ? 2 : 1;
+  const int N = (a->latent_h / 2) * (a->latent_w / 2), S = a->text_len + N;
+  const int lat = k.latent_channels * a->latent_h * a->latent_w;
+  if ((s = ensure_ws(h, carve(h, B, S, N, lat, nullptr, nullptr)))) return s;
+  Carve c;
+  carve(h, B, S, N, lat, (char*)h->ws, &c);
+  FwdPlan p;
+  memset(&p, 0, sizeof p);
+  p.B = B;
+  p.lat_h = a->latent_h;
+  p.lat_w = a->latent_w;
+  p.T = a->text_len;
+  const float sig = a->sigmas[a->step], sig_next = a->sigmas[a->step + 1];
+  p.lat.p[0] = a->x;
+  p.txt.p[0] = a->text_cond;
+  p.sigma[0] = sig;
+  if (guided) {
+    // skip-layer guidance window on the progress step/num_steps, inclusive at both ends
+    const double prog = (double)a->step / (double)a->num_steps;
+    const bool active = (double)a->slg_start <= prog && prog <= (double)a->slg_stop;
+    uint64_t mask = 0;
+    if (active)
+      for (int i = 0; i < a->n_skip; ++i) mask |= 1ULL << a->uncond_skip_layers[i];
+    p.lat.p[1] = a->x;
+    p.txt.p[1] = a->text_uncond;
+    p.sigma[1] = sig;
+    p.skip[1] = mask;
+  }
+  p.vel = c.vel;
+  if ((s = run_forward(h, p, c, (hipStream_t)stream))) return s;
+  // A12: FP32 CFG combine + Euler, in place on x
+  ProfScope ps(h, PC_CFG, (hipStream_t)stream);
+  HIP_TRY(h, launch_cfg_euler(c.vel, guided ? c.vel + lat : nullptr, a->x, lat, a->cfg_scale, sig, sig_next,
+                              (hipStream_t)stream));
+  return MOSS_OK;
+}
+
+int moss_cfg_euler(const float* v_cond, const float* v_uncond, float* x, int64_t n, float cfg, float sigma,
+                   float sigma_next, void* stream) {
+  if (!v_cond || !x || n < 0 || !std::isfinite(cfg) || cfg < 1.f || (!v_uncond && cfg != 1.f)) {
+    g_thread_error = "moss_cfg_euler: v_cond and x must be non-NULL, cfg >= 1, and v_uncond NULL only when cfg == 1";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if ((reinterpret_cast<uintptr_t>(v_cond) | reinterpret_cast<uintptr_t>(v_uncond) | reinterpret_cast<uintptr_t>(x)) & 15) {
+    g_thread_error = "moss_cfg_euler: pointers must be 16-byte aligned";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = launch_cfg_euler(v_cond, cfg == 1.f ? nullptr : v_uncond, x, n, cfg, sigma, sigma_next,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_thread_error = fmt("moss_cfg_euler launch failed: %s", hipGetErrorString(e));
+    return MOSS_ERR_DEVICE;
+  }
+  return MOSS_OK;
+}
+
+int moss_dit_modulation(moss_dit* h, const float* sigma, int32_t batch, void* mod, void* stream) {
+  int s = enter(h);
+  if (s) return s;
+  if (!sigma || !mod || batch < 1 || batch > kMaxBatch) return fail(h, MOSS_ERR_INVALID_ARGUMENT, "bad modulation arguments");
+  for (int b = 0; b < batch; ++b)
+    if (!(sigma[b] >= 0.f && sigma[b] <= 1.f)) return fail(h, MOSS_ERR_INVALID_ARGUMENT, "sigma outside [0, 1]");
+  if ((s = ensure_ws(h, carve(h, batch, 1, 1, 4, nullptr, nullptr)))) return s;
+  Carve c;
+  carve(h, batch, 1, 1, 4, (char*)h->ws, &c);
+  c.mod = (uint16_t*)mod;
+  return run_modulation(h, sigma, batch, c, (hipStream_t)stream);
+}
+
+int moss_dit_block(moss_dit* h, int32_t layer, void* x, int32_t batch, int32_t text_len, int32_t grid_h, int32_t grid_w,
+                   const void* mod, int64_t mod_stride, const moss_block_taps* taps, void* stream) {
+  int s = enter(h);
+  if (s) return s;
+  std::string msg;
+  if (layer < 0 || layer >= h->cfg.num_layers || !x || !mod || batch < 1 || batch > kMaxBatch)
+    return fail(h, MOSS_ERR_INVALID_ARGUMENT, "bad block arguments");
+  if ((s = check_latent(2 * grid_h, 2 * grid_w, msg)) || (s = check_text_len(text_len, msg))) return fail(h, s, msg);
+  if (mod_stride < h->mod_rows()) return fail(h, MOSS_ERR_INVALID_ARGUMENT, "mod_stride smaller than one sample's modulation");
+  if (taps && taps->struct_size != sizeof(moss_block_taps)) return fail(h, MOSS_ERR_ABI_MISMATCH, "moss_block_taps.struct_size mismatch");
+  const int N = grid_h * grid_w, S = text_len + N;
+  if ((s = ensure_ws(h, carve(h, batch, S, N, 4, nullptr, nullptr)))) return s;
+  Carve c;
+  carve(h, batch, S, N, 4, (char*)h->ws, &c);
+  return run_block(h, layer, (uint16_t*)x, batch, text_len, grid_w, S, (const uint16_t*)mod, (long)mod_stride, c, taps,
+                   (hipStream_t)stream);
+}
+
+int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, int32_t text_len, int32_t grid_w,
+                   int32_t rope, void* stream) {
+  if (!qkv || !out || batch < 1 || seq < 1 || heads < 1 || text_len < 0 || text_len > seq) {
+    g_thread_error = "moss_attention: bad arguments";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  const int n_img = seq - text_len;
+  if (rope && (grid_w < 1 || n_img % grid_w != 0 || grid_w > kRopeMaxPos || n_img / grid_w > kRopeMaxPos)) {
+    g_thread_error = "moss_attention: image rows must fill a grid of width grid_w (<= 256 per side)";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const long D = (long)heads * kHeadDim;
+  hipError_t e = hipSuccess;
+  if (rope) {
+    float* tab = nullptr;
+    e = rope_table(1.0e4f, &tab);
+    if (e == hipSuccess)
+      e = launch_rope_inplace((uint16_t*)qkv, batch, seq, text_len, grid_w, heads, 3 * D, tab,
+                              tab + kRopeMaxPos * (kHeadDim / 4), st);
+  }
+  if (e == hipSuccess) {
+    AttnArgs at;
+    at.qkv = (const uint16_t*)qkv;
+    at.out = (uint16_t*)out;
+    at.B = batch;
+    at.S = seq;
+    at.H = heads;
+    at.ld_qkv = 3 * D;
+    at.ld_out = D;
+    at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+    e = launch_attention(at, st);
+  }
+  if (e != hipSuccess) {
+    g_thread_error = fmt("moss_attention failed: %s", hipGetErrorString(e));
+    return MOSS_ERR_DEVICE;
+  }
+  return MOSS_OK;
+}
+
+int moss_gemm_bf16(const void* A, const void* W, float* out, int32_t M, int32_t N, int32_t K, void* stream) {
+  if (!A || !W || !out || M < 1 || N < 1 || K < 1 || K % 64 != 0 || N % 128 != 0) {
+    g_thread_error = "moss_gemm_bf16: need non-NULL pointers, K % 64 == 0, N % 128 == 0";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = launch_gemm(gemm_args((const uint16_t*)A, (const uint16_t*)W, M, N, K, out, N), EPI_F32,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_thread_error = fmt("moss_gemm_bf16 failed: %s", hipGetErrorString(e));
+    return MOSS_ERR_DEVICE;
+  }
+  return MOSS_OK;
+}
+
+int moss_dit_profile_enable(moss_dit* h, int32_t enable) {
+  const int s = enter(h);
+  if (s) return s;
+  h->prof_on = enable != 0;
+  return MOSS_OK;
+}
+
+int moss_dit_profile_read(moss_dit* h, double* ms, int64_t* launches) {
+  const int s = enter(h);
+  if (s) return s;
+  if (!ms || !launches) return fail(h, MOSS_ERR_INVALID_ARGUMENT, "ms and launches must not be NULL");
+  HIP_TRY(h, hipDeviceSynchronize());
+  for (int c = 0; c < MOSS_PROF_CLASSES; ++c) {
+    double sum = 0.0;
+    for (size_t i = 0; i < h->prof_used[c]; ++i) {
+      float t = 0.f;
+      HIP_TRY(h, hipEventElapsedTime(&t, h->prof_ev[c][i].first, h->prof_ev[c][i].second));
+      sum += t;
+    }
+    ms[c] = sum;
+    launches[c] = (int64_t)h->prof_used[c];
+    h->prof_used[c] = 0;
+  }
+  return MOSS_OK;
+}
+
+}  // extern "C"

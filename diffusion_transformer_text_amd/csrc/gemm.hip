@@ -1,0 +1,279 @@
+// bf16 MFMA GEMM with fused epilogues for the DiT projections (gfx950).
+//
+// The projections of a joint block are plain bf16 GEMMs with fp32 accumulation (MossInfer
+// integration guide, "Quality tier": the reference tier runs the DiT's bf16 GEMMs). Their
+// elementwise tails are fused into the GEMM epilogue, as the Qwen-Image 2.1 cookbook does with
+// separate kernels ("Lossless RoPE fusion", "Lossless MLP and residual fusion"): the rotary turn of
+// q/k, the gated residual add and the SiLU-multiply of the SwiGLU FFN.
+//
+// Tiling: a workgroup of 4 waves (2 x 2) computes a BM (tokens) x BN (features) tile, BK = 64,
+// with both operands staged through a double-buffered, XOR-swizzled LDS tile. Each wave issues
+// v_mfma_f32_32x32x16_bf16 with the WEIGHT fragment as the MFMA A operand and the activation
+// fragment as the B operand, so the accumulator of lane l holds token (l % 32) and, per group of
+// four registers, four consecutive output features: the epilogue stores 8-byte runs and finds the
+// rotary pair (2k, 2k+1) and the gate/up pair in its own registers.
+#include "common.h"
+#include "kernels.h"
+
+namespace moss {
+namespace {
+
+constexpr int BK = 64;
+constexpr int kThreads = 256;
+constexpr int kGroupM = 8;   // tile rows per L2 group
+
+template <int BM, int BN>
+struct Tile {
+  static constexpr int WM = BM / 2, WN = BN / 2;        // wave tile
+  static constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 MFMA blocks per wave
+  static constexpr int A_CHUNKS = BM * BK / 8 / kThreads;
+  static constexpr int W_CHUNKS = BN * BK / 8 / kThreads;
+  static constexpr int STAGE = (BM + BN) * BK;          // elements per LDS stage
+};
+
+// Element offset of 16-byte chunk c of row r in a [rows][BK] bf16 LDS tile. The chunk index is
+// XORed with the row's low 3 bits so that the 8 consecutive rows read by 8 consecutive lanes of a
+// fragment load fall into 8 distinct bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+
+// Maps the linear workgroup id to a (tile_m, tile_n) pair. Workgroups are dispatched round-robin
+// over the 8 XCDs; the remap gives each XCD a contiguous run of tiles, and within the run tiles go
+// in groups of kGroupM tile rows so the workgroups resident on one XCD share A rows and W columns
+// in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int nM, int nN, int& tm, int& tn) {
+  const int nt = gridDim.x;
+  int lin = blockIdx.x;
+  if ((nt & 7) == 0) lin = (lin & 7) * (nt >> 3) + (lin >> 3);
+  const int per_group = kGroupM * nN;
+  const int group = lin / per_group;
+  const int first_m = group * kGroupM;
+  const int gsize = min(nM - first_m, kGroupM);
+  const int in_group = lin - group * per_group;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
+  using T = Tile<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nN = p.N / BN, nM = (p.M + BM - 1) / BM;
+  int tm, tn;
+  tile_coords(nM, nN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // ---- global -> register assignment: chunk (row = tid/8 + 32 j, c = tid % 8) ----
+  const int ld_row = tid >> 3, ld_c = tid & 7;
+  uint32_t a_off[T::A_CHUNKS];
+  uint32_t w_off[T::W_CHUNKS];
+#pragma unroll
+  for (int j = 0; j < T::A_CHUNKS; ++j) {
+    const int r = min(m0 + ld_row + 32 * j, p.M - 1);
+    a_off[j] = (uint32_t)(r * p.lda + ld_c * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < T::W_CHUNKS; ++j) {
+    const int r = n0 + ld_row + 32 * j;
+    w_off[j] = (uint32_t)(r * p.ldw + ld_c * 8);
+  }
+  const int st_off = ld_row * BK + ((ld_c ^ (ld_row & 7)) << 3);   // + j * 32 * BK
+
+  uint4 ra[T::A_CHUNKS], rw[T::W_CHUNKS];
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < T::A_CHUNKS; ++j) ra[j] = *reinterpret_cast<const uint4*>(p.A + a_off[j] + k0);
+#pragma unroll
+    for (int j = 0; j < T::W_CHUNKS; ++j) rw[j] = *reinterpret_cast<const uint4*>(p.W + w_off[j] + k0);
+  };
+  auto store_tile = [&](int stage) {
+    uint16_t* sA = lds + stage * T::STAGE;
+    uint16_t* sW = sA + BM * BK;
+#pragma unroll
+    for (int j = 0; j < T::A_CHUNKS; ++j) *reinterpret_cast<uint4*>(sA + st_off + j * 32 * BK) = ra[j];
+#pragma unroll
+    for (int j = 0; j < T::W_CHUNKS; ++j) *reinterpret_cast<uint4*>(sW + st_off + j * 32 * BK) = rw[j];
+  };
+
+  floatx16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int fr = lane & 31, fh = lane >> 5;
+  const int KT = p.K / BK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) load_tile(kt + 1);
+    const uint16_t* sA = lds + cur * T::STAGE;
+    const uint16_t* sW = sA + BM * BK;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      bf16x8 fa[T::TM], fw[T::TN];
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * T::WM + i * 32 + fr, 2 * s + fh));
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j)
+        fw[j] = *reinterpret_cast<const bf16x8*>(sW + swz(wn * T::WN + j * 32 + fr, 2 * s + fh));
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: acc[i][j][4g + e] = C[token m, feature n + e] ----
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) {
+    const int m = m0 + wm * T::WM + i * 32 + fr;
+    if (m >= p.M) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // feature blocks (2q, 2q+1) of this wave are the gate and up rows of the same 32 h-columns
+      uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+      for (int q = 0; q < T::TN / 2; ++q) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int hc = (n0 + wn * T::WN) / 2 + q * 32 + 8 * g + 4 * fh;
+          float h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[i][2 * q][4 * g + e]) * acc[i][2 * q + 1][4 * g + e];
+          uint2 v;
+          v.x = pack2_bf16(h[0], h[1]);
+          v.y = pack2_bf16(h[2], h[3]);
+          *reinterpret_cast<uint2*>(out + (long)m * p.ldo + hc) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * T::WN + j * 32 + 8 * g + 4 * fh;
+          float c[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[e] = acc[i][j][4 * g + e];
+          if constexpr (EPI == EPI_BF16) {
+            const long orow = (long)(m / p.seg) * p.seg_stride + p.seg_off + m % p.seg;
+            uint2 v;
+            v.x = pack2_bf16(c[0], c[1]);
+            v.y = pack2_bf16(c[2], c[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow * p.ldo + n) = v;
+          } else if constexpr (EPI == EPI_QKV_ROPE) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c[e] = round_bf16(c[e]);
+            const int t = m % p.S;
+            if (n < p.rope_cols && t >= p.T) {
+              const int ni = t - p.T;
+              const int dim = n & (kHeadDim - 1);
+              const int pos = (dim < kHeadDim / 2) ? ni / p.grid_w : ni % p.grid_w;
+              const int k0 = (dim & (kHeadDim / 2 - 1)) >> 1;
+#pragma unroll
+              for (int pr = 0; pr < 2; ++pr) {
+                const float cs = p.rope_cos[pos * (kHeadDim / 4) + k0 + pr];
+                const float sn = p.rope_sin[pos * (kHeadDim / 4) + k0 + pr];
+                const float a = c[2 * pr], b = c[2 * pr + 1];
+                c[2 * pr] = a * cs - b * sn;
+                c[2 * pr + 1] = a * sn + b * cs;
+              }
+            }
+            uint2 v;
+            v.x = pack2_bf16(c[0], c[1]);
+            v.y = pack2_bf16(c[2], c[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (long)m * p.ldo + n) = v;
+          } else if constexpr (EPI == EPI_GATED_RES) {
+            uint16_t* xo = static_cast<uint16_t*>(p.out) + (long)m * p.ldo + n;
+            const uint2 xv = *reinterpret_cast<const uint2*>(xo);
+            const uint2 gv = *reinterpret_cast<const uint2*>(p.gate + (long)(m / p.rows_per_sample) * p.gate_stride + n);
+            const float x0 = __uint_as_float(xv.x << 16), x1 = __uint_as_float(xv.x & 0xffff0000u);
+            const float x2 = __uint_as_float(xv.y << 16), x3 = __uint_as_float(xv.y & 0xffff0000u);
+            const float g0 = __uint_as_float(gv.x << 16), g1 = __uint_as_float(gv.x & 0xffff0000u);
+            const float g2 = __uint_as_float(gv.y << 16), g3 = __uint_as_float(gv.y & 0xffff0000u);
+            uint2 v;
+            v.x = pack2_bf16(x0 + g0 * c[0], x1 + g1 * c[1]);
+            v.y = pack2_bf16(x2 + g2 * c[2], x3 + g3 * c[3]);
+            *reinterpret_cast<uint2*>(xo) = v;
+          } else if constexpr (EPI == EPI_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (long)m * p.ldo + n) =
+                make_float4(c[0], c[1], c[2], c[3]);
+          } else if constexpr (EPI == EPI_F32_UNPATCH) {
+            const int b = m / p.n_img, ni = m % p.n_img;
+            const int gw = p.lat_w / 2;
+            const int y = 2 * (ni / gw), x = 2 * (ni % gw);
+            const int ch = n >> 2;
+            float* v = static_cast<float*>(p.out) + (((long)b * p.C + ch) * p.lat_h + y) * p.lat_w + x;
+            *reinterpret_cast<float2*>(v) = make_float2(c[0], c[1]);
+            *reinterpret_cast<float2*>(v + p.lat_w) = make_float2(c[2], c[3]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const GemmArgs& a, int epi, hipStream_t stream) {
+  const int nM = (a.M + BM - 1) / BM, nN = a.N / BN;
+  dim3 grid(nM * nN), block(kThreads);
+  switch (epi) {
+    case EPI_BF16: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_BF16>), grid, block, 0, stream, a); break;
+    case EPI_QKV_ROPE: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_QKV_ROPE>), grid, block, 0, stream, a); break;
+    case EPI_GATED_RES: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_GATED_RES>), grid, block, 0, stream, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_SWIGLU>), grid, block, 0, stream, a); break;
+    case EPI_F32: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_F32>), grid, block, 0, stream, a); break;
+    case EPI_F32_UNPATCH:
+      // the output projection has N = C*4 = 128: only the 128-wide tile is ever used for it
+      if constexpr (BN == 128) {
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_F32_UNPATCH>), grid, block, 0, stream, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+__global__ void interleave_gate_up_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int F, int D) {
+  const long row = blockIdx.x;               // destination row
+  const int grp = (int)(row / 64), w = (int)(row % 64);
+  const long srow = (w < 32) ? (long)grp * 32 + w : (long)F + (long)grp * 32 + (w - 32);
+  const uint4* s = reinterpret_cast<const uint4*>(src + srow * D);
+  uint4* d = reinterpret_cast<uint4*>(dst + row * D);
+  for (int i = threadIdx.x; i < D / 8; i += blockDim.x) d[i] = s[i];
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream) {
+  if (a.M <= 0) return hipSuccess;
+  if (a.K % BK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
+  if ((long)a.M * a.lda >= (1L << 31) || (long)a.N * a.ldw >= (1L << 31)) return hipErrorInvalidValue;
+  // SwiGLU pairs feature blocks inside a wave: the wave's feature width must hold whole 64-row groups.
+  const bool big_n = (a.N % 256 == 0);
+  const long tiles256 = (long)((a.M + 255) / 256) * (a.N / 256);
+  if (big_n && epi != EPI_F32_UNPATCH && a.M > 1024 && tiles256 >= 256) return launch_tile<256, 256>(a, epi, stream);
+  if (a.N % 128 == 0) return launch_tile<128, 128>(a, epi, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_interleave_gate_up(const uint16_t* src, uint16_t* dst, int F, int D, hipStream_t stream) {
+  if (F % 32 != 0 || D % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(interleave_gate_up_kernel, dim3(2 * F), dim3(256), 0, stream, src, dst, F, D);
+  return hipGetLastError();
+}
+
+}  // namespace moss

@@ -1,0 +1,110 @@
+// Host-side launchers of the MOSS-Image DiT kernels (internal to the library; not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moss {
+
+constexpr int kMaxBatch = 8;       // samples per forward call
+constexpr int kRopeMaxPos = 256;   // grid side limit: 4096 px / 16 px per token
+constexpr int kHeadDim = 128;
+
+// ---------------------------------------------------------------------------------------------
+// bf16 MFMA GEMM: out[m, n] = epilogue(sum_k A[m, k] * W[n, k]); A [M, K] and W [N, K] row-major.
+// ---------------------------------------------------------------------------------------------
+enum Epilogue {
+  EPI_BF16 = 0,         // out bf16 [m, n] (rows remapped by seg/seg_stride/seg_off)
+  EPI_QKV_ROPE = 1,     // out bf16; columns < rope_cols of image rows get the axial rotary turn
+  EPI_GATED_RES = 2,    // out bf16 residual in place: x = bf16(x + gate[b, n] * acc)
+  EPI_SWIGLU = 3,       // W holds [gate | up] interleaved in 32-row groups; out h = bf16(SiLU(g) * u)
+  EPI_F32 = 4,          // out fp32 [m, n]
+  EPI_F32_UNPATCH = 5,  // out fp32 velocity [B, C, lat_h, lat_w]: m = image token, n = c*4 + dy*2 + dx
+};
+
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* W;
+  int M, N, K;
+  long lda, ldw;
+  void* out;
+  long ldo;
+  // EPI_BF16 row remap: out_row = (m / seg) * seg_stride + seg_off + m % seg
+  int seg, seg_stride, seg_off;
+  // EPI_GATED_RES: gate[(m / rows_per_sample) * gate_stride + n]
+  const uint16_t* gate;
+  int rows_per_sample;
+  long gate_stride;
+  // EPI_QKV_ROPE: sequence S = T text rows + image rows on a grid of width grid_w
+  const float* rope_cos;
+  const float* rope_sin;
+  int S, T, grid_w, rope_cols;
+  // EPI_F32_UNPATCH
+  int C, lat_h, lat_w, n_img;
+};
+
+// Picks a tile shape for (M, N) and launches. Returns hipSuccess or the launch error.
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream);
+// Interleave W_gate_up [2F, D] = [gate rows | up rows] into 32-row groups [g0 | u0 | g1 | u1 | ...].
+hipError_t launch_interleave_gate_up(const uint16_t* src, uint16_t* dst, int F, int D, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// LayerNorm + modulation: out[r] = bf16(LN(x[in_row(r)]) * (1 + scale[b]) + shift[b])
+// ---------------------------------------------------------------------------------------------
+struct LnModArgs {
+  const uint16_t* x;
+  uint16_t* out;
+  int rows, D;
+  int seg, seg_stride, seg_off;   // in_row = (r / seg) * seg_stride + seg_off + r % seg
+  int rows_per_sample;            // b = r / rows_per_sample
+  const uint16_t* shift;          // shift[b * mod_stride + i]
+  const uint16_t* scale;
+  long mod_stride;
+  float eps;
+};
+hipError_t launch_ln_mod(const LnModArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// Exact attention over qkv [B*S, 3*H*128] (q | k | v, head h at columns h*128), out o [B*S, H*128].
+// ---------------------------------------------------------------------------------------------
+struct AttnArgs {
+  const uint16_t* qkv;
+  uint16_t* out;
+  int B, S, H;
+  long ld_qkv, ld_out;
+  float scale_log2;   // log2(e) / sqrt(d)
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+
+// In-place axial rotary turn of the q and k columns of the image rows of qkv (standalone attention).
+hipError_t launch_rope_inplace(uint16_t* qkv, int B, int S, int T, int grid_w, int H, long ld,
+                               const float* cos_t, const float* sin_t, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// Timestep embedding + modulation
+// ---------------------------------------------------------------------------------------------
+// u[b, :] = bf16(SiLU(bf16(W_t2 bf16(SiLU(W_t1 e(sigma_b)))))) stored as fp32, e(sigma) sinusoidal.
+struct SigmaBatch {
+  float s[kMaxBatch];
+};
+hipError_t launch_time_mlp(SigmaBatch sigma, int B, const uint16_t* t_w1, const uint16_t* t_w2,
+                           int temb, float flow_multiplier, float* u_out, hipStream_t stream);
+// m[b, r] = bf16(sum_j W[r, j] * u[b, j]) for r < rows (all modulation rows of every block + final).
+hipError_t launch_mod_gemv(const uint16_t* W, int rows, int temb, const float* u, int B,
+                           uint16_t* m_out, long m_stride, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// Embedding inputs, guidance
+// ---------------------------------------------------------------------------------------------
+struct PtrBatch {
+  const float* p[kMaxBatch];
+};
+// tokens[b*N + n, ch*4 + dy*2 + dx] = bf16(latent_b[ch, 2r+dy, 2c+dx]), n = r*(w/2) + c
+hipError_t launch_patchify(PtrBatch latents, int B, int C, int h, int w, uint16_t* tokens, hipStream_t stream);
+// x[b*S + t, :] = bf16(text_b[t, :]) for t < T
+hipError_t launch_text_cast(PtrBatch text, int B, int T, int D, int S, uint16_t* x, hipStream_t stream);
+// x = x + (sigma_next - sigma) * (v_u + cfg * (v_c - v_u)); v_u == nullptr means v = v_c.
+hipError_t launch_cfg_euler(const float* v_c, const float* v_u, float* x, long n, float cfg, float sigma,
+                            float sigma_next, hipStream_t stream);
+
+}  // namespace moss

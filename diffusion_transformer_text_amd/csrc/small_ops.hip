@@ -1,0 +1,188 @@
+// Small HBM- or latency-bound kernels of the denoising step: timestep embedding and modulation,
+// patchify and text cast, and the fused FP32 guidance + Euler update.
+#include "common.h"
+#include "kernels.h"
+
+namespace moss {
+namespace {
+
+// Time MLP for one sample per workgroup. Sinusoidal features of t = flow_multiplier * sigma
+// (cos half, then sin half, frequencies exp(-ln(1e4) k / 128)), then u = SiLU(W_t2 SiLU(W_t1 e)).
+// Each stored intermediate is rounded to bf16, as a bf16 model holds it between layers. The angle
+// and the trigonometric functions are evaluated in fp64: t reaches 1000 and fp32 would lose the
+// phase to ~1e-4.
+__global__ void time_mlp_kernel(SigmaBatch sigma, const uint16_t* __restrict__ w1,
+                                const uint16_t* __restrict__ w2, int E, float flow_multiplier,
+                                float* __restrict__ u_out) {
+  __shared__ float e[256];
+  __shared__ float a1[1024];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const double tt = (double)flow_multiplier * (double)sigma.s[b];
+  if (t < 128) {
+    const double f = exp(-log(1.0e4) * (double)t / 128.0);
+    e[t] = round_bf16((float)cos(tt * f));
+    e[t + 128] = round_bf16((float)sin(tt * f));
+  }
+  __syncthreads();
+  if (t < E) {
+    const uint16_t* row = w1 + (long)t * 256;
+    float acc = 0.f;
+    for (int j = 0; j < 256; ++j) acc += bf16_to_f32(row[j]) * e[j];
+    a1[t] = round_bf16(silu_f32(acc));
+  }
+  __syncthreads();
+  if (t < E) {
+    const uint16_t* row = w2 + (long)t * E;
+    float acc = 0.f;
+    for (int j = 0; j < E; ++j) acc += bf16_to_f32(row[j]) * a1[j];
+    const float temb = round_bf16(acc);
+    u_out[(long)b * E + t] = round_bf16(silu_f32(temb));
+  }
+}
+
+// m[b, r] = bf16(W[r, :] . u[b, :]) for temb = 256: 32 lanes per row (16 bytes each), two rows per
+// wave instruction, grid-stride over row pairs. Reads every modulation weight once per call.
+__global__ __launch_bounds__(256) void mod_gemv_kernel(const uint16_t* __restrict__ W, int rows,
+                                                       const float* __restrict__ u, int B,
+                                                       uint16_t* __restrict__ m, long m_stride) {
+  __shared__ float us[kMaxBatch * 256];
+  for (int i = threadIdx.x; i < B * 256; i += blockDim.x) us[i] = u[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, half = lane >> 5, sl = lane & 31;
+  const int wave_global = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * 4;
+  for (int pr = wave_global; pr * 2 < rows; pr += nwaves) {
+    const int row = pr * 2 + half;
+    const bool ok = row < rows;
+    uint4 wv = make_uint4(0, 0, 0, 0);
+    if (ok) wv = *reinterpret_cast<const uint4*>(W + (long)row * 256 + sl * 8);
+    const uint32_t wr[4] = {wv.x, wv.y, wv.z, wv.w};
+    float wf[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wf[2 * j] = __uint_as_float(wr[j] << 16);
+      wf[2 * j + 1] = __uint_as_float(wr[j] & 0xffff0000u);
+    }
+    for (int b = 0; b < B; ++b) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += wf[j] * us[b * 256 + sl * 8 + j];
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (ok && sl == 0) m[(long)b * m_stride + row] = f32_to_bf16(acc);
+    }
+  }
+}
+
+__global__ void patchify_kernel(PtrBatch lat, int B, int C, int h, int w, uint16_t* __restrict__ tokens) {
+  const int P = C * 4;
+  const int gw = w / 2, N = (h / 2) * gw;
+  const long total = (long)B * N * P;
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (long)gridDim.x * blockDim.x) {
+    const int j = (int)(idx % P);
+    const long row = idx / P;
+    const int b = (int)(row / N), n = (int)(row % N);
+    const int r = n / gw, c = n % gw;
+    const int ch = j >> 2, dy = (j >> 1) & 1, dx = j & 1;
+    tokens[idx] = f32_to_bf16(lat.p[b][((long)ch * h + 2 * r + dy) * w + 2 * c + dx]);
+  }
+}
+
+__global__ void text_cast_kernel(PtrBatch text, int B, int T, int D, int S, uint16_t* __restrict__ x) {
+  const long per = (long)T * D / 4;
+  const long total = (long)B * per;
+  for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (long)gridDim.x * blockDim.x) {
+    const int b = (int)(idx / per);
+    const long e = (idx % per) * 4;
+    const long t = e / D, i = e % D;
+    const float4 v = *reinterpret_cast<const float4*>(text.p[b] + e);
+    uint2 o;
+    o.x = pack2_bf16(v.x, v.y);
+    o.y = pack2_bf16(v.z, v.w);
+    *reinterpret_cast<uint2*>(x + ((long)b * S + t) * D + i) = o;
+  }
+}
+
+// Fused FP32 classifier-free guidance and flow-matching Euler step ("MOSS-Image" SGLang cookbook,
+// "Guidance and precision": CFG arithmetic and scheduler updates in FP32).
+__global__ void cfg_euler_kernel(const float* __restrict__ vc, const float* __restrict__ vu, float* __restrict__ x,
+                                 long n, float cfg, float dt) {
+  const long n4 = n / 4;
+  const long stride = (long)gridDim.x * blockDim.x;
+  const long t0 = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (long i = t0; i < n4; i += stride) {
+    const float4 c = reinterpret_cast<const float4*>(vc)[i];
+    float4 xv = reinterpret_cast<float4*>(x)[i];
+    float4 v = c;
+    if (vu != nullptr) {
+      const float4 u = reinterpret_cast<const float4*>(vu)[i];
+      v.x = u.x + cfg * (c.x - u.x);
+      v.y = u.y + cfg * (c.y - u.y);
+      v.z = u.z + cfg * (c.z - u.z);
+      v.w = u.w + cfg * (c.w - u.w);
+    }
+    xv.x = xv.x + dt * v.x;
+    xv.y = xv.y + dt * v.y;
+    xv.z = xv.z + dt * v.z;
+    xv.w = xv.w + dt * v.w;
+    reinterpret_cast<float4*>(x)[i] = xv;
+  }
+  for (long i = n4 * 4 + t0; i < n; i += stride) {
+    float v = vc[i];
+    if (vu != nullptr) v = vu[i] + cfg * (vc[i] - vu[i]);
+    x[i] = x[i] + dt * v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_time_mlp(SigmaBatch sigma, int B, const uint16_t* t_w1, const uint16_t* t_w2,
+                           int temb, float flow_multiplier, float* u_out, hipStream_t stream) {
+  if (temb > 1024 || temb < 1) return hipErrorInvalidValue;
+  const int threads = temb < 128 ? 128 : ((temb + 63) / 64) * 64;
+  hipLaunchKernelGGL(time_mlp_kernel, dim3(B), dim3(threads), 0, stream, sigma, t_w1, t_w2, temb,
+                     flow_multiplier, u_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mod_gemv(const uint16_t* W, int rows, int temb, const float* u, int B, uint16_t* m_out,
+                           long m_stride, hipStream_t stream) {
+  if (temb != 256 || B > kMaxBatch) return hipErrorInvalidValue;
+  const int pairs = (rows + 1) / 2;
+  int grid = (pairs + 3) / 4;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(mod_gemv_kernel, dim3(grid), dim3(256), 0, stream, W, rows, u, B, m_out, m_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_patchify(PtrBatch latents, int B, int C, int h, int w, uint16_t* tokens, hipStream_t stream) {
+  const long total = (long)B * (h / 2) * (w / 2) * C * 4;
+  int grid = (int)((total + 255) / 256);
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL(patchify_kernel, dim3(grid), dim3(256), 0, stream, latents, B, C, h, w, tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_text_cast(PtrBatch text, int B, int T, int D, int S, uint16_t* x, hipStream_t stream) {
+  if (D % 4 != 0) return hipErrorInvalidValue;
+  const long total = (long)B * T * D / 4;
+  int grid = (int)((total + 255) / 256);
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL(text_cast_kernel, dim3(grid), dim3(256), 0, stream, text, B, T, D, S, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_cfg_euler(const float* v_c, const float* v_u, float* x, long n, float cfg, float sigma,
+                            float sigma_next, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if ((reinterpret_cast<uintptr_t>(v_c) | reinterpret_cast<uintptr_t>(v_u) | reinterpret_cast<uintptr_t>(x)) & 15)
+    return hipErrorInvalidValue;
+  long grid = (n / 4 + 255) / 256;
+  if (grid < 1) grid = 1;
+  if (grid > 2048) grid = 2048;
+  hipLaunchKernelGGL(cfg_euler_kernel, dim3((unsigned)grid), dim3(256), 0, stream, v_c, v_u, x, n, cfg,
+                     sigma_next - sigma);
+  return hipGetLastError();
+}
+
+}  // namespace moss

@@ -1,0 +1,74 @@
+/* moss_dit_ops.h -- kernel-level entry points of the MOSS-Image DiT library.
+ *
+ * These expose the pieces of one forward pass on their own, for parity checks of each step against
+ * an independent implementation and for per-kernel measurement. They follow the conventions of
+ * moss_dit.h (status codes, borrowed device pointers, enqueue on `stream`, host-side validation).
+ */
+#ifndef MOSS_DIT_OPS_H
+#define MOSS_DIT_OPS_H
+
+#include <stdint.h>
+#include "moss_dit.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Per-block modulation ("MOSS-Image" InvokeAI guide, "Transformer formats", names the time-embedding
+ * and modulation layers): u = SiLU(W_t2 SiLU(W_t1 e(sigma))), then for every block
+ * (shift1, scale1, gate1, shift2, scale2, gate2) = W_mod,l u and for the final layer
+ * (shift_f, scale_f) = W_fmod u.
+ * sigma: host fp32 [B]. mod: device bf16 [B, num_layers*6*hidden + 2*hidden] (block l's six chunks
+ * at l*6*hidden, the final pair at num_layers*6*hidden). */
+int moss_dit_modulation(moss_dit* h, const float* sigma, int32_t batch, void* mod, void* stream);
+
+/* Optional outputs of moss_dit_block (device pointers, NULL = not written), rows = B*S:
+ *   a      bf16 [rows, D]   LN1-modulated input of the qkv projection
+ *   qkv    bf16 [rows, 3D]  q | k | v, q and k rotated on image rows
+ *   o      bf16 [rows, D]   attention output
+ *   attn   fp32 [rows, D]   o W_o^T (branch output before the gated add)
+ *   x1     bf16 [rows, D]   residual after the attention branch
+ *   a2     bf16 [rows, D]   LN2-modulated input of the FFN
+ *   h      bf16 [rows, F]   SiLU(a2 W_g^T) * (a2 W_u^T)
+ *   ffn    fp32 [rows, D]   h W_down^T (branch output before the gated add) */
+typedef struct {
+  uint32_t struct_size;
+  void *a, *qkv, *o, *attn, *x1, *a2, *h, *ffn;
+} moss_block_taps;
+void moss_block_taps_init(moss_block_taps* t, uint32_t size);
+
+/* One joint block `layer` of the handle's weights on a residual stream x (device bf16 [B, S, D],
+ * updated in place), S = text_len + grid_h*grid_w, the first text_len rows of each sample being
+ * text. mod: device bf16 [B, mod_stride] laid out as moss_dit_modulation writes it. */
+int moss_dit_block(moss_dit* h, int32_t layer, void* x, int32_t batch, int32_t text_len, int32_t grid_h,
+                   int32_t grid_w, const void* mod, int64_t mod_stride, const moss_block_taps* taps,
+                   void* stream);
+
+/* Exact attention at head_dim 128 on packed qkv (device bf16 [B, S, 3*H*128], q | k | v), out device
+ * bf16 [B, S, H*128]. rope != 0: q and k of the image rows (sequence index >= text_len, grid of width
+ * grid_w) are first turned by the axial rotary embedding (theta 1e4) -- in place, qkv is modified. */
+int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, int32_t text_len,
+                   int32_t grid_w, int32_t rope, void* stream);
+
+/* bf16 GEMM out = A W^T with an fp32 output (device A bf16 [M, K], W bf16 [N, K], out fp32 [M, N]);
+ * K % 64 == 0, N % 128 == 0. */
+int moss_gemm_bf16(const void* A, const void* W, float* out, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* Per-kernel-class timing with HIP events recorded on the call's stream around every launch of the
+ * handle's compute calls. Off by default; while on, each launch is bracketed by two events (a few
+ * microseconds of host overhead per launch, no change to any result). Classes, in order:
+ *   0 modulation (time MLP + modulation GEMV)   1 embed (text cast, patchify, patch GEMM)
+ *   2 LayerNorm-modulation (LN1 and LN2)          3 qkv GEMM + RoPE
+ *   4 attention                                  5 out GEMM + gated residual
+ *   6 gate/up GEMM + SiLU*mul                    7 down GEMM + gated residual
+ *   8 final layer (LN-mod + output GEMM)         9 CFG + Euler */
+#define MOSS_PROF_CLASSES 10
+int moss_dit_profile_enable(moss_dit* h, int32_t enable);
+/* Synchronises the device, writes the summed milliseconds and the launch count of each class since
+ * the last read (host arrays of MOSS_PROF_CLASSES), and resets the counters. */
+int moss_dit_profile_read(moss_dit* h, double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOSS_DIT_OPS_H */

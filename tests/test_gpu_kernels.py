@@ -1,0 +1,166 @@
+"""Kernel-level parity on the GPU: GEMM, guidance + Euler, attention (with RoPE) against the oracle.
+
+Each case logs its name and shape before touching the GPU."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import bf16_normal_bits, f32_to_bf16_bits
+from tests.gpu_util import REL_L2_BF16, REL_L2_FP32, dev_bf16, host_bf16, log, rel_l2
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+dt = pytest.importorskip("diffusion_transformer_text_amd")
+
+
+# ------------------------------------------------------------------------------------------------
+# GEMM
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(300, 256, 192), (130, 128, 64), (4196, 4096, 256), (8704, 3072, 8192)])
+def test_gemm_small_integers_bitwise(M, N, K):
+    """Small-integer bf16 inputs give exact fp32 sums: the MFMA GEMM must match bit for bit."""
+    log(f"gemm int M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    W = rng.integers(-4, 5, (N, K)).astype(np.float32)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    dt.moss_gemm_bf16(dev_bf16(f32_to_bf16_bits(A), torch), dev_bf16(f32_to_bf16_bits(W), torch), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rows = np.unique(np.concatenate([rng.integers(0, M, 200), [0, M - 1]]))
+    ref = A[rows].astype(np.float64) @ W.T.astype(np.float64)
+    np.testing.assert_array_equal(got[rows], ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(8704, 9216, 3072), (257, 384, 128)])
+def test_gemm_random_vs_fp64(M, N, K):
+    log(f"gemm random M={M} N={N} K={K}")
+    rng = np.random.default_rng(7)
+    A = bf16_normal_bits(rng, (M, K))
+    W = bf16_normal_bits(rng, (N, K), 0.02)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    dt.moss_gemm_bf16(dev_bf16(A, torch), dev_bf16(W, torch), out)
+    torch.cuda.synchronize()
+    rows = np.unique(rng.integers(0, M, 128))
+    ref = O.from_bf16_bits(A[rows]) @ O.from_bf16_bits(W).T
+    # fp32 accumulation of K bf16 products: ~sqrt(K) * 2^-24 relative
+    assert rel_l2(out.cpu().numpy()[rows], ref) < 1e-5
+
+
+# ------------------------------------------------------------------------------------------------
+# FP32 guidance + Euler
+# ------------------------------------------------------------------------------------------------
+
+def test_cfg_euler_vs_oracle_and_identities():
+    log("cfg_euler")
+    rng = np.random.default_rng(3)
+    n = 32 * 128 * 128 + 3                  # ragged tail
+    vc, vu, x = (rng.standard_normal(n).astype(np.float32) for _ in range(3))
+    sig = O.sigmas(50, 5.0).astype(np.float32)
+    s, sn = float(sig[10]), float(sig[11])
+    tc, tu, tx = (torch.from_numpy(a).cuda() for a in (vc, vu, x))
+    dt.moss_cfg_euler(tc, tu, tx, 3.0, s, sn)
+    torch.cuda.synchronize()
+    ref = O.euler_step(x.astype(np.float64), O.cfg_combine(vc.astype(np.float64), vu.astype(np.float64), 3.0), s, sn)
+    assert rel_l2(tx.cpu().numpy(), ref) <= REL_L2_FP32
+    # cfg = 1: v = v_c exactly, no negative input at all; v_c == v_u: v = v_c for any scale. Both
+    # paths then apply the same update, so they agree bit for bit; against a single rounding of the
+    # exact x + dt v_c they agree to 1 ulp (the kernel's update is one fused multiply-add).
+    outs = []
+    for vu_in, scale in ((None, 1.0), (tc.clone(), 4.5)):
+        tx = torch.from_numpy(x).cuda()
+        dt.moss_cfg_euler(tc, vu_in, tx, scale, s, sn)
+        torch.cuda.synchronize()
+        outs.append(tx.cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+    d = np.float64(np.float32(sn) - np.float32(s))
+    once = (x.astype(np.float64) + d * vc.astype(np.float64)).astype(np.float32)
+    ulp = np.abs(outs[0].view(np.int32).astype(np.int64) - once.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1 and np.mean(ulp == 0) > 0.999
+
+
+def test_cfg_euler_point_mass_lands_on_target():
+    """Driving the kernel with the point-mass field v = (x - x*)/sigma for 50 steps lands on x*."""
+    log("cfg_euler point mass")
+    rng = np.random.default_rng(4)
+    n = 4096
+    xs = rng.standard_normal(n).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
+    xs_d = torch.from_numpy(xs).cuda()
+    sig = dt.moss_sigmas(50, 5.0)
+    for i in range(50):
+        v = (x - xs_d) / float(sig[i])
+        dt.moss_cfg_euler(v, None, x, 1.0, float(sig[i]), float(sig[i + 1]))
+    torch.cuda.synchronize()
+    assert rel_l2(x.cpu().numpy(), xs) <= REL_L2_FP32
+
+
+# ------------------------------------------------------------------------------------------------
+# attention (+ RoPE)
+# ------------------------------------------------------------------------------------------------
+
+def _attn_case(B, T, gh, gw, H, seed, rows_per_head=None, heads=None):
+    S = T + gh * gw
+    log(f"attention B={B} S={S} (T={T}, grid {gh}x{gw}) H={H}")
+    rng = np.random.default_rng(seed)
+    qkv_bits = bf16_normal_bits(rng, (B, S, 3 * H * 128))
+    qkv = dev_bf16(qkv_bits, torch)
+    out = torch.empty((B, S, H * 128), dtype=torch.bfloat16, device="cuda")
+    dt.moss_attention(qkv, out, B, S, H, T, gw, rope=True)
+    torch.cuda.synchronize()
+    got = host_bf16(out)
+    x = O.from_bf16_bits(qkv_bits)
+    D = H * 128
+    errs = []
+    for b in range(B):
+        for h in (heads if heads is not None else range(H)):
+            sl = slice(h * 128, (h + 1) * 128)
+            q = O.bf16_round(O.rope_rows(x[b][:, sl], T, gw, 128, 1e4))
+            k = O.bf16_round(O.rope_rows(x[b][:, D + h * 128:D + (h + 1) * 128], T, gw, 128, 1e4))
+            v = x[b][:, 2 * D + h * 128:2 * D + (h + 1) * 128]
+            rows = np.arange(S) if rows_per_head is None else np.unique(
+                np.concatenate([rng.integers(0, S, rows_per_head), [0, T, S - 1]]))
+            ref = O.attention(q[rows], k, v, 1, 128)
+            errs.append(rel_l2(got[b][rows][:, sl], ref))
+    return max(errs)
+
+
+@pytest.mark.parametrize("B,T,gh,gw,H", [(1, 1, 0, 1, 1), (1, 3, 1, 2, 2), (2, 32, 8, 8, 2), (1, 2, 8, 16, 1),
+                                         (1, 1, 16, 16, 1), (2, 5, 5, 5, 2)])
+def test_attention_small_vs_oracle(B, T, gh, gw, H):
+    err = _attn_case(B, T, gh, gw, H, seed=B * 100 + T + gh * gw)
+    assert err <= REL_L2_BF16, err
+
+
+def test_attention_full_shape_sampled_rows():
+    """Batch 2 (cond + uncond), 24 heads x 128, 512 text + 4096 image tokens on a 64x64 grid."""
+    err = _attn_case(2, 512, 64, 64, 24, seed=0, rows_per_head=48, heads=[0, 7, 23])
+    assert err <= REL_L2_BF16, err
+
+
+def test_attention_2048_sequence_sampled_rows():
+    """One sample at 2048^2: 4096 text + 16384 image tokens (128x128 grid)."""
+    err = _attn_case(1, 4096, 128, 128, 24, seed=1, rows_per_head=32, heads=[5])
+    assert err <= REL_L2_BF16, err
+
+
+def test_attention_special_cases():
+    log("attention special cases")
+    # identical keys -> mean of V; one dominant key -> that key's value
+    S, H = 70, 1
+    rng = np.random.default_rng(9)
+    x = np.zeros((1, S, 3 * 128))
+    x[0, :, :128] = rng.standard_normal((S, 128))
+    x[0, :, 128:256] = rng.standard_normal((1, 128))
+    x[0, :, 256:] = rng.standard_normal((S, 128))
+    bits = f32_to_bf16_bits(x.astype(np.float32))
+    out = torch.empty((1, S, 128), dtype=torch.bfloat16, device="cuda")
+    dt.moss_attention(dev_bf16(bits, torch), out, 1, S, H, S, 1, rope=False)
+    torch.cuda.synchronize()
+    vmean = O.from_bf16_bits(bits)[0, :, 256:].mean(0)
+    assert rel_l2(host_bf16(out)[0], np.repeat(vmean[None], S, 0)) < 5e-3
