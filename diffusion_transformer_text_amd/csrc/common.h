@@ -36,6 +36,13 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's bytes land at
+// lds_window + 16 * i, where lds_window must be the same for the whole wave. Completion is tracked
+// by vmcnt like any global load.
+__device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_window) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_window, 16, 0, 0);
+}
+
 // Wave-wide (64 lanes) sum.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

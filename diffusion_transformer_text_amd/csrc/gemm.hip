@@ -65,37 +65,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   tile_coords(nM, nN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // ---- global -> register assignment: chunk (row = tid/8 + 32 j, c = tid % 8) ----
-  const int ld_row = tid >> 3, ld_c = tid & 7;
-  uint32_t a_off[T::A_CHUNKS];
-  uint32_t w_off[T::W_CHUNKS];
+  // ---- global -> LDS, without staging registers: global_load_lds_dwordx4 writes lane i's 16 bytes
+  // to (LDS base + 16 i), so one instruction fills a 1 KB window = 8 rows of 128 bytes. The XOR
+  // swizzle is realised by the choice of source: window lane i stores physical chunk i % 8 of row
+  // i / 8, which holds logical chunk (i % 8) ^ (row & 7).
+  constexpr int A_WIN = BM / 8, W_WIN = BN / 8;          // 1 KB windows per tile
+  constexpr int A_PER_WAVE = A_WIN / 4, W_PER_WAVE = W_WIN / 4;
+  const int win_row = lane >> 3, win_chunk = (lane & 7) ^ (win_row & 7);
+  uint32_t a_off[A_PER_WAVE], w_off[W_PER_WAVE];
 #pragma unroll
-  for (int j = 0; j < T::A_CHUNKS; ++j) {
-    const int r = min(m0 + ld_row + 32 * j, p.M - 1);
-    a_off[j] = (uint32_t)(r * p.lda + ld_c * 8);
+  for (int j = 0; j < A_PER_WAVE; ++j) {
+    const int r = min(m0 + (wave + 4 * j) * 8 + win_row, p.M - 1);
+    a_off[j] = (uint32_t)(r * p.lda + win_chunk * 8);
   }
 #pragma unroll
-  for (int j = 0; j < T::W_CHUNKS; ++j) {
-    const int r = n0 + ld_row + 32 * j;
-    w_off[j] = (uint32_t)(r * p.ldw + ld_c * 8);
+  for (int j = 0; j < W_PER_WAVE; ++j) {
+    const int r = n0 + (wave + 4 * j) * 8 + win_row;
+    w_off[j] = (uint32_t)(r * p.ldw + win_chunk * 8);
   }
-  const int st_off = ld_row * BK + ((ld_c ^ (ld_row & 7)) << 3);   // + j * 32 * BK
-
-  uint4 ra[T::A_CHUNKS], rw[T::W_CHUNKS];
-  auto load_tile = [&](int kt) {
+  auto issue_tile = [&](int kt, int stage) {
     const int k0 = kt * BK;
-#pragma unroll
-    for (int j = 0; j < T::A_CHUNKS; ++j) ra[j] = *reinterpret_cast<const uint4*>(p.A + a_off[j] + k0);
-#pragma unroll
-    for (int j = 0; j < T::W_CHUNKS; ++j) rw[j] = *reinterpret_cast<const uint4*>(p.W + w_off[j] + k0);
-  };
-  auto store_tile = [&](int stage) {
     uint16_t* sA = lds + stage * T::STAGE;
     uint16_t* sW = sA + BM * BK;
 #pragma unroll
-    for (int j = 0; j < T::A_CHUNKS; ++j) *reinterpret_cast<uint4*>(sA + st_off + j * 32 * BK) = ra[j];
+    for (int j = 0; j < A_PER_WAVE; ++j)
+      load_lds_16(p.A + a_off[j] + k0, sA + (wave + 4 * j) * 512);
 #pragma unroll
-    for (int j = 0; j < T::W_CHUNKS; ++j) *reinterpret_cast<uint4*>(sW + st_off + j * 32 * BK) = rw[j];
+    for (int j = 0; j < W_PER_WAVE; ++j)
+      load_lds_16(p.W + w_off[j] + k0, sW + (wave + 4 * j) * 512);
   };
 
   floatx16 acc[T::TM][T::TN];
@@ -107,32 +104,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int fr = lane & 31, fh = lane >> 5;
+  // fragment rows of this lane; their low 3 bits equal fr & 7, so the swizzle term is per lane
+  const int a_row0 = wm * T::WM + fr, w_row0 = wn * T::WN + fr;
   const int KT = p.K / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  bf16x8 fa[2][T::TM], fw[2][T::TN];
+  auto load_frags = [&](const uint16_t* sA, const uint16_t* sW, int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(sA + swz(a_row0 + i * 32, 2 * s + fh));
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+      fw[buf][j] = *reinterpret_cast<const bf16x8*>(sW + swz(w_row0 + j * 32, 2 * s + fh));
+  };
+
+  issue_tile(0, 0);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) load_tile(kt + 1);
+    __syncthreads();                 // tile kt has landed in LDS; stage cur ^ 1 is free again
+    if (kt + 1 < KT) issue_tile(kt + 1, cur ^ 1);
     const uint16_t* sA = lds + cur * T::STAGE;
     const uint16_t* sW = sA + BM * BK;
+    load_frags(sA, sW, 0, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 fa[T::TM], fw[T::TN];
-#pragma unroll
-      for (int i = 0; i < T::TM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * T::WM + i * 32 + fr, 2 * s + fh));
-#pragma unroll
-      for (int j = 0; j < T::TN; ++j)
-        fw[j] = *reinterpret_cast<const bf16x8*>(sW + swz(wn * T::WN + j * 32 + fr, 2 * s + fh));
+      if (s + 1 < BK / 16) load_frags(sA, sW, s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fa[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][j], fa[s & 1][i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) store_tile(cur ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: acc[i][j][4g + e] = C[token m, feature n + e] ----
