@@ -23,18 +23,25 @@ constexpr int D = kHeadDim;   // 128
 constexpr int BQ = 128;
 constexpr int BKV = 64;
 
-// K tile: [64 keys][128 d], 16-byte chunk c of row `key` at chunk c ^ (key & 7).
-__device__ __forceinline__ int k_off(int key, int chunk) { return key * D + ((chunk ^ (key & 7)) << 3); }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// V^T tile: [128 d][64 keys], 8-byte unit u (4 keys) of row d at unit u ^ f(d). f makes both the
-// transposed writes (16 rows d = 8c + e at once) and the fragment reads (16 consecutive rows) hit
-// distinct banks.
-__device__ __forceinline__ int vt_f(int d) { return (d & 15) ^ ((d >> 3) & 15); }
-__device__ __forceinline__ int vt_off(int d, int key) { return d * BKV + ((((key >> 2) ^ vt_f(d)) & 15) << 2) + (key & 3); }
+// LDS tiles, both [64 keys][128 d] bf16 (256-byte rows of 16 chunks of 16 bytes):
+//   K: chunk c of row `key` sits at chunk c ^ (key & 7)  -> 8 consecutive rows read by ds_read_b128 at
+//      the same logical chunk hit 8 distinct bank groups;
+//   V: chunk c of row `key` sits at chunk c ^ (2 (key & 3)) -> a transpose read (4 rows x 32 bytes per
+//      16-lane group) hits 8 distinct 16-byte slots.
+// Both tiles are filled by direct global -> LDS loads (1 KB per wave instruction = 4 rows); the
+// swizzle is realised by the choice of source chunk.
+
+// gfx950 transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+// (i % 4) of the 8-byte pieces addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12.
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+}
 
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BKV * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * BKV];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BKV * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, fh = lane >> 5;
@@ -54,45 +61,51 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   for (int ds = 0; ds < D / 16; ++ds)
     qf[ds] = *reinterpret_cast<const bf16x8*>(Qg + (long)q_ld * p.ld_qkv + 16 * ds + 8 * fh);
 
-  // K/V staging assignment. K: item = tid + 256 j -> key = item >> 4, chunk = item & 15.
-  // V: item = tid + 256 j -> key pair = item >> 4 (keys 2 pair, 2 pair + 1), d chunk = item & 15.
-  const int it_c = tid & 15, it_r = tid >> 4;
-  uint4 rk[4], rv[4];
-  auto load_kv = [&](int k0) {
+  // ---- direct-load assignment: wave w fills windows 4w..4w+3 of each tile (rows 16w .. 16w+15) ----
+  const int win_r = lane >> 4, win_pc = lane & 15;
+  const int k_lc = win_pc ^ (win_r + 0);            // + 4 (window & 1) handled per window below
+  const int v_lc = win_pc ^ (2 * win_r);
+  // per-lane source offsets of this wave's windows, relative to the tile's first key row
+  int k_src[4], v_src[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = min(k0 + it_r + 16 * j, S - 1);
-      rk[j] = *reinterpret_cast<const uint4*>(Kg + (long)key * p.ld_qkv + it_c * 8);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int w = wave * 4 + j;                    // window: rows 4w .. 4w+3
+    const int row = 4 * w + win_r;
+    k_src[j] = (int)(row * p.ld_qkv) + 8 * (k_lc ^ (4 * (w & 1)));
+    v_src[j] = (int)(row * p.ld_qkv) + 8 * v_lc;
+  }
+  auto issue_tile = [&](int k0, int stage) {
+    if (k0 + BKV <= S) {
+      const uint16_t* kt = Kg + (long)k0 * p.ld_qkv;
+      const uint16_t* vt = Vg + (long)k0 * p.ld_qkv;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pair = it_r + 16 * j;
+      for (int j = 0; j < 4; ++j) {
+        load_lds_16(kt + k_src[j], &sK[stage][(wave * 4 + j) * 512]);
+        load_lds_16(vt + v_src[j], &sV[stage][(wave * 4 + j) * 512]);
+      }
+    } else {
+      // ragged last tile: rows past the sequence re-read its last row (their scores are masked)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int key = min(k0 + 2 * pair + kk, S - 1);
-        rv[2 * j + kk] = *reinterpret_cast<const uint4*>(Vg + (long)key * p.ld_qkv + it_c * 8);
+      for (int j = 0; j < 4; ++j) {
+        const int w = wave * 4 + j;
+        const long key = min(k0 + 4 * w + win_r, S - 1);
+        load_lds_16(Kg + key * p.ld_qkv + 8 * (k_lc ^ (4 * (w & 1))), &sK[stage][w * 512]);
+        load_lds_16(Vg + key * p.ld_qkv + 8 * v_lc, &sV[stage][w * 512]);
       }
     }
   };
-  auto store_kv = [&](int stage) {
+
+  // ---- per-lane LDS read offsets (elements), loop-invariant ----
+  int k_ofs[D / 16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&sK[stage][k_off(it_r + 16 * j, it_c)]) = rk[j];
+  for (int ds = 0; ds < D / 16; ++ds) k_ofs[ds] = fr * D + (((2 * ds + fh) ^ (fr & 7)) << 3);
+  const int g = lane >> 4, j16 = lane & 15;
+  int v_ofs[D / 32];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pair = it_r + 16 * j;
-      const uint32_t* a = reinterpret_cast<const uint32_t*>(&rv[2 * j]);
-      const uint32_t* c = reinterpret_cast<const uint32_t*>(&rv[2 * j + 1]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // d = 8 it_c + 2w and 2w + 1: pack (key 2pair, key 2pair+1) per d
-        const uint32_t lo = (a[w] & 0xffffu) | (c[w] << 16);
-        const uint32_t hi = (a[w] >> 16) | (c[w] & 0xffff0000u);
-        const int d0 = 8 * it_c + 2 * w;
-        *reinterpret_cast<uint32_t*>(&sV[stage][vt_off(d0, 2 * pair)]) = lo;
-        *reinterpret_cast<uint32_t*>(&sV[stage][vt_off(d0 + 1, 2 * pair)]) = hi;
-      }
-    }
-  };
+  for (int db = 0; db < D / 32; ++db) {
+    const int lc = 4 * db + 2 * (g & 1) + ((j16 & 3) >> 1);
+    v_ofs[db] = ((j16 >> 2) + 4 * (g >> 1)) * D + ((lc ^ (2 * (j16 >> 2))) << 3) + 4 * (j16 & 1);
+  }
 
   floatx16 o[D / 32];
 #pragma unroll
@@ -103,13 +116,14 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   const float c = p.scale_log2;
 
   const int ntiles = (S + BKV - 1) / BKV;
-  load_kv(0);
-  store_kv(0);
-  __syncthreads();
+  issue_tile(0, 0);
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
     const int k0 = t * BKV;
-    if (t + 1 < ntiles) load_kv(k0 + BKV);
+    __syncthreads();                  // tile t has landed; the other stage is free again
+    if (t + 1 < ntiles) issue_tile(k0 + BKV, cur ^ 1);
+    const uint16_t* tK = sK[cur];
+    const uint16_t* tV = sV[cur];
 
     // ---- S^T = K Q^T for 2 blocks of 32 keys ----
     floatx16 s[2];
@@ -119,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[cur][k_off(32 * kb + fr, 2 * ds + fh)]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(tK + kb * 32 * D + k_ofs[ds]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kb], 0, 0, 0);
       }
     }
@@ -134,15 +148,27 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
         }
     }
     // ---- online softmax (one query per lane, shared with lane ^ 32) ----
-    float mx = -INFINITY;
+    // The running max is only moved when a score exceeds it by more than 2^8 in the exp2 domain:
+    // with a stale max the probabilities stay below 256 (exact in fp32, same relative precision in
+    // bf16), the final normalisation divides by the sum taken against the same max, so the result
+    // is unchanged while the O rescale (64 multiplies per lane) runs only a few times per row.
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+      for (int e = (kb == 0 ? 2 : 0); e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f((m_run - m_new) * c);
-    const float mc = m_new * c;
+    if (__any((mx - m_run) * c > 8.0f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
     float lsum = 0.f;
     bf16x8 pf[2][2];
 #pragma unroll
@@ -152,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          pv[j] = exp2f(s[kb][8 * hs + j] * c - mc);
+          pv[j] = __builtin_amdgcn_exp2f(s[kb][8 * hs + j] * c - mc);
           lsum += pv[j];
         }
         uint32_t w[4];
@@ -161,32 +187,24 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
         pf[kb][hs] = *reinterpret_cast<bf16x8*>(w);
       }
     }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+    l_run += lsum;
 
-    // ---- O^T += V^T P^T ----
+    // ---- O^T += V^T P^T: the V^T fragment (d = 32 db + fr, keys 32 kb + 16 hs + 4 fh + {0..3, 8..11})
+    //      comes from two transpose reads of the row-major V tile ----
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = 32 * db + fr;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          const int key_a = 32 * kb + 16 * hs + 4 * fh;
-          const uint2 va = *reinterpret_cast<const uint2*>(&sV[cur][vt_off(d, key_a)]);
-          const uint2 vb = *reinterpret_cast<const uint2*>(&sV[cur][vt_off(d, key_a + 8)]);
-          uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
-          const bf16x8 vf = *reinterpret_cast<bf16x8*>(w);
+          const uint16_t* vp = tV + v_ofs[db] + (32 * kb + 16 * hs) * D;
+          const v4i16 lo = lds_read_tr16(vp);
+          const v4i16 hi = lds_read_tr16(vp + 8 * D);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][hs], o[db], 0, 0, 0);
         }
       }
     }
-    if (t + 1 < ntiles) store_kv(cur ^ 1);
-    __syncthreads();
   }
 
   // ---- normalise and store: lane holds query my_q, d = 32 db + 8 g + 4 fh + [0, 4) ----
@@ -197,11 +215,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * fh;
+      for (int gg = 0; gg < 4; ++gg) {
+        const int d = 32 * db + 8 * gg + 4 * fh;
         uint2 w;
-        w.x = pack2_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        w.y = pack2_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        w.x = pack2_bf16(o[db][4 * gg] * inv, o[db][4 * gg + 1] * inv);
+        w.y = pack2_bf16(o[db][4 * gg + 2] * inv, o[db][4 * gg + 3] * inv);
         *reinterpret_cast<uint2*>(orow + d) = w;
       }
   }

@@ -20,19 +20,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 with gfx950's v_cvt_pk_bf16_f32 (round to nearest even under the default mode).
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const floatx2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pack2_bf16(f, 0.f) & 0xffffu); }
 
 // Round an fp32 value to the nearest bf16 and return it as fp32.
-__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
-
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(pack2_bf16(f, 0.f) << 16); }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
