@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=3, help="steps of the per-kernel event pass")
     ap.add_argument("--text-len", type=int, default=256)
     ap.add_argument("--latent", type=int, default=128, help="latent side (1024 px / 8)")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="MiB of a plain device-to-device copy run once before the steps (scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -139,6 +142,16 @@ def main():
     P = 128
     lat_elems = 32 * lat_side * lat_side
     mod_rows = L * 6 * D + 2 * D
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calibrate_copy} MiB done")
+        del src, dst
 
     t0 = time.time()
     log(f"[bench] drawing random bf16 weights (42 blocks, hidden 3072, FFN 8192) on the GPU")

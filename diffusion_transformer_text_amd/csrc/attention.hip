@@ -26,8 +26,9 @@ constexpr int BKV = 64;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // LDS tiles, both [64 keys][128 d] bf16 (256-byte rows of 16 chunks of 16 bytes):
-//   K: chunk c of row `key` sits at chunk c ^ (key & 7)  -> 8 consecutive rows read by ds_read_b128 at
-//      the same logical chunk hit 8 distinct bank groups;
+//   K: chunk c of row `key` sits at chunk c ^ (key & 15) -> the 16 consecutive rows of one 16-lane
+//      phase of a ds_read_b128 at the same logical chunk hit 16 distinct bank groups (a 256-byte row
+//      spans all 64 banks, so only the chunk index decides the bank);
 //   V: chunk c of row `key` sits at chunk c ^ (2 (key & 3)) -> a transpose read (4 rows x 32 bytes per
 //      16-lane group) hits 8 distinct 16-byte slots.
 // Both tiles are filled by direct global -> LDS loads (1 KB per wave instruction = 4 rows); the
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
 
   // ---- direct-load assignment: wave w fills windows 4w..4w+3 of each tile (rows 16w .. 16w+15) ----
   const int win_r = lane >> 4, win_pc = lane & 15;
-  const int k_lc = win_pc ^ (win_r + 0);            // + 4 (window & 1) handled per window below
+  const int k_lc = win_pc ^ win_r;                  // ^ 4 (window & 3) per window below
   const int v_lc = win_pc ^ (2 * win_r);
   // per-lane source offsets of this wave's windows, relative to the tile's first key row
   int k_src[4], v_src[4];
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   for (int j = 0; j < 4; ++j) {
     const int w = wave * 4 + j;                    // window: rows 4w .. 4w+3
     const int row = 4 * w + win_r;
-    k_src[j] = (int)(row * p.ld_qkv) + 8 * (k_lc ^ (4 * (w & 1)));
+    k_src[j] = (int)(row * p.ld_qkv) + 8 * (k_lc ^ (4 * (w & 3)));
     v_src[j] = (int)(row * p.ld_qkv) + 8 * v_lc;
   }
   auto issue_tile = [&](int k0, int stage) {
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
       for (int j = 0; j < 4; ++j) {
         const int w = wave * 4 + j;
         const long key = min(k0 + 4 * w + win_r, S - 1);
-        load_lds_16(Kg + key * p.ld_qkv + 8 * (k_lc ^ (4 * (w & 1))), &sK[stage][w * 512]);
+        load_lds_16(Kg + key * p.ld_qkv + 8 * (k_lc ^ (4 * (w & 3))), &sK[stage][w * 512]);
         load_lds_16(Vg + key * p.ld_qkv + 8 * v_lc, &sV[stage][w * 512]);
       }
     }
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   // ---- per-lane LDS read offsets (elements), loop-invariant ----
   int k_ofs[D / 16];
 #pragma unroll
-  for (int ds = 0; ds < D / 16; ++ds) k_ofs[ds] = fr * D + (((2 * ds + fh) ^ (fr & 7)) << 3);
+  for (int ds = 0; ds < D / 16; ++ds) k_ofs[ds] = fr * D + (((2 * ds + fh) ^ (fr & 15)) << 3);
   const int g = lane >> 4, j16 = lane & 15;
   int v_ofs[D / 32];
 #pragma unroll

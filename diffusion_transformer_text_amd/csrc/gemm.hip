@@ -6,7 +6,7 @@
 // separate kernels ("Lossless RoPE fusion", "Lossless MLP and residual fusion"): the rotary turn of
 // q/k, the gated residual add and the SiLU-multiply of the SwiGLU FFN.
 //
-// Tiling: a workgroup of 4 waves (2 x 2) computes a BM (tokens) x BN (features) tile, BK = 64,
+// Tiling: a workgroup of WAVES_M x WAVES_N waves computes a BM (tokens) x BN (features) tile, BK = 64,
 // with both operands staged through a double-buffered, XOR-swizzled LDS tile. Each wave issues
 // v_mfma_f32_32x32x16_bf16 with the WEIGHT fragment as the MFMA A operand and the activation
 // fragment as the B operand, so the accumulator of lane l holds token (l % 32) and, per group of
@@ -19,22 +19,27 @@ namespace moss {
 namespace {
 
 constexpr int BK = 64;
-constexpr int kThreads = 256;
 constexpr int kGroupM = 8;   // tile rows per L2 group
 
-template <int BM, int BN>
+template <int BM, int BN, int WAVES_M, int WAVES_N>
 struct Tile {
-  static constexpr int WM = BM / 2, WN = BN / 2;        // wave tile
+  static constexpr int NW = WAVES_M * WAVES_N;          // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
   static constexpr int TM = WM / 32, TN = WN / 32;      // 32x32 MFMA blocks per wave
-  static constexpr int A_CHUNKS = BM * BK / 8 / kThreads;
-  static constexpr int W_CHUNKS = BN * BK / 8 / kThreads;
   static constexpr int STAGE = (BM + BN) * BK;          // elements per LDS stage
+  static_assert(WN % 64 == 0, "a wave's features must hold whole 64-row gate/up groups");
+  static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "1 KB load windows must split evenly");
 };
 
-// Element offset of 16-byte chunk c of row r in a [rows][BK] bf16 LDS tile. The chunk index is
-// XORed with the row's low 3 bits so that the 8 consecutive rows read by 8 consecutive lanes of a
-// fragment load fall into 8 distinct bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+// Element offset of 16-byte chunk c of row r in a [rows][BK] bf16 LDS tile. A fragment load reads
+// one chunk from each of 32 consecutive rows; gfx950 serves ds_read_b128 in phases of 16 lanes over
+// 64 four-byte banks (256 bytes), i.e. two 128-byte rows per bank line. XOR-ing the chunk index
+// with (r & 7) ^ ((r >> 3) & 1) puts the 16 rows of a phase on 16 distinct (row parity, chunk)
+// slots; a plain (r & 7) leaves rows r and r + 8 on the same banks (measured: every read 2-way
+// conflicted, SQ_LDS_BANK_CONFLICT = half of SQ_LDS_IDX_ACTIVE).
+__device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ swz_key(r)) << 3); }
 
 // Maps the linear workgroup id to a (tile_m, tile_n) pair. Workgroups are dispatched round-robin
 // over the 8 XCDs; the remap gives each XCD a contiguous run of tiles, and within the run tiles go
@@ -53,13 +58,13 @@ __device__ __forceinline__ void tile_coords(int nM, int nN, int& tm, int& tn) {
   tn = in_group / gsize;
 }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-  using T = Tile<BM, BN>;
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs p) {
+  using T = Tile<BM, BN, WAVES_M, WAVES_N>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int nN = p.N / BN, nM = (p.M + BM - 1) / BM;
   int tm, tn;
   tile_coords(nM, nN, tm, tn);
@@ -68,31 +73,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   // ---- global -> LDS, without staging registers: global_load_lds_dwordx4 writes lane i's 16 bytes
   // to (LDS base + 16 i), so one instruction fills a 1 KB window = 8 rows of 128 bytes. The XOR
   // swizzle is realised by the choice of source: window lane i stores physical chunk i % 8 of row
-  // i / 8, which holds logical chunk (i % 8) ^ (row & 7).
+  // i / 8, which holds logical chunk (i % 8) ^ swz_key(row).
   constexpr int A_WIN = BM / 8, W_WIN = BN / 8;          // 1 KB windows per tile
-  constexpr int A_PER_WAVE = A_WIN / 4, W_PER_WAVE = W_WIN / 4;
-  const int win_row = lane >> 3, win_chunk = (lane & 7) ^ (win_row & 7);
+  constexpr int A_PER_WAVE = A_WIN / T::NW, W_PER_WAVE = W_WIN / T::NW;
+  // window rows are 8 w + lane / 8 with w = wave + NW j (NW even), so the row's swizzle key is
+  // (lane / 8) ^ (wave & 1) for every window of this wave
+  const int win_row = lane >> 3, win_chunk = (lane & 7) ^ win_row ^ (wave & 1);
   uint32_t a_off[A_PER_WAVE], w_off[W_PER_WAVE];
 #pragma unroll
   for (int j = 0; j < A_PER_WAVE; ++j) {
-    const int r = min(m0 + (wave + 4 * j) * 8 + win_row, p.M - 1);
+    const int r = min(m0 + (wave + T::NW * j) * 8 + win_row, p.M - 1);
     a_off[j] = (uint32_t)(r * p.lda + win_chunk * 8);
   }
 #pragma unroll
   for (int j = 0; j < W_PER_WAVE; ++j) {
-    const int r = n0 + (wave + 4 * j) * 8 + win_row;
+    const int r = n0 + (wave + T::NW * j) * 8 + win_row;
     w_off[j] = (uint32_t)(r * p.ldw + win_chunk * 8);
   }
-  auto issue_tile = [&](int kt, int stage) {
+  // loads of one tile are spread over the four k16 slices of the previous tile's MFMA work, so the
+  // wave never waits behind its own queue of memory instructions before starting to compute
+  constexpr int LOADS = A_PER_WAVE + W_PER_WAVE;
+  constexpr int LOADS_PER_SLICE = (LOADS + BK / 16 - 1) / (BK / 16);
+  auto issue_part = [&](int kt, int stage, int part) {
     const int k0 = kt * BK;
     uint16_t* sA = lds + stage * T::STAGE;
     uint16_t* sW = sA + BM * BK;
 #pragma unroll
-    for (int j = 0; j < A_PER_WAVE; ++j)
-      load_lds_16(p.A + a_off[j] + k0, sA + (wave + 4 * j) * 512);
-#pragma unroll
-    for (int j = 0; j < W_PER_WAVE; ++j)
-      load_lds_16(p.W + w_off[j] + k0, sW + (wave + 4 * j) * 512);
+    for (int q = 0; q < LOADS_PER_SLICE; ++q) {
+      const int j = part * LOADS_PER_SLICE + q;
+      if (j < A_PER_WAVE) {
+        load_lds_16(p.A + a_off[j] + k0, sA + (wave + T::NW * j) * 512);
+      } else if (j < LOADS) {
+        const int jw = j - A_PER_WAVE;
+        load_lds_16(p.W + w_off[jw] + k0, sW + (wave + T::NW * jw) * 512);
+      }
+    }
   };
 
   floatx16 acc[T::TM][T::TN];
@@ -104,7 +119,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int fr = lane & 31, fh = lane >> 5;
-  // fragment rows of this lane; their low 3 bits equal fr & 7, so the swizzle term is per lane
+  // fragment rows of this lane: wave and block offsets are multiples of 32, so swz_key(row) =
+  // swz_key(fr) and the swizzle term is a per-lane constant
   const int a_row0 = wm * T::WM + fr, w_row0 = wn * T::WN + fr;
   const int KT = p.K / BK;
   bf16x8 fa[2][T::TM], fw[2][T::TN];
@@ -117,22 +133,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
       fw[buf][j] = *reinterpret_cast<const bf16x8*>(sW + swz(w_row0 + j * 32, 2 * s + fh));
   };
 
-  issue_tile(0, 0);
+#pragma unroll
+  for (int part = 0; part < BK / 16; ++part) issue_part(0, 0, part);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     __syncthreads();                 // tile kt has landed in LDS; stage cur ^ 1 is free again
-    if (kt + 1 < KT) issue_tile(kt + 1, cur ^ 1);
+    const bool more = kt + 1 < KT;
     const uint16_t* sA = lds + cur * T::STAGE;
     const uint16_t* sW = sA + BM * BK;
     load_frags(sA, sW, 0, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
+      // the next slice's fragment reads are issued before this slice's MFMAs and kept there: the
+      // LDS latency then hides behind TM * TN matrix instructions instead of stalling the wave
       if (s + 1 < BK / 16) load_frags(sA, sW, s + 1, (s + 1) & 1);
+      if (more) issue_part(kt + 1, cur ^ 1, s);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][j], fa[s & 1][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -225,26 +247,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t launch_tile(const GemmArgs& a, int epi, hipStream_t stream) {
   const int nM = (a.M + BM - 1) / BM, nN = a.N / BN;
-  dim3 grid(nM * nN), block(kThreads);
+  dim3 grid(nM * nN), block(64 * WAVES_M * WAVES_N);
+#define MOSS_GEMM_LAUNCH(E) \
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, E>), grid, block, 0, stream, a)
   switch (epi) {
-    case EPI_BF16: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_BF16>), grid, block, 0, stream, a); break;
-    case EPI_QKV_ROPE: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_QKV_ROPE>), grid, block, 0, stream, a); break;
-    case EPI_GATED_RES: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_GATED_RES>), grid, block, 0, stream, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_SWIGLU>), grid, block, 0, stream, a); break;
-    case EPI_F32: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_F32>), grid, block, 0, stream, a); break;
+    case EPI_BF16: MOSS_GEMM_LAUNCH(EPI_BF16); break;
+    case EPI_QKV_ROPE: MOSS_GEMM_LAUNCH(EPI_QKV_ROPE); break;
+    case EPI_GATED_RES: MOSS_GEMM_LAUNCH(EPI_GATED_RES); break;
+    case EPI_SWIGLU: MOSS_GEMM_LAUNCH(EPI_SWIGLU); break;
+    case EPI_F32: MOSS_GEMM_LAUNCH(EPI_F32); break;
     case EPI_F32_UNPATCH:
       // the output projection has N = C*4 = 128: only the 128-wide tile is ever used for it
       if constexpr (BN == 128) {
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI_F32_UNPATCH>), grid, block, 0, stream, a);
+        MOSS_GEMM_LAUNCH(EPI_F32_UNPATCH);
         break;
       } else {
         return hipErrorInvalidValue;
       }
     default: return hipErrorInvalidValue;
   }
+#undef MOSS_GEMM_LAUNCH
   return hipGetLastError();
 }
 
@@ -266,8 +291,8 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream) {
   // SwiGLU pairs feature blocks inside a wave: the wave's feature width must hold whole 64-row groups.
   const bool big_n = (a.N % 256 == 0);
   const long tiles256 = (long)((a.M + 255) / 256) * (a.N / 256);
-  if (big_n && epi != EPI_F32_UNPATCH && a.M > 1024 && tiles256 >= 256) return launch_tile<256, 256>(a, epi, stream);
-  if (a.N % 128 == 0) return launch_tile<128, 128>(a, epi, stream);
+  if (big_n && epi != EPI_F32_UNPATCH && a.M > 1024 && tiles256 >= 256) return launch_tile<256, 256, 2, 4>(a, epi, stream);
+  if (a.N % 128 == 0) return launch_tile<128, 128, 2, 2>(a, epi, stream);
   return hipErrorInvalidValue;
 }
 
