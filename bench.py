@@ -66,6 +66,24 @@ def class_work(cls, L, D, F, S, N, T, B, skipped, lat_elems, mod_rows, P):
     return 0, 0
 
 
+def measured_traffic(kernel_class):
+    """HBM bytes per launch of `kernel_class` from the committed FETCH_SIZE / WRITE_SIZE passes, or None
+    when there is no such record or the kernel sources changed since it was taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "gemm_gate_up_traffic.json")
+    try:
+        rec = json.load(open(path))
+        if rec.get("kernel") != kernel_class:
+            return None
+        src = b"".join(open(os.path.join(here, f), "rb").read() for f in rec["sources"])
+        if hashlib.sha256(src).hexdigest() != rec["sources_sha256"]:
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def _host_f64(t):
     import numpy as np
     import torch
@@ -217,11 +235,11 @@ def main():
     launches = kernels[dom]["launches_per_step"]
     if dom.startswith("gemm") or dom == "attention":
         roof = {"bound": "mfma", "achieved": kernels[dom]["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": kernels[dom]["frac_mfma_peak"], "traffic": None, "kernel": dom,
+                "frac": kernels[dom]["frac_mfma_peak"], "traffic": measured_traffic(dom), "kernel": dom,
                 "flops_per_launch": fl / launches, "avg_launch_ms": kernels[dom]["ms_per_step"] / launches}
     else:
         roof = {"bound": "hbm", "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": kernels[dom]["frac_hbm_peak"], "traffic": None, "kernel": dom,
+                "frac": kernels[dom]["frac_hbm_peak"], "traffic": measured_traffic(dom), "kernel": dom,
                 "bytes_per_launch": by / launches, "avg_launch_ms": kernels[dom]["ms_per_step"] / launches}
     log(f"[bench] per-kernel: {json.dumps(kernels)}")
 
