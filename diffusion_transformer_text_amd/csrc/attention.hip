@@ -29,8 +29,9 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 //   K: chunk c of row `key` sits at chunk c ^ (key & 15) -> the 16 consecutive rows of one 16-lane
 //      phase of a ds_read_b128 at the same logical chunk hit 16 distinct bank groups (a 256-byte row
 //      spans all 64 banks, so only the chunk index decides the bank);
-//   V: chunk c of row `key` sits at chunk c ^ (2 (key & 3)) -> a transpose read (4 rows x 32 bytes per
-//      16-lane group) hits 8 distinct 16-byte slots.
+//   V: chunk c of row `key` sits at chunk c ^ (4 (key & 3)) -> a transpose read (4 rows x 32 bytes per
+//      16-lane group, two groups per 256-byte bank phase) hits distinct 16-byte slots; the earlier
+//      c ^ 2 (key & 3) measured 33 % of LDS cycles as bank conflicts (32-lane phases for the b64 read).
 // Both tiles are filled by direct global -> LDS loads (1 KB per wave instruction = 4 rows); the
 // swizzle is realised by the choice of source chunk.
 
@@ -46,7 +47,15 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, fh = lane >> 5;
-  const int q0 = blockIdx.x * BQ, h = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Remap the linear
+  // id so that XCD x runs a contiguous range of (sample, head) pairs with all their query tiles:
+  // the ~2 heads resident on an XCD at a time share their K/V in that XCD's L2.
+  const int nq = (p.S + BQ - 1) / BQ;
+  const int total = nq * p.H * p.B;
+  int lin = blockIdx.x;
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  const int bh = lin / nq;
+  const int q0 = (lin - bh * nq) * BQ, h = bh % p.H, b = bh / p.H;
   const int S = p.S;
   const int DM = p.H * D;
   const uint16_t* base = p.qkv + (long)b * S * p.ld_qkv;
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   // ---- direct-load assignment: wave w fills windows 4w..4w+3 of each tile (rows 16w .. 16w+15) ----
   const int win_r = lane >> 4, win_pc = lane & 15;
   const int k_lc = win_pc ^ win_r;                  // ^ 4 (window & 3) per window below
-  const int v_lc = win_pc ^ (2 * win_r);
+  const int v_lc = win_pc ^ (4 * win_r);
   // per-lane source offsets of this wave's windows, relative to the tile's first key row
   int k_src[4], v_src[4];
 #pragma unroll
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int lc = 4 * db + 2 * (g & 1) + ((j16 & 3) >> 1);
-    v_ofs[db] = ((j16 >> 2) + 4 * (g >> 1)) * D + ((lc ^ (2 * (j16 >> 2))) << 3) + 4 * (j16 & 1);
+    v_ofs[db] = ((j16 >> 2) + 4 * (g >> 1)) * D + ((lc ^ (4 * (j16 >> 2))) << 3) + 4 * (j16 & 1);
   }
 
   floatx16 o[D / 32];
@@ -252,8 +261,9 @@ __global__ void rope_inplace_kernel(uint16_t* qkv, int B, int S, int T, int grid
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   if (a.S <= 0 || a.B <= 0) return hipSuccess;
   if (a.ld_qkv % 8 != 0 || a.ld_out % 4 != 0) return hipErrorInvalidValue;
-  dim3 grid((a.S + BQ - 1) / BQ, a.H, a.B);
-  hipLaunchKernelGGL(attention_kernel, grid, dim3(256), 0, stream, a);
+  const long wgs = (long)((a.S + BQ - 1) / BQ) * a.H * a.B;
+  if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
