@@ -935,6 +935,10 @@ int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t hea
   }
   hipStream_t st = (hipStream_t)stream;
   const long D = (long)heads * kHeadDim;
+  if (2L * seq * 3 * D > 0x7fffffffL) {
+    g_thread_error = "moss_attention: one sample's qkv rows must stay below 2 GiB";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
   hipError_t e = hipSuccess;
   if (rope) {
     float* tab = nullptr;

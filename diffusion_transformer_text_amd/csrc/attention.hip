@@ -24,6 +24,7 @@ constexpr int BQ = 128;
 constexpr int BKV = 64;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // LDS tiles, both [64 keys][128 d] bf16 (256-byte rows of 16 chunks of 16 bytes):
 //   K: chunk c of row `key` sits at chunk c ^ (key & 15) -> the 16 consecutive rows of one 16-lane
@@ -42,8 +43,13 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
 }
 
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BKV * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BKV * D];
+  // Two LDS stages each for K and V, as four separate arrays: every access below names a fixed array
+  // (the tile loop is unrolled by two), so the compiler can tell a read of one stage from the
+  // direct loads still landing in another and waits for those loads only at the next barrier.
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[BKV * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[BKV * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[BKV * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[BKV * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, fh = lane >> 5;
@@ -60,8 +66,6 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   const int DM = p.H * D;
   const uint16_t* base = p.qkv + (long)b * S * p.ld_qkv;
   const uint16_t* Qg = base + h * D;
-  const uint16_t* Kg = base + DM + h * D;
-  const uint16_t* Vg = base + 2 * DM + h * D;
 
   // Q fragments (MFMA B operand of S^T = K Q^T): query q, d = 16 ds + 8 fh + [0, 8)
   const int my_q = q0 + wave * 32 + fr;
@@ -72,37 +76,34 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
     qf[ds] = *reinterpret_cast<const bf16x8*>(Qg + (long)q_ld * p.ld_qkv + 16 * ds + 8 * fh);
 
   // ---- direct-load assignment: wave w fills windows 4w..4w+3 of each tile (rows 16w .. 16w+15) ----
+  // A tile is read through a buffer resource over the sample's rows from the tile's first key on, so
+  // rows past the end of the sequence (ragged last tile) come back as zeros from the hardware range
+  // check: their scores are masked and their probabilities are zero.
   const int win_r = lane >> 4, win_pc = lane & 15;
   const int k_lc = win_pc ^ win_r;                  // ^ 4 (window & 3) per window below
   const int v_lc = win_pc ^ (4 * win_r);
-  // per-lane source offsets of this wave's windows, relative to the tile's first key row
-  int k_src[4], v_src[4];
+  // per-lane byte offsets of this wave's windows, relative to the tile's first key row
+  int k_vo[4], v_vo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int w = wave * 4 + j;                    // window: rows 4w .. 4w+3
     const int row = 4 * w + win_r;
-    k_src[j] = (int)(row * p.ld_qkv) + 8 * (k_lc ^ (4 * (w & 3)));
-    v_src[j] = (int)(row * p.ld_qkv) + 8 * v_lc;
+    k_vo[j] = 2 * (row * p.ld_qkv + DM + h * D + 8 * (k_lc ^ (4 * (w & 3))));
+    v_vo[j] = 2 * (row * p.ld_qkv + 2 * DM + h * D + 8 * v_lc);
   }
-  auto issue_tile = [&](int k0, int stage) {
-    if (k0 + BKV <= S) {
-      const uint16_t* kt = Kg + (long)k0 * p.ld_qkv;
-      const uint16_t* vt = Vg + (long)k0 * p.ld_qkv;
+  auto tile_rsrc = [&](int t) {
+    const int k0 = t * BKV;
+    return make_rsrc(base + (long)k0 * p.ld_qkv, 2 * (S - k0) * p.ld_qkv);
+  };
+  auto issue_k = [&](int t, uint16_t* dst) {
+    const auto r = tile_rsrc(t);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        load_lds_16(kt + k_src[j], &sK[stage][(wave * 4 + j) * 512]);
-        load_lds_16(vt + v_src[j], &sV[stage][(wave * 4 + j) * 512]);
-      }
-    } else {
-      // ragged last tile: rows past the sequence re-read its last row (their scores are masked)
+    for (int j = 0; j < 4; ++j) buf_load_lds_16(r, dst + (wave * 4 + j) * 512, k_vo[j]);
+  };
+  auto issue_v = [&](int t, uint16_t* dst) {
+    const auto r = tile_rsrc(t);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int w = wave * 4 + j;
-        const long key = min(k0 + 4 * w + win_r, S - 1);
-        load_lds_16(Kg + key * p.ld_qkv + 8 * (k_lc ^ (4 * (w & 3))), &sK[stage][w * 512]);
-        load_lds_16(Vg + key * p.ld_qkv + 8 * v_lc, &sV[stage][w * 512]);
-      }
-    }
+    for (int j = 0; j < 4; ++j) buf_load_lds_16(r, dst + (wave * 4 + j) * 512, v_vo[j]);
   };
 
   // ---- per-lane LDS read offsets (elements), loop-invariant ----
@@ -125,49 +126,33 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.scale_log2;
 
-  const int ntiles = (S + BKV - 1) / BKV;
-  issue_tile(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const int k0 = t * BKV;
-    __syncthreads();                  // tile t has landed; the other stage is free again
-    if (t + 1 < ntiles) issue_tile(k0 + BKV, cur ^ 1);
-    const uint16_t* tK = sK[cur];
-    const uint16_t* tV = sV[cur];
-
-    // ---- S^T = K Q^T for 2 blocks of 32 keys ----
-    floatx16 s[2];
+  // S^T = K Q^T for the 64 keys of one LDS tile (2 blocks of 32 keys)
+  auto scores = [&](const uint16_t* tK, floatx16 (&sc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(tK + kb * 32 * D + k_ofs[ds]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], sc[kb], 0, 0, 0);
       }
     }
-    // mask keys past the end of the sequence (last tile only)
-    if (k0 + BKV > S) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * fh + (e & 3);
-          if (key >= S) s[kb][e] = -INFINITY;
-        }
-    }
-    // ---- online softmax (one query per lane, shared with lane ^ 32) ----
-    // The running max is only moved when a score exceeds it by more than 2^8 in the exp2 domain:
-    // with a stale max the probabilities stay below 256 (exact in fp32, same relative precision in
-    // bf16), the final normalisation divides by the sum taken against the same max, so the result
-    // is unchanged while the O rescale (64 multiplies per lane) runs only a few times per row.
-    float mx = fmaxf(s[0][0], s[0][1]);
+  };
+  // row max of one tile's scores: in-lane over 32 values, then with lane ^ 32 (same query)
+  auto rowmax = [&](const floatx16 (&sc)[2]) {
+    float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = (kb == 0 ? 2 : 0); e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      for (int e = (kb == 0 ? 2 : 0); e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+  };
+  // The running max only moves when a score exceeds it by more than 2^8 in the exp2 domain: with a
+  // stale max the probabilities stay below 256 (exact in fp32, same relative precision in bf16), the
+  // final normalisation divides by the sum taken against the same max, so the result is unchanged
+  // while the O rescale (64 multiplies per lane) runs only a few times per row.
+  auto maybe_rescale = [&](float mx) {
     if (__any((mx - m_run) * c > 8.0f)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
@@ -178,9 +163,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       m_run = m_new;
     }
+  };
+  // P = exp2(s c - m c) as bf16 MFMA operands, and the running row sum
+  auto probs = [&](const floatx16 (&sc)[2], bf16x8 (&pf)[2][2]) {
     const float mc = m_run * c;
     float lsum = 0.f;
-    bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -188,19 +175,20 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          pv[j] = __builtin_amdgcn_exp2f(s[kb][8 * hs + j] * c - mc);
+          pv[j] = __builtin_amdgcn_exp2f(sc[kb][8 * hs + j] * c - mc);
           lsum += pv[j];
         }
-        uint32_t w[4];
+        u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[j] = pack2_bf16(pv[2 * j], pv[2 * j + 1]);
-        pf[kb][hs] = *reinterpret_cast<bf16x8*>(w);
+        pf[kb][hs] = __builtin_bit_cast(bf16x8, w);
       }
     }
     l_run += lsum;
-
-    // ---- O^T += V^T P^T: the V^T fragment (d = 32 db + fr, keys 32 kb + 16 hs + 4 fh + {0..3, 8..11})
-    //      comes from two transpose reads of the row-major V tile ----
+  };
+  // O^T += V^T P^T: the V^T fragment (d = 32 db + fr, keys 32 kb + 16 hs + 4 fh + {0..3, 8..11})
+  // comes from two transpose reads of the row-major V tile
+  auto pv_update = [&](const uint16_t* tV, const bf16x8 (&pf)[2][2]) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -215,6 +203,121 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
         }
       }
     }
+  };
+
+  // ---- software pipeline: K runs one tile ahead of V. In iteration t the MFMAs of S(t+1) are
+  // interleaved with the softmax VALU work of tile t, and the MFMAs of P(t) V(t) with the row max of
+  // S(t+1). Stages: K(t) lives in sK[t & 1], V(t) in sV[t & 1]. Iteration t reads K(t+1) and V(t)
+  // and refills the two stages read one iteration earlier: K(t+2) -> sK[t & 1], V(t+1) -> sV[(t+1) & 1]. ----
+  const int ntiles = (S + BKV - 1) / BKV;
+  issue_k(0, sK0);
+  issue_v(0, sV0);
+  if (ntiles > 1) issue_k(1, sK1);
+  lds_copy_barrier();
+  floatx16 s_cur[2];
+  scores(sK0, s_cur);
+  float mx_cur = rowmax(s_cur);
+  // s_cur holds S(t) on entry; S(t+1) is written to s_next (the unrolled pair swaps the two)
+  auto iteration = [&](int t, uint16_t* kFree, const uint16_t* kNext, uint16_t* vFree, const uint16_t* vCur,
+                       floatx16 (&s_cur)[2], floatx16 (&s_next)[2]) {
+    lds_copy_barrier();              // K(t+1) and V(t) have landed; kFree and vFree are no longer read
+    if (t + 2 < ntiles) issue_k(t + 2, kFree);
+    issue_v(t + 1, vFree);
+    maybe_rescale(mx_cur);
+    // region A: S(t+1) on the matrix core while the VALU turns S(t) into probabilities. Step i issues
+    // one MFMA (accumulators alternate so consecutive MFMAs are independent), the LDS read of the K
+    // fragment four steps ahead, and the exp2/sum/pack of two scores; sched_barrier keeps that order.
+    bf16x8 pf[2][2];
+    {
+      const uint16_t* tK = kNext;
+      const float mc = m_run * c;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s_next[kb][e] = 0.f;
+      bf16x8 kf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kf[i] = *reinterpret_cast<const bf16x8*>(tK + (i & 1) * 32 * D + k_ofs[i >> 1]);
+      float lsum = 0.f;
+      u32x4 w[4];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s_next[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1], s_next[i & 1], 0, 0, 0);
+        if (i + 4 < 16)
+          kf[i & 3] = *reinterpret_cast<const bf16x8*>(tK + (i & 1) * 32 * D + k_ofs[(i + 4) >> 1]);
+        const float p0 = __builtin_amdgcn_exp2f(s_cur[i >> 3][2 * (i & 7)] * c - mc);
+        const float p1 = __builtin_amdgcn_exp2f(s_cur[i >> 3][2 * (i & 7) + 1] * c - mc);
+        lsum += p0 + p1;
+        w[i >> 2][i & 3] = pack2_bf16(p0, p1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run += lsum;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) pf[kb][hs] = __builtin_bit_cast(bf16x8, w[2 * kb + hs]);
+    }
+    // region B: P(t) V(t) on the matrix core while the VALU finds the row max of S(t+1). Step i
+    // (16 per tile: 4 d-blocks x 2 key blocks x 2 halves) is one MFMA into o[i & 3], the two
+    // transpose reads of the V fragment two steps ahead, and the max over two scores.
+    float mx_next;
+    {
+      const uint16_t* tV = vCur;
+      auto vfrag = [&](int i) {
+        const int db = i & 3, hs = (i >> 2) & 1, kb = i >> 3;
+        const uint16_t* vp = tV + v_ofs[db] + (32 * kb + 16 * hs) * D;
+        const v4i16 lo = lds_read_tr16(vp);
+        const v4i16 hi = lds_read_tr16(vp + 8 * D);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vf[3];
+      vf[0] = vfrag(0);
+      vf[1] = vfrag(1);
+      float mx = -INFINITY;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + 2 < 16) vf[(i + 2) % 3] = vfrag(i + 2);
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pf[i >> 3][(i >> 2) & 1], o[i & 3], 0, 0, 0);
+        mx = fmaxf(mx, fmaxf(s_next[i >> 3][(2 * i) & 15], s_next[i >> 3][(2 * i + 1) & 15]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mx_next = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    mx_cur = mx_next;
+  };
+  floatx16 s_alt[2];
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    iteration(t, sK0, sK1, sV1, sV0, s_cur, s_alt);
+    iteration(t + 1, sK1, sK0, sV0, sV1, s_alt, s_cur);
+  }
+  if (t + 1 < ntiles) {
+    iteration(t, sK0, sK1, sV1, sV0, s_cur, s_alt);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_alt[kb];
+  }
+  // ---- last tile: mask keys past the sequence, then the same softmax and P V ----
+  {
+    const int t = ntiles - 1;
+    const int k0 = t * BKV;
+    lds_copy_barrier();              // V(t) has landed
+    if (k0 + BKV > S) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * fh + (e & 3);
+          if (key >= S) s_cur[kb][e] = -INFINITY;
+        }
+      mx_cur = rowmax(s_cur);
+    }
+    maybe_rescale(mx_cur);
+    bf16x8 pf[2][2];
+    probs(s_cur, pf);
+    pv_update((t & 1) ? sV1 : sV0, pf);
   }
 
   // ---- normalise and store: lane holds query my_q, d = 32 db + 8 g + 4 fh + [0, 4) ----
@@ -263,6 +366,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   if (a.ld_qkv % 8 != 0 || a.ld_out % 4 != 0) return hipErrorInvalidValue;
   const long wgs = (long)((a.S + BQ - 1) / BQ) * a.H * a.B;
   if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
+  if (2L * a.S * a.ld_qkv > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit buffer offsets per sample
   hipLaunchKernelGGL(attention_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

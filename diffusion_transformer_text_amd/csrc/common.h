@@ -43,6 +43,26 @@ __device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_window) 
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_window, 16, 0, 0);
 }
 
+// Buffer resource over `bytes` bytes from `base` (raw: stride 0, 32-bit dwords). A buffer access whose
+// per-lane offset reaches `bytes` returns zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane i's bytes, read at byte
+// offset `voffset` of the resource, land at lds_window + 16 * i (lds_window uniform over the wave).
+__device__ __forceinline__ void buf_load_lds_16(__amdgpu_buffer_rsrc_t r, void* lds_window, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_window, 16, voffset, 0, 0, 0);
+}
+
+// Barrier that publishes direct-to-LDS copies: wait until this wave's vector-memory loads (the LDS
+// copies included) have completed (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima), then
+// synchronise the workgroup. After it every wave's copies issued before the barrier are visible.
+__device__ __forceinline__ void lds_copy_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+}
+
 // Wave-wide (64 lanes) sum.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

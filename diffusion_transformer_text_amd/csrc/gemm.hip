@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_kernel(Ge
   for (int part = 0; part < BK / 16; ++part) issue_part(0, 0, part);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    __syncthreads();                 // tile kt has landed in LDS; stage cur ^ 1 is free again
+    lds_copy_barrier();                 // tile kt has landed in LDS; stage cur ^ 1 is free again
     const bool more = kt + 1 < KT;
     const uint16_t* sA = lds + cur * T::STAGE;
     const uint16_t* sW = sA + BM * BK;
