@@ -21,9 +21,17 @@ Parity status of each function (pins in tests/test_oracle_pins.py):
   forward                     skip == zeroed gate rows (bitwise), per-sample independence
   cfg_combine, euler_step,    pinned: CFG identities, telescoping under constant v, point-mass field
   sample_step                 lands exactly on x*, cfg = 1 runs no negative pass
+  negative_pass_runs          pinned: hand table of the truncation boundary (X * steps, steps from 0)
+  guidance_combine            pinned: hand values of each term, v_s = v_c leaves the two-pass result,
+                              linearity in slg_scale
+  sample_step (three-pass,    pinned: the third row equals the conditional forward with the skipped
+  truncation)                 blocks' gate rows zeroed (bitwise); slg 0 / empty skip list / outside
+                              the window give the two-pass step bitwise; a truncated step equals the
+                              CFG-1 step bitwise
 """
 from .moss_oracle import *  # noqa: F401,F403
 from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, embed, euler_step,  # noqa
-                          final_layer, forward, from_bf16_bits, layernorm, ln_modulate, modulation,
+                          final_layer, forward, from_bf16_bits, guidance_combine, layernorm, ln_modulate,
+                          modulation, negative_pass_runs,
                           patchify, rope_angles, apply_rope, rope_rows, sample_step, sigmas, silu,
                           slg_active, time_features, unpatchify, weights_to_f64)

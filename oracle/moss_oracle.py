@@ -17,6 +17,8 @@ Pages (titles as published):
         "Skip layers".
   [QI]  "Qwen-Image 2.1" -- SGLang cookbook, sections "Lossless RoPE fusion", "Lossless MLP and
         residual fusion", "Lossless LayerNorm modulation" (fused-op idioms of a single-stream DiT).
+  [MI]  "MossInfer integration guide" -- the feature table (rows "Generation", "Lossy accelerators")
+        and its list of opt-in accelerators (CFG truncation).
 
 Where the pages leave a step open the plainest reading is taken; each such reading is named at the
 function that makes it. Pins: every function here is checked in tests/test_oracle_pins.py against
@@ -373,28 +375,60 @@ def euler_step(x: np.ndarray, v: np.ndarray, sigma: float, sigma_next: float) ->
     return x + (sigma_next - sigma) * v
 
 
+def negative_pass_runs(step: int, num_steps: int, cfg_scale: float, cfg_truncation: float = 1.0) -> bool:
+    """Whether the negative (unconditional) branch runs at this step. CFG 1 runs none ([IV]
+    "Generation settings"). CFG truncation X in [0, 1] (default 1 = off) drops the negative branch
+    from step X*steps on ([MI] feature table, "Lossy accelerators", and its list of opt-in
+    accelerators). Reading: with steps numbered from 0, the branch runs iff step < X*steps."""
+    return cfg_scale > 1.0 and step < cfg_truncation * num_steps
+
+
+def guidance_combine(v_cond: np.ndarray, v_uncond: Optional[np.ndarray], v_skip: Optional[np.ndarray],
+                     cfg_scale: float, slg_scale: float) -> np.ndarray:
+    """Guided velocity from up to three predictions. Without a negative branch (v_uncond None) the
+    guided part is v_c, else the ordinary linear combination v_u + cfg (v_c - v_u) (see cfg_combine).
+    Three-pass skip-layer guidance adds a skipped conditional prediction v_s ([SG] "3. Guidance and
+    precision"; [MI] feature table lists skip-layer guidance and its scale). The pages give no formula:
+    reading, the skip-layer guidance form v + slg (v_c - v_s), with v_s absent (None) meaning no term."""
+    if v_uncond is None:
+        v = np.asarray(v_cond, dtype=np.float64)
+    else:
+        v = cfg_combine(v_cond, v_uncond, cfg_scale)
+    if v_skip is not None:
+        v = v + slg_scale * (v_cond - v_skip)
+    return v
+
+
 def sample_step(x: np.ndarray, text_cond: np.ndarray, text_uncond: Optional[np.ndarray], W: Dict,
                 cfg: Config, step: int, sigma_table: np.ndarray, cfg_scale: float = 3.0,
                 uncond_skip_layers: Sequence[int] = (22,), slg_start: float = 0.01,
-                slg_stop: float = 1.0, mirror: bool = False, velocities: Optional[List] = None):
-    """One denoising step: DiT(cond), DiT(uncond, skipping uncond_skip_layers inside the SLG window),
-    CFG combine, Euler. x [1, C, h, w]. The negative pass runs only when CFG > 1 ([IV] "Skip layers":
-    the setting has no effect at CFG 1)."""
+                slg_stop: float = 1.0, mirror: bool = False, velocities: Optional[List] = None,
+                slg_scale: float = 0.0, cfg_truncation: float = 1.0):
+    """One denoising step: DiT(cond); DiT(uncond) when the negative branch runs (CFG > 1 and not
+    truncated), skipping uncond_skip_layers inside the SLG window; with slg_scale > 0 (three-pass
+    skip-layer guidance) inside the same window, DiT(cond) skipping the same layers; the guidance
+    combine; Euler. x [1, C, h, w]. Readings: the third pass skips the same list in the same window
+    (the cookbook's advice to set uncond_skip_layers also for three-pass SLG), and it is the negative
+    branch alone that CFG 1 or truncation removes."""
     N = len(sigma_table) - 1
     s, s_next = float(sigma_table[step]), float(sigma_table[step + 1])
-    if cfg_scale == 1.0:
-        v_c = forward(x, text_cond, [s], W, cfg, mirror=mirror)
-        v = cfg_combine(v_c, None, 1.0)
-        v_u = None
-    else:
-        skip_u = set(uncond_skip_layers) if slg_active(step, N, slg_start, slg_stop) else set()
-        lat = np.concatenate([x, x], axis=0)
-        txt = np.concatenate([text_cond, text_uncond], axis=0)
-        vv = forward(lat, txt, [s, s], W, cfg, skip=[set(), skip_u], mirror=mirror)
-        v_c, v_u = vv[0:1], vv[1:2]
-        v = cfg_combine(v_c, v_u, cfg_scale)
+    window = slg_active(step, N, slg_start, slg_stop)
+    skip = set(uncond_skip_layers) if window else set()
+    neg = negative_pass_runs(step, N, cfg_scale, cfg_truncation)
+    third = slg_scale > 0.0 and len(skip) > 0
+    lat, txt, sig, skips = [x], [text_cond], [s], [set()]
+    if neg:
+        lat.append(x), txt.append(text_uncond), sig.append(s), skips.append(skip)
+    if third:
+        lat.append(x), txt.append(text_cond), sig.append(s), skips.append(skip)
+    vv = forward(np.concatenate(lat, axis=0), np.concatenate(txt, axis=0), sig, W, cfg, skip=skips,
+                 mirror=mirror)
+    v_c = vv[0:1]
+    v_u = vv[1:2] if neg else None
+    v_s = vv[len(lat) - 1:len(lat)] if third else None
+    v = guidance_combine(v_c, v_u, v_s, cfg_scale, slg_scale)
     if velocities is not None:
-        velocities.append((v_c, v_u))
+        velocities.append((v_c, v_u, v_s))
     return euler_step(x, v, s, s_next)
 
 

@@ -471,6 +471,79 @@ def test_sample_step_guidance_paths():
     np.testing.assert_allclose(b, x + (sig[2] - sig[1]) * v_ref, atol=1e-14)
 
 
+def test_cfg_truncation_boundary_table():
+    # "drops the negative branch from step X * steps on" (MossInfer guide, lossy accelerators); steps
+    # are numbered from 0, X = 1 (the default) is off, and CFG 1 runs no negative branch at all.
+    runs = lambda X, N, cfg=3.0: [i for i in range(N) if O.negative_pass_runs(i, N, cfg, X)]
+    assert runs(1.0, 50) == list(range(50))
+    assert runs(0.0, 50) == []
+    assert runs(0.8, 50) == list(range(40))
+    assert runs(0.5, 3) == [0, 1]           # 1.5: step 1 still runs, step 2 does not
+    assert runs(0.5, 2) == [0]
+    assert runs(1.0, 50, cfg=1.0) == []
+
+
+def test_guidance_combine_hand_values():
+    one, zero, quarter = np.ones(3), np.zeros(3), np.full(3, 0.25)
+    # v_u + cfg (v_c - v_u) + slg (v_c - v_s) = 0 + 3*1 + 2*0.75
+    np.testing.assert_array_equal(O.guidance_combine(one, zero, quarter, 3.0, 2.0), np.full(3, 4.5))
+    # no negative branch: v_c + slg (v_c - v_s) = 1 + 2*0.75
+    np.testing.assert_array_equal(O.guidance_combine(one, None, quarter, 3.0, 2.0), np.full(3, 2.5))
+    # no third prediction: the two-pass combine, and v_c alone without a negative branch
+    np.testing.assert_array_equal(O.guidance_combine(one, zero, None, 3.0, 2.0), np.full(3, 3.0))
+    np.testing.assert_array_equal(O.guidance_combine(one, None, None, 3.0, 2.0), one)
+    rng = np.random.default_rng(21)
+    vc, vu, vs = rng.standard_normal((3, 50))
+    # v_s = v_c adds nothing, bitwise; the term is linear in slg_scale
+    np.testing.assert_array_equal(O.guidance_combine(vc, vu, vc, 3.0, 5.0), O.cfg_combine(vc, vu, 3.0))
+    f = lambda g: O.guidance_combine(vc, vu, vs, 3.0, g)
+    np.testing.assert_allclose(f(2.5) - f(0.0), (f(1.0) - f(0.0)) + (f(1.5) - f(0.0)), atol=1e-13)
+
+
+def test_three_pass_slg_and_truncation_paths():
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(22)
+    W = _tiny_weights(cfg, rng)
+    x = rng.standard_normal((1, 32, 4, 4))
+    tc = rng.standard_normal((1, 3, cfg.hidden))
+    tu = np.zeros_like(tc)
+    sig = O.sigmas(2, 5.0)
+    two = O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, (1,))
+    # step 1 is inside the default window: the third row is the conditional forward with block 1
+    # skipped, i.e. with block 1's gate rows zeroed (an independent route to the same prediction)
+    vel = []
+    three = O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, (1,), velocities=vel, slg_scale=2.0)
+    v_c, v_u, v_s = vel[0]
+    W0 = {k: (list(v) if isinstance(v, list) else v) for k, v in W.items()}
+    mw = W["mod_w"][1].copy()
+    mw[2 * cfg.hidden:3 * cfg.hidden] = 0.0
+    mw[5 * cfg.hidden:] = 0.0
+    W0["mod_w"] = [W["mod_w"][0], mw]
+    np.testing.assert_array_equal(v_s, O.forward(x, tc, [sig[1]], W0, cfg))
+    np.testing.assert_array_equal(v_c, O.forward(x, tc, [sig[1]], W, cfg))
+    assert not np.allclose(three, two)
+    dv = (three - two) / (sig[2] - sig[1])
+    np.testing.assert_allclose(dv, 2.0 * (v_c - v_s), atol=1e-10)
+    # the same step without the term: slg 0, an empty skip list, or a step outside the window
+    np.testing.assert_array_equal(O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, (1,), slg_scale=0.0), two)
+    np.testing.assert_array_equal(O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, (), slg_scale=2.0),
+                                  O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, ()))
+    np.testing.assert_array_equal(O.sample_step(x, tc, tu, W, cfg, 0, sig, 3.0, (1,), slg_scale=2.0),
+                                  O.sample_step(x, tc, tu, W, cfg, 0, sig, 3.0, (1,)))
+    # truncation at X = 0.5 of 2 steps: step 1 runs without the negative branch, i.e. as at CFG 1
+    vel = []
+    tr = O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, (1,), velocities=vel, cfg_truncation=0.5)
+    assert vel[0][1] is None and vel[0][2] is None
+    np.testing.assert_array_equal(tr, O.sample_step(x, tc, None, W, cfg, 1, sig, 1.0, (1,)))
+    np.testing.assert_array_equal(O.sample_step(x, tc, tu, W, cfg, 0, sig, 3.0, (1,), cfg_truncation=0.5),
+                                  O.sample_step(x, tc, tu, W, cfg, 0, sig, 3.0, (1,)))
+    # truncated three-pass step: v_c + slg (v_c - v_s)
+    vel = []
+    trs = O.sample_step(x, tc, tu, W, cfg, 1, sig, 3.0, (1,), velocities=vel, slg_scale=2.0, cfg_truncation=0.5)
+    assert vel[0][1] is None
+    np.testing.assert_allclose((trs - x) / (sig[2] - sig[1]), 3.0 * v_c - 2.0 * v_s, atol=1e-10)
+
+
 # ------------------------------------------------------------------------------------------------
 # dimension pins (the SwiGLU / shape readings against the pages' printed sizes)
 # ------------------------------------------------------------------------------------------------
