@@ -135,6 +135,10 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=3, help="steps of the per-kernel event pass")
     ap.add_argument("--text-len", type=int, default=256)
     ap.add_argument("--latent", type=int, default=128, help="latent side (1024 px / 8)")
+    ap.add_argument("--variant-steps", type=int, default=3,
+                    help="steps timed for each guidance variant (three-pass SLG, CFG truncation; 0 = skip)")
+    ap.add_argument("--steps-2048", type=int, default=2,
+                    help="window steps timed at 2048^2 with 4096 text tokens, for its s/image (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="MiB of a plain device-to-device copy run once before the steps (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -205,8 +209,13 @@ def main():
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
     fwd_per_s = 2.0 * 1000.0 / ms_step
-    step_flops = (2 * L - 1) * (block_linear_flops(S, D, F) + attention_flops(1, S, D)) + \
-        2 * (2.0 * N * P * D) * 2 + 2.0 * 2 * mod_rows * 256
+    def flops_of_step(block_samples, rows, S_, N_):
+        # blocks run per (sample, block) pair; patch embedding + final projection and the modulation
+        # GEMV per row
+        return block_samples * (block_linear_flops(S_, D, F) + attention_flops(1, S_, D)) + \
+            rows * (2.0 * N_ * P * D) * 2 + 2.0 * rows * mod_rows * 256
+
+    step_flops = flops_of_step(2 * L - 1, 2, S, N)
     mfma_frac = step_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
     log(f"[bench] {ms_step:.2f} ms/step, {fwd_per_s:.2f} forwards/s, whole-step MFMA fraction {mfma_frac:.3f}")
 
@@ -258,6 +267,60 @@ def main():
         assert torch.isfinite(x).all().item()
         log(f"[bench] {args.image_steps}-step image: {s_image:.2f} s (DiT + guidance only)")
 
+    def timed(fn, n):
+        fn(0)                                     # untimed: grows the workspace for a new shape
+        torch.cuda.synchronize()
+        start.record()
+        for k in range(n):
+            fn(k)
+        end.record()
+        end.synchronize()
+        return start.elapsed_time(end) / n
+
+    # ---- guidance variants at the same size: three-pass skip-layer guidance inside the window (rows
+    # cond, uncond skipping 22, cond skipping 22) and a CFG-truncated step (the conditional row only) ----
+    variants = None
+    if args.variant_steps > 0:
+        x.copy_(x0)
+        ms3 = timed(lambda k: model.moss_sample_step(x, text_cond, text_uncond, sig, 1 + (k % 49), cfg_scale=3.0,
+                                                     uncond_skip_layers=[22], slg_scale=2.5), args.variant_steps)
+        ms1 = timed(lambda k: model.moss_sample_step(x, text_cond, text_uncond, sig, 25 + (k % 25), cfg_scale=3.0,
+                                                     uncond_skip_layers=[22], cfg_truncation=0.5), args.variant_steps)
+        f3, f1 = flops_of_step(3 * L - 2, 3, S, N), flops_of_step(L, 1, S, N)
+        variants = {
+            "three_pass_slg": {"ms_per_step": round(ms3, 3), "rows": 3, "slg_scale": 2.5,
+                               "tflops": round(f3 / (ms3 * 1e-3) / 1e12, 1),
+                               "mfma_fraction": round(f3 / (ms3 * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)},
+            "cfg_truncated": {"ms_per_step": round(ms1, 3), "rows": 1, "cfg_truncation": 0.5,
+                              "tflops": round(f1 / (ms1 * 1e-3) / 1e12, 1),
+                              "mfma_fraction": round(f1 / (ms1 * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)},
+        }
+        log(f"[bench] guidance variants: {json.dumps(variants)}")
+
+    # ---- 2048^2 with a 4096-token prompt (16384 image tokens, S = 20480): step 0 (full CFG) and
+    # window steps, 50-step image = step 0 + 49 window steps ----
+    big = None
+    if args.steps_2048 > 0:
+        T2, side2 = 4096, 256
+        N2 = (side2 // 2) ** 2
+        S2 = T2 + N2
+        tc2 = torch.randn((1, T2, D), generator=g, device="cuda", dtype=torch.float32)
+        tu2 = torch.zeros_like(tc2)
+        x2 = torch.randn((1, 32, side2, side2), generator=g, device="cuda", dtype=torch.float32)
+        sig2 = dt.moss_sigmas(50, 5.0)
+        ms0 = timed(lambda k: model.moss_sample_step(x2, tc2, tu2, sig2, 0, cfg_scale=3.0, uncond_skip_layers=[22]), 1)
+        msw = timed(lambda k: model.moss_sample_step(x2, tc2, tu2, sig2, 1 + k, cfg_scale=3.0,
+                                                     uncond_skip_layers=[22]), args.steps_2048)
+        assert torch.isfinite(x2).all().item()
+        fw = flops_of_step(2 * L - 1, 2, S2, N2)
+        big = {"s_per_image": round((ms0 + 49 * msw) / 1000.0, 3), "ms_step0": round(ms0, 2),
+               "ms_per_window_step": round(msw, 2), "seq_len": S2, "text_len": T2, "image_tokens": N2,
+               "tflops": round(fw / (msw * 1e-3) / 1e12, 1),
+               "mfma_fraction": round(fw / (msw * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+               "method": "step 0 (full CFG) + 49 x the mean of the timed window steps (negative pass skips 22)"}
+        log(f"[bench] 2048^2: {json.dumps(big)}")
+        del tc2, tu2, x2
+
     cpu = None
     if args.cpu_baseline_blocks > 0:
         log(f"[bench] cpu_baseline: oracle on {args.cpu_baseline_blocks} block(s) of one sample")
@@ -278,6 +341,8 @@ def main():
         "step_tflop": round(step_flops / 1e12, 2),
         "roofline": roof,
         "kernels": kernels,
+        "guidance_variants": variants,
+        "sampling_2048": big,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

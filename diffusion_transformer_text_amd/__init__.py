@@ -63,7 +63,8 @@ class moss_step_args(C.Structure):
                 ("text_len", C.c_int32), ("num_steps", C.c_int32), ("step", C.c_int32), ("x", C.c_void_p),
                 ("text_cond", C.c_void_p), ("text_uncond", C.c_void_p), ("sigmas", C.POINTER(C.c_float)),
                 ("cfg_scale", C.c_float), ("slg_start", C.c_float), ("slg_stop", C.c_float),
-                ("uncond_skip_layers", C.POINTER(C.c_int32)), ("n_skip", C.c_int32)]
+                ("uncond_skip_layers", C.POINTER(C.c_int32)), ("n_skip", C.c_int32), ("slg_scale", C.c_float),
+                ("cfg_truncation", C.c_float)]
 
 
 class moss_block_taps(C.Structure):
@@ -95,6 +96,7 @@ _sig("moss_sigmas", C.c_int, C.c_int32, C.c_float, C.POINTER(C.c_float))
 _sig("moss_sample_step", C.c_int, _P, C.POINTER(moss_step_args), _P)
 _sig("moss_validate_step_args", C.c_int, C.POINTER(moss_dit_config), C.POINTER(moss_step_args), C.c_char_p, C.c_int32)
 _sig("moss_cfg_euler", C.c_int, _P, _P, _P, C.c_int64, C.c_float, C.c_float, C.c_float, _P)
+_sig("moss_guidance_euler", C.c_int, _P, _P, _P, _P, C.c_int64, C.c_float, C.c_float, C.c_float, C.c_float, _P)
 _sig("moss_dit_modulation", C.c_int, _P, C.POINTER(C.c_float), C.c_int32, _P, _P)
 _sig("moss_dit_block", C.c_int, _P, C.c_int32, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64,
      C.POINTER(moss_block_taps), _P)
@@ -110,7 +112,8 @@ PROF_CLASSES = ["modulation", "embed", "ln_mod", "gemm_qkv_rope", "attention", "
 EXPORTED = ["moss_dit_abi_version", "moss_status_string", "moss_dit_last_error", "moss_dit_config_init",
             "moss_dit_weights_init", "moss_dit_create", "moss_dit_destroy", "moss_forward_args_init",
             "moss_dit_forward", "moss_validate_forward_args", "moss_sigmas", "moss_step_args_init",
-            "moss_sample_step", "moss_validate_step_args", "moss_cfg_euler", "moss_dit_modulation",
+            "moss_sample_step", "moss_validate_step_args", "moss_cfg_euler", "moss_guidance_euler",
+            "moss_dit_modulation",
             "moss_block_taps_init", "moss_dit_block", "moss_attention", "moss_gemm_bf16",
             "moss_dit_profile_enable", "moss_dit_profile_read"]
 
@@ -203,6 +206,18 @@ def moss_cfg_euler(v_cond, v_uncond, x, cfg: float, sigma: float, sigma_next: fl
         _check_dev(v_uncond, torch.float32, "v_uncond")
     _check(_lib.moss_cfg_euler(_ptr(v_cond), _ptr(v_uncond), _ptr(x), x.numel(), cfg, sigma, sigma_next,
                                _stream(stream)))
+
+
+def moss_guidance_euler(v_cond, v_uncond, v_skip, x, cfg: float, slg: float, sigma: float, sigma_next: float,
+                        stream=None):
+    import torch
+    for t, n in ((v_cond, "v_cond"), (x, "x")):
+        _check_dev(t, torch.float32, n)
+    for t, n in ((v_uncond, "v_uncond"), (v_skip, "v_skip")):
+        if t is not None:
+            _check_dev(t, torch.float32, n)
+    _check(_lib.moss_guidance_euler(_ptr(v_cond), _ptr(v_uncond), _ptr(v_skip), _ptr(x), x.numel(), cfg, slg, sigma,
+                                    sigma_next, _stream(stream)))
 
 
 def moss_attention(qkv, out, batch: int, seq: int, heads: int, text_len: int, grid_w: int, rope: bool = True,
@@ -310,7 +325,7 @@ class MossDiT:
 
     def moss_sample_step(self, x, text_cond, text_uncond, sigmas: np.ndarray, step: int, cfg_scale: float = 3.0,
                          uncond_skip_layers: Sequence[int] = (22,), slg_start: float = 0.01, slg_stop: float = 1.0,
-                         stream=None):
+                         slg_scale: float = 0.0, cfg_truncation: float = 1.0, stream=None):
         import torch
         _check_dev(x, torch.float32, "x")
         _check_dev(text_cond, torch.float32, "text_cond")
@@ -327,6 +342,7 @@ class MossDiT:
         sk = (C.c_int32 * max(1, len(uncond_skip_layers)))(*[int(l) for l in uncond_skip_layers])
         a.uncond_skip_layers = C.cast(sk, C.POINTER(C.c_int32))
         a.n_skip = len(uncond_skip_layers)
+        a.slg_scale, a.cfg_truncation = slg_scale, cfg_truncation
         _check(_lib.moss_sample_step(self.handle, C.byref(a), _stream(stream)), self.handle)
 
     def moss_dit_modulation(self, sigma: Sequence[float], mod, stream=None):

@@ -282,6 +282,14 @@ int validate_step(const moss_dit_config* c, const moss_step_args* a, std::string
     msg = "slg_start and slg_stop must be finite";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
+  if (!std::isfinite(a->slg_scale) || a->slg_scale < 0.f) {
+    msg = "slg_scale must be finite and >= 0";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (!std::isfinite(a->cfg_truncation) || a->cfg_truncation < 0.f || a->cfg_truncation > 1.f) {
+    msg = "cfg_truncation must be in [0, 1] (1 = off)";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
   if (!a->x || !a->text_cond || !a->sigmas) {
     msg = "x, text_cond and sigmas must not be NULL";
     return MOSS_ERR_INVALID_ARGUMENT;
@@ -335,7 +343,7 @@ size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, 
   t.tokens = (uint16_t*)take((size_t)B * N * P * 2);
   t.mod = (uint16_t*)take((size_t)B * H->mod_rows() * 2);
   t.u = (float*)take((size_t)B * k.temb_dim * 4);
-  t.vel = (float*)take((size_t)2 * lat_elems * 4);
+  t.vel = (float*)take((size_t)B * lat_elems * 4);   // one velocity per row of the step's batch
   if (c) *c = t;
   return off;
 }
@@ -643,6 +651,8 @@ void moss_step_args_init(moss_step_args* a, uint32_t size) {
   d.slg_stop = 1.0f;
   d.uncond_skip_layers = kDefaultSkip;
   d.n_skip = 1;
+  d.slg_scale = 0.0f;
+  d.cfg_truncation = 1.0f;
   memcpy(a, &d, size < sizeof d ? size : sizeof d);
 }
 
@@ -834,8 +844,17 @@ int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream) {
   std::string msg;
   if ((s = validate_step(&h->cfg, a, msg))) return fail(h, s, msg);
   const moss_dit_config& k = h->cfg;
-  const bool guided = a->cfg_scale > 1.f;
-  const int B = guided ? 2 : 1;
+  // Rows of the batch: [cond | uncond (negative branch) | cond skipping layers (three-pass SLG)].
+  // The skip-layer window is on the progress step/num_steps, inclusive at both ends; the negative
+  // branch runs for cfg > 1 until step cfg_truncation * num_steps.
+  const double prog = (double)a->step / (double)a->num_steps;
+  const bool window = (double)a->slg_start <= prog && prog <= (double)a->slg_stop;
+  uint64_t mask = 0;
+  if (window)
+    for (int i = 0; i < a->n_skip; ++i) mask |= 1ULL << a->uncond_skip_layers[i];
+  const bool neg = a->cfg_scale > 1.f && (double)a->step < (double)a->cfg_truncation * (double)a->num_steps;
+  const bool third = a->slg_scale > 0.f && mask != 0;
+  const int B = 1 + (neg ? 1 : 0) + (third ? 1 : 0);
   const int N = (a->latent_h / 2) * (a->latent_w / 2), S = a->text_len + N;
   const int lat = k.latent_channels * a->latent_h * a->latent_w;
   if ((s = ensure_ws(h, carve(h, B, S, N, lat, nullptr, nullptr)))) return s;
@@ -848,27 +867,21 @@ int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream) {
   p.lat_w = a->latent_w;
   p.T = a->text_len;
   const float sig = a->sigmas[a->step], sig_next = a->sigmas[a->step + 1];
-  p.lat.p[0] = a->x;
-  p.txt.p[0] = a->text_cond;
-  p.sigma[0] = sig;
-  if (guided) {
-    // skip-layer guidance window on the progress step/num_steps, inclusive at both ends
-    const double prog = (double)a->step / (double)a->num_steps;
-    const bool active = (double)a->slg_start <= prog && prog <= (double)a->slg_stop;
-    uint64_t mask = 0;
-    if (active)
-      for (int i = 0; i < a->n_skip; ++i) mask |= 1ULL << a->uncond_skip_layers[i];
-    p.lat.p[1] = a->x;
-    p.txt.p[1] = a->text_uncond;
-    p.sigma[1] = sig;
-    p.skip[1] = mask;
+  for (int r = 0; r < B; ++r) {
+    const bool is_uncond = neg && r == 1;
+    p.lat.p[r] = a->x;
+    p.txt.p[r] = is_uncond ? a->text_uncond : a->text_cond;
+    p.sigma[r] = sig;
+    p.skip[r] = r == 0 ? 0 : mask;
   }
   p.vel = c.vel;
   if ((s = run_forward(h, p, c, (hipStream_t)stream))) return s;
-  // A12: FP32 CFG combine + Euler, in place on x
+  // A12: FP32 guidance combine + Euler, in place on x
   ProfScope ps(h, PC_CFG, (hipStream_t)stream);
-  HIP_TRY(h, launch_cfg_euler(c.vel, guided ? c.vel + lat : nullptr, a->x, lat, a->cfg_scale, sig, sig_next,
-                              (hipStream_t)stream));
+  const float* v_u = neg ? c.vel + lat : nullptr;
+  const float* v_s = third ? c.vel + (long)(B - 1) * lat : nullptr;
+  HIP_TRY(h, launch_guidance_euler(c.vel, v_u, v_s, a->x, lat, a->cfg_scale, a->slg_scale, sig, sig_next,
+                                   (hipStream_t)stream));
   return MOSS_OK;
 }
 
@@ -886,6 +899,26 @@ int moss_cfg_euler(const float* v_cond, const float* v_uncond, float* x, int64_t
                                         (hipStream_t)stream);
   if (e != hipSuccess) {
     g_thread_error = fmt("moss_cfg_euler launch failed: %s", hipGetErrorString(e));
+    return MOSS_ERR_DEVICE;
+  }
+  return MOSS_OK;
+}
+
+int moss_guidance_euler(const float* v_cond, const float* v_uncond, const float* v_skip, float* x, int64_t n,
+                        float cfg, float slg, float sigma, float sigma_next, void* stream) {
+  if (!v_cond || !x || n < 0 || !std::isfinite(cfg) || cfg < 1.f || !std::isfinite(slg)) {
+    g_thread_error = "moss_guidance_euler: v_cond and x must be non-NULL, cfg >= 1 and slg finite";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if ((reinterpret_cast<uintptr_t>(v_cond) | reinterpret_cast<uintptr_t>(v_uncond) |
+       reinterpret_cast<uintptr_t>(v_skip) | reinterpret_cast<uintptr_t>(x)) & 15) {
+    g_thread_error = "moss_guidance_euler: pointers must be 16-byte aligned";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = launch_guidance_euler(v_cond, v_uncond, v_skip, x, n, cfg, slg, sigma, sigma_next,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_thread_error = fmt("moss_guidance_euler launch failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;

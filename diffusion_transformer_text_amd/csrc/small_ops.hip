@@ -105,8 +105,12 @@ __global__ void text_cast_kernel(PtrBatch text, int B, int T, int D, int S, uint
 
 // Fused FP32 classifier-free guidance and flow-matching Euler step ("MOSS-Image" SGLang cookbook,
 // "Guidance and precision": CFG arithmetic and scheduler updates in FP32).
-__global__ void cfg_euler_kernel(const float* __restrict__ vc, const float* __restrict__ vu, float* __restrict__ x,
-                                 long n, float cfg, float dt) {
+// Guided velocity and Euler update, all fp32: v = v_c, or v_u + cfg (v_c - v_u) when the negative
+// branch ran (vu != nullptr); plus slg (v_c - v_s) when the skipped conditional prediction ran
+// (vs != nullptr); then x += dt v. With vs == v_c the extra term is exactly zero.
+__global__ void guidance_euler_kernel(const float* __restrict__ vc, const float* __restrict__ vu,
+                                      const float* __restrict__ vs, float* __restrict__ x, long n, float cfg,
+                                      float slg, float dt) {
   const long n4 = n / 4;
   const long stride = (long)gridDim.x * blockDim.x;
   const long t0 = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -121,6 +125,13 @@ __global__ void cfg_euler_kernel(const float* __restrict__ vc, const float* __re
       v.z = u.z + cfg * (c.z - u.z);
       v.w = u.w + cfg * (c.w - u.w);
     }
+    if (vs != nullptr) {
+      const float4 k = reinterpret_cast<const float4*>(vs)[i];
+      v.x = v.x + slg * (c.x - k.x);
+      v.y = v.y + slg * (c.y - k.y);
+      v.z = v.z + slg * (c.z - k.z);
+      v.w = v.w + slg * (c.w - k.w);
+    }
     xv.x = xv.x + dt * v.x;
     xv.y = xv.y + dt * v.y;
     xv.z = xv.z + dt * v.z;
@@ -130,6 +141,7 @@ __global__ void cfg_euler_kernel(const float* __restrict__ vc, const float* __re
   for (long i = n4 * 4 + t0; i < n; i += stride) {
     float v = vc[i];
     if (vu != nullptr) v = vu[i] + cfg * (vc[i] - vu[i]);
+    if (vs != nullptr) v = v + slg * (vc[i] - vs[i]);
     x[i] = x[i] + dt * v;
   }
 }
@@ -172,17 +184,23 @@ hipError_t launch_text_cast(PtrBatch text, int B, int T, int D, int S, uint16_t*
   return hipGetLastError();
 }
 
-hipError_t launch_cfg_euler(const float* v_c, const float* v_u, float* x, long n, float cfg, float sigma,
-                            float sigma_next, hipStream_t stream) {
+hipError_t launch_guidance_euler(const float* v_c, const float* v_u, const float* v_s, float* x, long n, float cfg,
+                                 float slg, float sigma, float sigma_next, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  if ((reinterpret_cast<uintptr_t>(v_c) | reinterpret_cast<uintptr_t>(v_u) | reinterpret_cast<uintptr_t>(x)) & 15)
+  if ((reinterpret_cast<uintptr_t>(v_c) | reinterpret_cast<uintptr_t>(v_u) | reinterpret_cast<uintptr_t>(v_s) |
+       reinterpret_cast<uintptr_t>(x)) & 15)
     return hipErrorInvalidValue;
   long grid = (n / 4 + 255) / 256;
   if (grid < 1) grid = 1;
   if (grid > 2048) grid = 2048;
-  hipLaunchKernelGGL(cfg_euler_kernel, dim3((unsigned)grid), dim3(256), 0, stream, v_c, v_u, x, n, cfg,
-                     sigma_next - sigma);
+  hipLaunchKernelGGL(guidance_euler_kernel, dim3((unsigned)grid), dim3(256), 0, stream, v_c, v_u, v_s, x, n, cfg,
+                     slg, sigma_next - sigma);
   return hipGetLastError();
+}
+
+hipError_t launch_cfg_euler(const float* v_c, const float* v_u, float* x, long n, float cfg, float sigma,
+                            float sigma_next, hipStream_t stream) {
+  return launch_guidance_euler(v_c, v_u, nullptr, x, n, cfg, 0.f, sigma, sigma_next, stream);
 }
 
 }  // namespace moss

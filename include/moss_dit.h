@@ -126,9 +126,18 @@ int moss_validate_forward_args(const moss_dit_config* cfg, const moss_forward_ar
 int moss_sigmas(int32_t num_steps, float shift, float* sigmas /* host [num_steps + 1] */);
 
 /* ---------------------------------------------------------------------------------------------
- * One denoising step of one image: x_{step+1} = x_step + (sigma_{step+1} - sigma_step) * v, with
- * v = v_u + cfg_scale * (v_c - v_u) (cfg_scale > 1) or v = v_c (cfg_scale == 1, no negative pass).
- * The negative pass skips uncond_skip_layers when slg_start <= step/num_steps <= slg_stop. */
+ * One denoising step of one image: x_{step+1} = x_step + (sigma_{step+1} - sigma_step) * v.
+ *   - The conditional pass always runs: v_c.
+ *   - The negative (unconditional) pass runs when cfg_scale > 1 and step < cfg_truncation *
+ *     num_steps, skipping uncond_skip_layers when slg_start <= step/num_steps <= slg_stop
+ *     ("MOSS-Image" SGLang cookbook, "3. Guidance and precision"; CFG truncation drops the negative
+ *     branch from step X*steps on: MossInfer integration guide, feature table "Lossy accelerators").
+ *     Then v = v_u + cfg_scale * (v_c - v_u), else v = v_c.
+ *   - Three-pass skip-layer guidance (slg_scale > 0; the cookbook's "adds a skipped conditional
+ *     prediction"): inside the same window, a third pass runs the conditional input skipping the
+ *     same uncond_skip_layers, v_s, and v += slg_scale * (v_c - v_s). The pages give no formula; this
+ *     is the skip-layer guidance form. slg_scale = 0 (default) is the two-pass recipe.
+ * All guidance arithmetic is fp32. */
 typedef struct {
   uint32_t struct_size;
   int32_t latent_h, latent_w, text_len, num_steps, step;
@@ -140,8 +149,11 @@ typedef struct {
   float slg_start, slg_stop;
   const int32_t* uncond_skip_layers; /* host [n_skip], each in [0, num_layers)                       */
   int32_t n_skip;
+  float slg_scale;                   /* >= 0; > 0 runs the third (skipped conditional) pass           */
+  float cfg_truncation;              /* in [0, 1]; 1 = off                                            */
 } moss_step_args;
-/* Defaults: cfg 3, slg_start 0.01, slg_stop 1.0, uncond_skip_layers = {22}, num_steps 50, step 0. */
+/* Defaults: cfg 3, slg_start 0.01, slg_stop 1.0, uncond_skip_layers = {22}, num_steps 50, step 0,
+ * slg_scale 0 (two-pass), cfg_truncation 1 (off). */
 void moss_step_args_init(moss_step_args* a, uint32_t size);
 int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream);
 /* Host-only check of step arguments (no GPU needed). msg (may be NULL) receives the reason. */
@@ -153,6 +165,12 @@ int moss_validate_step_args(const moss_dit_config* cfg, const moss_step_args* a,
  * All pointers device fp32 [n], 16-byte aligned. */
 int moss_cfg_euler(const float* v_cond, const float* v_uncond, float* x, int64_t n, float cfg,
                    float sigma, float sigma_next, void* stream);
+
+/* The same with the three-pass skip-layer guidance term: v as above (v_uncond == NULL: no negative
+ * branch, any cfg >= 1 is then unused), plus slg * (v_cond - v_skip) when v_skip != NULL (slg finite).
+ * This is the combine moss_sample_step runs. All pointers device fp32 [n], 16-byte aligned. */
+int moss_guidance_euler(const float* v_cond, const float* v_uncond, const float* v_skip, float* x, int64_t n,
+                        float cfg, float slg, float sigma, float sigma_next, void* stream);
 
 #ifdef __cplusplus
 }

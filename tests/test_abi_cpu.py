@@ -78,6 +78,8 @@ def test_step_defaults_are_the_pages():
     assert s.slg_start == np.float32(g["slg_start"]) and s.slg_stop == g["slg_stop"]
     assert [s.uncond_skip_layers[i] for i in range(s.n_skip)] == g["uncond_skip_layers"]
     assert (s.latent_h * 8, s.latent_w * 8) == (g["height"], g["width"])
+    # the guidance variants are off by default: two-pass recipe, no CFG truncation
+    assert s.slg_scale == 0.0 and s.cfg_truncation == 1.0
 
 
 @pytest.mark.parametrize("N,shift", [(50, 5.0), (2, 5.0), (7, 1.0), (1000, 3.0)])
@@ -120,6 +122,11 @@ def test_validate_step_accepts_defaults_and_2048():
     ("step", 50, 1, "step"),
     ("num_steps", 0, 1, "num_steps"),
     ("struct_size", 8, 5, "struct_size"),
+    ("slg_scale", -0.5, 1, "slg_scale"),
+    ("slg_scale", float("inf"), 1, "slg_scale"),
+    ("cfg_truncation", 1.5, 1, "cfg_truncation"),
+    ("cfg_truncation", -0.1, 1, "cfg_truncation"),
+    ("cfg_truncation", float("nan"), 1, "cfg_truncation"),
 ])
 def test_validate_step_errors(field, value, status, needle):
     cfg = dt.moss_dit_config_init()

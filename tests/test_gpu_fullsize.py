@@ -8,6 +8,10 @@
   from the benchmark's seeded draw: the residual stream is dumped after every block and blocks
   0, 21, 22 and 41 are recomputed by the oracle on sampled rows from the GPU's input to that block;
   the embedding and the final layer + unpatchify are checked in full.
+* Whole sampling steps at the benchmark's shapes (the three-pass skip-layer guidance step at 1024^2,
+  three rows; a step at 2048^2 with a 4096-token prompt): the step equals the guidance combine of the
+  library's own batched forward (rows are computed independently, so the step's rows and the
+  forward's rows are the same numbers) up to fp32 rounding.
 
 The oracle computes a sampled row exactly: its keys and values come from every row of the sequence.
 """
@@ -16,7 +20,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import REL_L2_BF16, dev_bf16, host_bf16, host_bits, log, oracle_cfg, rel_l2
+from tests.gpu_util import REL_L2_BF16, REL_L2_FP32, dev_bf16, host_bf16, host_bits, log, oracle_cfg, rel_l2
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -162,3 +166,45 @@ def test_full_forward_1024_block_chain():
     model.close()
     for k, e in errs.items():
         assert e <= REL_L2_BF16, (k, e)
+
+
+def _step_vs_forward(model, T, side, step, slg_scale, seed):
+    D = 3072
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    tc = torch.randn((1, T, D), generator=g, device="cuda", dtype=torch.float32)
+    tu = torch.zeros_like(tc)
+    x0 = torch.randn((1, 32, side, side), generator=g, device="cuda", dtype=torch.float32)
+    sig = dt.moss_sigmas(50, 5.0)
+    x = x0.clone()
+    model.moss_sample_step(x, tc, tu, sig, step, cfg_scale=3.0, uncond_skip_layers=[22], slg_scale=slg_scale)
+    rows = 3 if slg_scale > 0 else 2
+    lat = torch.cat([x0] * rows).contiguous()
+    txt = torch.cat([tc, tu, tc][:rows]).contiguous()
+    vel = torch.empty_like(lat)
+    skip = [0, 1 << 22, 1 << 22][:rows]
+    model.moss_dit_forward(lat, txt, [float(sig[step])] * rows, vel, skip_mask=skip)
+    torch.cuda.synchronize()
+    assert torch.isfinite(x).all().item() and torch.isfinite(vel).all().item()
+    v = vel.cpu().numpy().astype(np.float64)
+    guided = v[1:2] + 3.0 * (v[0:1] - v[1:2])
+    if rows == 3:
+        guided = guided + slg_scale * (v[0:1] - v[2:3])
+    x_ref = x0.cpu().numpy().astype(np.float64) + float(sig[step + 1] - sig[step]) * guided
+    d_got = x.cpu().numpy().astype(np.float64) - x0.cpu().numpy()
+    d_ref = x_ref - x0.cpu().numpy()
+    return rel_l2(d_got, d_ref)
+
+
+@pytest.mark.timeout(600)
+def test_three_pass_step_1024_and_step_2048():
+    w = synth.torch_weights(synth.FULL, seed=0, device="cuda")
+    model = dt.MossDiT(dt.moss_dit_config_init(), w)
+    log("three-pass SLG step at 1024^2 (rows: cond, uncond skipping 22, cond skipping 22)")
+    e3 = _step_vs_forward(model, 256, 128, 5, 2.5, seed=7)
+    log(f"  update vs forward-based combine: rel-L2 {e3:.2e}")
+    log("step at 2048^2 with 4096 text tokens (S = 20480)")
+    e2 = _step_vs_forward(model, 4096, 256, 5, 0.0, seed=8)
+    log(f"  update vs forward-based combine: rel-L2 {e2:.2e}")
+    model.close()
+    assert e3 <= REL_L2_FP32 and e2 <= REL_L2_FP32

@@ -84,6 +84,42 @@ def test_cfg_euler_vs_oracle_and_identities():
     assert ulp.max() <= 1 and np.mean(ulp == 0) > 0.999
 
 
+def test_guidance_euler_vs_oracle_and_identities():
+    """The three-input combine: random inputs against the oracle's guidance_combine + Euler (fp64),
+    hand values of each term, and v_s = v_c giving the two-input kernel's result bit for bit."""
+    log("guidance_euler")
+    rng = np.random.default_rng(5)
+    n = 32 * 128 * 128 + 5                  # ragged tail
+    vc, vu, vs, x = (rng.standard_normal(n).astype(np.float32) for _ in range(4))
+    sig = O.sigmas(50, 5.0).astype(np.float32)
+    s, sn = float(sig[10]), float(sig[11])
+    tc, tu, ts = (torch.from_numpy(a).cuda() for a in (vc, vu, vs))
+    f64 = lambda a: a.astype(np.float64)
+    for vu_in, vu_ref in ((tu, f64(vu)), (None, None)):
+        tx = torch.from_numpy(x).cuda()
+        dt.moss_guidance_euler(tc, vu_in, ts, tx, 3.0, 2.5, s, sn)
+        torch.cuda.synchronize()
+        ref = O.euler_step(f64(x), O.guidance_combine(f64(vc), vu_ref, f64(vs), 3.0, 2.5), s, sn)
+        assert rel_l2(tx.cpu().numpy(), ref) <= REL_L2_FP32
+    # hand values: v_c = 1, v_u = 0, v_s = 0.25, cfg 3, slg 2 -> v = 4.5 (2.5 without v_u), x0 = 0
+    m = 1024
+    one, zero, q = (torch.full((m,), v, device="cuda") for v in (1.0, 0.0, 0.25))
+    for vu_in, v in ((zero, 4.5), (None, 2.5)):
+        tx = torch.zeros(m, device="cuda")
+        dt.moss_guidance_euler(one, vu_in, q, tx, 3.0, 2.0, 1.0, 0.5)
+        torch.cuda.synchronize()
+        assert torch.all(tx == -0.5 * v).item()
+    # v_s = v_c: the term vanishes exactly, so the result is moss_cfg_euler's bit for bit
+    outs = []
+    for fn in (lambda t: dt.moss_guidance_euler(tc, tu, tc.clone(), t, 3.0, 7.0, s, sn),
+               lambda t: dt.moss_cfg_euler(tc, tu, t, 3.0, s, sn)):
+        tx = torch.from_numpy(x).cuda()
+        fn(tx)
+        torch.cuda.synchronize()
+        outs.append(tx.cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
 def test_cfg_euler_point_mass_lands_on_target():
     """Driving the kernel with the point-mass field v = (x - x*)/sigma for 50 steps lands on x*."""
     log("cfg_euler point mass")

@@ -241,6 +241,86 @@ def test_sample_step_guidance_paths_bitwise():
     np.testing.assert_array_equal(xa.cpu().numpy(), xc.cpu().numpy())
 
 
+@pytest.mark.parametrize("mod_scale", MODES)
+@pytest.mark.parametrize("step,slg_scale,trunc", [(1, 2.5, 1.0), (1, 2.5, 0.5), (1, 0.0, 0.5), (0, 2.5, 0.5)])
+def test_guidance_variants_vs_oracle(mod_scale, step, slg_scale, trunc):
+    """Three-pass skip-layer guidance (a third, skipped conditional pass inside the window: step 1 of 2;
+    step 0 is outside) and CFG truncation (X = 0.5 of 2 steps drops the negative branch at step 1),
+    one step from identical inputs against the oracle. With the x50 modulation the skip-layer term
+    itself (three-pass minus two-pass update) is compared too."""
+    m, w, inp, W, ocfg, _ = model(mod_scale)
+    log(f"guidance variant mod_scale={mod_scale} step={step} slg={slg_scale} trunc={trunc}")
+    sig = dt.moss_sigmas(2, 5.0)
+    tc = torch.from_numpy(inp.text_cond).cuda()
+    tu = torch.from_numpy(inp.text_uncond).cuda()
+    args = dict(cfg_scale=3.0, uncond_skip_layers=[1])
+
+    def gpu(**kw):
+        x = torch.from_numpy(inp.latents.copy()).cuda()
+        m.moss_sample_step(x, tc, tu, sig, step, **kw)
+        torch.cuda.synchronize()
+        return x.cpu().numpy()
+
+    def ref(**kw):
+        f = lambda a: a.astype(np.float64)
+        return O.sample_step(f(inp.latents), f(inp.text_cond), f(inp.text_uncond), W, ocfg, step, f(sig), 3.0, (1,),
+                             0.01, 1.0, mirror=True, **kw)
+
+    x0 = inp.latents.astype(np.float64)
+    got = gpu(slg_scale=slg_scale, cfg_truncation=trunc, **args)
+    want = ref(slg_scale=slg_scale, cfg_truncation=trunc)
+    e = rel_l2(got - x0, want - x0)
+    log(f"  rel-L2 of the update {e:.3e}")
+    assert e <= REL_L2_BF16
+    if slg_scale > 0 and step == 1 and mod_scale == 50.0:
+        d_got = got - gpu(slg_scale=0.0, cfg_truncation=trunc, **args)
+        d_want = want - ref(slg_scale=0.0, cfg_truncation=trunc)
+        e2 = rel_l2(d_got, d_want)
+        log(f"  rel-L2 of the skip-layer term {e2:.3e}")
+        assert e2 <= REL_L2_BF16
+
+
+def test_guidance_variants_bitwise():
+    m, w, inp, W, ocfg, _ = model(50.0)
+    log("guidance variants bitwise")
+    sig = dt.moss_sigmas(2, 5.0)
+    tc = torch.from_numpy(inp.text_cond).cuda()
+    tu = torch.from_numpy(inp.text_uncond).cuda()
+
+    def step(i, **kw):
+        x = torch.from_numpy(inp.latents.copy()).cuda()
+        m.moss_sample_step(x, tc, tu if kw.get("cfg_scale", 3.0) > 1 else None, sig, i, **kw)
+        torch.cuda.synchronize()
+        return x.cpu().numpy()
+
+    # no third pass: outside the window (step 0), an empty skip list, or slg 0
+    np.testing.assert_array_equal(step(0, uncond_skip_layers=[1], slg_scale=2.5), step(0, uncond_skip_layers=[1]))
+    np.testing.assert_array_equal(step(1, uncond_skip_layers=[], slg_scale=2.5), step(1, uncond_skip_layers=[]))
+    # a truncated step is the CFG-1 step; before the truncation point nothing changes
+    np.testing.assert_array_equal(step(1, uncond_skip_layers=[1], cfg_truncation=0.5),
+                                  step(1, cfg_scale=1.0, uncond_skip_layers=[1]))
+    np.testing.assert_array_equal(step(0, uncond_skip_layers=[1], cfg_truncation=0.5), step(0, uncond_skip_layers=[1]))
+    # the three-pass step from the library's own predictions: rows [cond, uncond skipping 1, cond
+    # skipping 1] of one forward give v_c, v_u, v_s; the step applies v_u + 3 (v_c - v_u) + 2.5 (v_c - v_s)
+    lat = torch.from_numpy(np.concatenate([inp.latents] * 3)).cuda()
+    txt = torch.from_numpy(np.concatenate([inp.text_cond, inp.text_uncond, inp.text_cond])).cuda()
+    vel = torch.empty_like(lat)
+    m.moss_dit_forward(lat, txt, [float(sig[1])] * 3, vel, skip_mask=[0, 1 << 1, 1 << 1])
+    torch.cuda.synchronize()
+    v = vel.cpu().numpy().astype(np.float64)
+    vc, vu, vs = v[0:1], v[1:2], v[2:3]
+    assert not np.array_equal(vc, vs)
+    x3 = step(1, uncond_skip_layers=[1], slg_scale=2.5)
+    x_ref = inp.latents.astype(np.float64) + float(sig[2] - sig[1]) * (vu + 3.0 * (vc - vu) + 2.5 * (vc - vs))
+    assert rel_l2(x3, x_ref) <= REL_L2_FP32
+    # and the same step through the standalone combine entry point, bit for bit
+    xk = torch.from_numpy(inp.latents.copy()).cuda()
+    dt.moss_guidance_euler(vel[0:1].contiguous(), vel[1:2].contiguous(), vel[2:3].contiguous(), xk, 3.0, 2.5,
+                           float(sig[1]), float(sig[2]))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(xk.cpu().numpy(), x3)
+
+
 def test_residual_dump_and_skip_rows():
     m, w, inp, W, ocfg, _ = model(50.0)
     log("residual dump")
