@@ -12,6 +12,8 @@
 // fragment as the B operand, so the accumulator of lane l holds token (l % 32) and, per group of
 // four registers, four consecutive output features: the epilogue stores 8-byte runs and finds the
 // rotary pair (2k, 2k+1) and the gate/up pair in its own registers.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -56,6 +58,98 @@ __device__ __forceinline__ void tile_coords(int nM, int nN, int& tm, int& tn) {
   const int in_group = lin - group * per_group;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+
+// ---- epilogue: acc[i][j][4g + e] = C[token m, feature n + e] ----
+template <class T, int EPI>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, floatx16 (&acc)[T::TM][T::TN], int m0, int n0, int wm,
+                                           int wn, int fr, int fh) {
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i) {
+    const int m = m0 + wm * T::WM + i * 32 + fr;
+    if (m >= p.M) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // feature blocks (2q, 2q+1) of this wave are the gate and up rows of the same 32 h-columns
+      uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+      for (int q = 0; q < T::TN / 2; ++q) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int hc = (n0 + wn * T::WN) / 2 + q * 32 + 8 * g + 4 * fh;
+          float h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[i][2 * q][4 * g + e]) * acc[i][2 * q + 1][4 * g + e];
+          uint2 v;
+          v.x = pack2_bf16(h[0], h[1]);
+          v.y = pack2_bf16(h[2], h[3]);
+          *reinterpret_cast<uint2*>(out + (long)m * p.ldo + hc) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * T::WN + j * 32 + 8 * g + 4 * fh;
+          float c[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[e] = acc[i][j][4 * g + e];
+          if constexpr (EPI == EPI_BF16) {
+            const long orow = (long)(m / p.seg) * p.seg_stride + p.seg_off + m % p.seg;
+            uint2 v;
+            v.x = pack2_bf16(c[0], c[1]);
+            v.y = pack2_bf16(c[2], c[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow * p.ldo + n) = v;
+          } else if constexpr (EPI == EPI_QKV_ROPE) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c[e] = round_bf16(c[e]);
+            const int t = m % p.S;
+            if (n < p.rope_cols && t >= p.T) {
+              const int ni = t - p.T;
+              const int dim = n & (kHeadDim - 1);
+              const int pos = (dim < kHeadDim / 2) ? ni / p.grid_w : ni % p.grid_w;
+              const int k0 = (dim & (kHeadDim / 2 - 1)) >> 1;
+#pragma unroll
+              for (int pr = 0; pr < 2; ++pr) {
+                const float cs = p.rope_cos[pos * (kHeadDim / 4) + k0 + pr];
+                const float sn = p.rope_sin[pos * (kHeadDim / 4) + k0 + pr];
+                const float a = c[2 * pr], b = c[2 * pr + 1];
+                c[2 * pr] = a * cs - b * sn;
+                c[2 * pr + 1] = a * sn + b * cs;
+              }
+            }
+            uint2 v;
+            v.x = pack2_bf16(c[0], c[1]);
+            v.y = pack2_bf16(c[2], c[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (long)m * p.ldo + n) = v;
+          } else if constexpr (EPI == EPI_GATED_RES) {
+            uint16_t* xo = static_cast<uint16_t*>(p.out) + (long)m * p.ldo + n;
+            const uint2 xv = *reinterpret_cast<const uint2*>(xo);
+            const uint2 gv = *reinterpret_cast<const uint2*>(p.gate + (long)(m / p.rows_per_sample) * p.gate_stride + n);
+            const float x0 = __uint_as_float(xv.x << 16), x1 = __uint_as_float(xv.x & 0xffff0000u);
+            const float x2 = __uint_as_float(xv.y << 16), x3 = __uint_as_float(xv.y & 0xffff0000u);
+            const float g0 = __uint_as_float(gv.x << 16), g1 = __uint_as_float(gv.x & 0xffff0000u);
+            const float g2 = __uint_as_float(gv.y << 16), g3 = __uint_as_float(gv.y & 0xffff0000u);
+            uint2 v;
+            v.x = pack2_bf16(x0 + g0 * c[0], x1 + g1 * c[1]);
+            v.y = pack2_bf16(x2 + g2 * c[2], x3 + g3 * c[3]);
+            *reinterpret_cast<uint2*>(xo) = v;
+          } else if constexpr (EPI == EPI_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (long)m * p.ldo + n) =
+                make_float4(c[0], c[1], c[2], c[3]);
+          } else if constexpr (EPI == EPI_F32_UNPATCH) {
+            const int b = m / p.n_img, ni = m % p.n_img;
+            const int gw = p.lat_w / 2;
+            const int y = 2 * (ni / gw), x = 2 * (ni % gw);
+            const int ch = n >> 2;
+            float* v = static_cast<float*>(p.out) + (((long)b * p.C + ch) * p.lat_h + y) * p.lat_w + x;
+            *reinterpret_cast<float2*>(v) = make_float2(c[0], c[1]);
+            *reinterpret_cast<float2*>(v + p.lat_w) = make_float2(c[2], c[3]);
+          }
+        }
+      }
+    }
+  }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
@@ -158,93 +252,149 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_kernel(Ge
     }
   }
 
-  // ---- epilogue: acc[i][j][4g + e] = C[token m, feature n + e] ----
+  store_tile<T, EPI>(p, acc, m0, n0, wm, wn, fr, fh);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Deep-pipelined variant for the big projections: BK = 32 and four LDS stages (the same 128 KB as two
+// stages of BK = 64), so a k-tile's global -> LDS copies are issued three k-tiles before it is used
+// and have about three times as long to land. The stages are four separate LDS arrays and the k loop
+// is unrolled by four, so every LDS access names a fixed array: the compiler then sees that reading
+// one stage does not alias the copies still landing in the others and does not wait for them. The
+// wait for a k-tile is explicit (s_waitcnt vmcnt(N) with N = the copies issued after that k-tile),
+// followed by a barrier; the barrier sits between the two k16 slices of the previous k-tile, so the
+// next k-tile's first fragment reads overlap the second slice's MFMAs.
+// LDS rows are 32 bf16 (64 bytes, four 16-byte chunks); chunk c of row r is stored at chunk
+// c ^ ((r >> 2) & 3): the 16 rows a ds_read_b128 phase reads then cover 16 distinct (bank quarter,
+// chunk) slots (conflict-free), and a 1 KB copy window holds 16 whole rows.
+constexpr int BK2 = 32;
+__device__ __forceinline__ int swz2(int r, int c) { return r * BK2 + ((c ^ ((r >> 2) & 3)) << 3); }
+
+// Workgroup barrier for the deep pipeline: s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier. vmcnt(N)
+// leaves only the N newest copies in flight (the main loop issues no other vector-memory
+// instruction, and they complete in order), lgkmcnt(0) finishes this wave's LDS reads (so a stage
+// may be refilled after the barrier). The barrier is written as asm with a memory clobber on
+// purpose: __syncthreads() carries a workgroup fence, and the compiler treats the pending copies as
+// LDS writes under that fence and waits for all of them (vmcnt(0)), which would drain the pipeline.
+// The clobber keeps the compiler from moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void copy_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_deep_kernel(GemmArgs p) {
+  using T = Tile<BM, BN, WAVES_M, WAVES_N>;
+  constexpr int SZ = (BM + BN) * BK2;                     // elements per stage: A rows, then W rows
+  __shared__ __attribute__((aligned(16))) uint16_t st0[SZ];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[SZ];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[SZ];
+  __shared__ __attribute__((aligned(16))) uint16_t st3[SZ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int nN = p.N / BN, nM = (p.M + BM - 1) / BM;
+  int tm, tn;
+  tile_coords(nM, nN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // copy windows: 16 rows x 64 bytes; lane i writes LDS bytes 16 i (row i / 4, physical chunk i % 4)
+  // and so reads logical chunk (i % 4) ^ ((row >> 2) & 3) = (i % 4) ^ ((i >> 4) & 3) of its row
+  constexpr int A_WIN = BM / 16, W_WIN = BN / 16;
+  constexpr int A_PER_WAVE = A_WIN / T::NW, W_PER_WAVE = W_WIN / T::NW;
+  constexpr int LOADS = A_PER_WAVE + W_PER_WAVE;          // copies per wave per k-tile
+  static_assert(A_WIN % T::NW == 0 && W_WIN % T::NW == 0, "windows must split evenly over the waves");
+  static_assert(2 * LOADS < 16, "vmcnt immediate");
+  const int win_row = lane >> 2, win_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t a_off[A_PER_WAVE], w_off[W_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < T::TM; ++i) {
-    const int m = m0 + wm * T::WM + i * 32 + fr;
-    if (m >= p.M) continue;
-    if constexpr (EPI == EPI_SWIGLU) {
-      // feature blocks (2q, 2q+1) of this wave are the gate and up rows of the same 32 h-columns
-      uint16_t* out = static_cast<uint16_t*>(p.out);
-#pragma unroll
-      for (int q = 0; q < T::TN / 2; ++q) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int hc = (n0 + wn * T::WN) / 2 + q * 32 + 8 * g + 4 * fh;
-          float h[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[i][2 * q][4 * g + e]) * acc[i][2 * q + 1][4 * g + e];
-          uint2 v;
-          v.x = pack2_bf16(h[0], h[1]);
-          v.y = pack2_bf16(h[2], h[3]);
-          *reinterpret_cast<uint2*>(out + (long)m * p.ldo + hc) = v;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < T::TN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * T::WN + j * 32 + 8 * g + 4 * fh;
-          float c[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) c[e] = acc[i][j][4 * g + e];
-          if constexpr (EPI == EPI_BF16) {
-            const long orow = (long)(m / p.seg) * p.seg_stride + p.seg_off + m % p.seg;
-            uint2 v;
-            v.x = pack2_bf16(c[0], c[1]);
-            v.y = pack2_bf16(c[2], c[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + orow * p.ldo + n) = v;
-          } else if constexpr (EPI == EPI_QKV_ROPE) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) c[e] = round_bf16(c[e]);
-            const int t = m % p.S;
-            if (n < p.rope_cols && t >= p.T) {
-              const int ni = t - p.T;
-              const int dim = n & (kHeadDim - 1);
-              const int pos = (dim < kHeadDim / 2) ? ni / p.grid_w : ni % p.grid_w;
-              const int k0 = (dim & (kHeadDim / 2 - 1)) >> 1;
-#pragma unroll
-              for (int pr = 0; pr < 2; ++pr) {
-                const float cs = p.rope_cos[pos * (kHeadDim / 4) + k0 + pr];
-                const float sn = p.rope_sin[pos * (kHeadDim / 4) + k0 + pr];
-                const float a = c[2 * pr], b = c[2 * pr + 1];
-                c[2 * pr] = a * cs - b * sn;
-                c[2 * pr + 1] = a * sn + b * cs;
-              }
-            }
-            uint2 v;
-            v.x = pack2_bf16(c[0], c[1]);
-            v.y = pack2_bf16(c[2], c[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (long)m * p.ldo + n) = v;
-          } else if constexpr (EPI == EPI_GATED_RES) {
-            uint16_t* xo = static_cast<uint16_t*>(p.out) + (long)m * p.ldo + n;
-            const uint2 xv = *reinterpret_cast<const uint2*>(xo);
-            const uint2 gv = *reinterpret_cast<const uint2*>(p.gate + (long)(m / p.rows_per_sample) * p.gate_stride + n);
-            const float x0 = __uint_as_float(xv.x << 16), x1 = __uint_as_float(xv.x & 0xffff0000u);
-            const float x2 = __uint_as_float(xv.y << 16), x3 = __uint_as_float(xv.y & 0xffff0000u);
-            const float g0 = __uint_as_float(gv.x << 16), g1 = __uint_as_float(gv.x & 0xffff0000u);
-            const float g2 = __uint_as_float(gv.y << 16), g3 = __uint_as_float(gv.y & 0xffff0000u);
-            uint2 v;
-            v.x = pack2_bf16(x0 + g0 * c[0], x1 + g1 * c[1]);
-            v.y = pack2_bf16(x2 + g2 * c[2], x3 + g3 * c[3]);
-            *reinterpret_cast<uint2*>(xo) = v;
-          } else if constexpr (EPI == EPI_F32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (long)m * p.ldo + n) =
-                make_float4(c[0], c[1], c[2], c[3]);
-          } else if constexpr (EPI == EPI_F32_UNPATCH) {
-            const int b = m / p.n_img, ni = m % p.n_img;
-            const int gw = p.lat_w / 2;
-            const int y = 2 * (ni / gw), x = 2 * (ni % gw);
-            const int ch = n >> 2;
-            float* v = static_cast<float*>(p.out) + (((long)b * p.C + ch) * p.lat_h + y) * p.lat_w + x;
-            *reinterpret_cast<float2*>(v) = make_float2(c[0], c[1]);
-            *reinterpret_cast<float2*>(v + p.lat_w) = make_float2(c[2], c[3]);
-          }
-        }
-      }
-    }
+  for (int j = 0; j < A_PER_WAVE; ++j) {
+    const int r = min(m0 + (wave + T::NW * j) * 16 + win_row, p.M - 1);
+    a_off[j] = (uint32_t)(r * p.lda + win_chunk * 8);
   }
+#pragma unroll
+  for (int j = 0; j < W_PER_WAVE; ++j) {
+    const int r = n0 + (wave + T::NW * j) * 16 + win_row;
+    w_off[j] = (uint32_t)(r * p.ldw + win_chunk * 8);
+  }
+  // copies go through buffer resources over A and W (byte offsets < 2^31, checked at launch)
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (int)(2L * p.M * p.lda));
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, (int)(2L * p.N * p.ldw));
+  auto issue = [&](int kt, uint16_t* st) {
+    const int k0 = kt * BK2;
+#pragma unroll
+    for (int j = 0; j < A_PER_WAVE; ++j) buf_load_lds_16(rA, st + (wave + T::NW * j) * 512, 2 * (int)(a_off[j] + k0));
+#pragma unroll
+    for (int j = 0; j < W_PER_WAVE; ++j)
+      buf_load_lds_16(rW, st + BM * BK2 + (wave + T::NW * j) * 512, 2 * (int)(w_off[j] + k0));
+  };
+
+  floatx16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int fr = lane & 31, fh = lane >> 5;
+  const int a_row0 = wm * T::WM + fr, w_row0 = wn * T::WN + fr;
+  bf16x8 fa[2][T::TM], fw[2][T::TN];
+  auto load_frags = [&](const uint16_t* st, int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + swz2(a_row0 + i * 32, 2 * s + fh));
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+      fw[buf][j] = *reinterpret_cast<const bf16x8*>(st + BM * BK2 + swz2(w_row0 + j * 32, 2 * s + fh));
+  };
+  auto mfmas = [&](int buf) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int KT = p.K / BK2;                               // a multiple of 4 (checked at launch)
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  copy_barrier<2 * LOADS>();                              // k-tile 0 has landed
+  load_frags(st0, 0, 0);
+  // Step t: k-tile t is in stage t % 4 and its slice-0 fragments are in flight in buffer 0. ISSUE:
+  // copy k-tile t + 3 into `fill` (the stage of k-tile t - 1, whose last reads finished before the
+  // previous barrier). AFTER: k-tiles issued after k-tile t + 1 (2 in steady state; -1 = no next).
+  auto step = [&](auto issue_c, auto after_c, int t, const uint16_t* cur, const uint16_t* nxt, uint16_t* fill) {
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr int AFTER = decltype(after_c)::value;
+    if constexpr (ISSUE) issue(t + 3, fill);
+    load_frags(cur, 1, 1);
+    mfmas(0);
+    if constexpr (AFTER >= 0) {
+      copy_barrier<AFTER * LOADS>();
+      load_frags(nxt, 0, 0);
+    }
+    mfmas(1);
+  };
+  using Y = std::true_type;
+  using N = std::false_type;
+  using A2 = std::integral_constant<int, 2>;
+  int t = 0;
+  for (; t + 4 < KT; t += 4) {                            // steady state: straight-line code
+    step(Y{}, A2{}, t, st0, st1, st3);
+    step(Y{}, A2{}, t + 1, st1, st2, st0);
+    step(Y{}, A2{}, t + 2, st2, st3, st1);
+    step(Y{}, A2{}, t + 3, st3, st0, st2);
+  }
+  step(Y{}, A2{}, t, st0, st1, st3);                      // last four k-tiles: t = KT - 4
+  step(N{}, std::integral_constant<int, 1>{}, t + 1, st1, st2, st0);
+  step(N{}, std::integral_constant<int, 0>{}, t + 2, st2, st3, st1);
+  step(N{}, std::integral_constant<int, -1>{}, t + 3, st3, st0, st2);
+  store_tile<T, EPI>(p, acc, m0, n0, wm, wn, fr, fh);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -284,6 +434,24 @@ __global__ void interleave_gate_up_kernel(const uint16_t* __restrict__ src, uint
 
 }  // namespace
 
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+hipError_t launch_tile_deep(const GemmArgs& a, int epi, hipStream_t stream) {
+  const int nM = (a.M + BM - 1) / BM, nN = a.N / BN;
+  dim3 grid(nM * nN), block(64 * WAVES_M * WAVES_N);
+#define MOSS_GEMM_LAUNCH(E) \
+  hipLaunchKernelGGL((gemm_bf16_deep_kernel<BM, BN, WAVES_M, WAVES_N, E>), grid, block, 0, stream, a)
+  switch (epi) {
+    case EPI_BF16: MOSS_GEMM_LAUNCH(EPI_BF16); break;
+    case EPI_QKV_ROPE: MOSS_GEMM_LAUNCH(EPI_QKV_ROPE); break;
+    case EPI_GATED_RES: MOSS_GEMM_LAUNCH(EPI_GATED_RES); break;
+    case EPI_SWIGLU: MOSS_GEMM_LAUNCH(EPI_SWIGLU); break;
+    case EPI_F32: MOSS_GEMM_LAUNCH(EPI_F32); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOSS_GEMM_LAUNCH
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream) {
   if (a.M <= 0) return hipSuccess;
   if (a.K % BK != 0 || a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
@@ -291,7 +459,11 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream) {
   // SwiGLU pairs feature blocks inside a wave: the wave's feature width must hold whole 64-row groups.
   const bool big_n = (a.N % 256 == 0);
   const long tiles256 = (long)((a.M + 255) / 256) * (a.N / 256);
-  if (big_n && epi != EPI_F32_UNPATCH && a.M > 1024 && tiles256 >= 256) return launch_tile<256, 256, 2, 4>(a, epi, stream);
+  const bool fits32 = 2L * a.M * a.lda < (1L << 31) && 2L * a.N * a.ldw < (1L << 31);   // buffer byte offsets
+  if (big_n && epi != EPI_F32_UNPATCH && a.M > 1024 && tiles256 >= 256) {
+    if (fits32 && a.K % (4 * BK2) == 0) return launch_tile_deep<256, 256, 2, 4>(a, epi, stream);
+    return launch_tile<256, 256, 2, 4>(a, epi, stream);
+  }
   if (a.N % 128 == 0) return launch_tile<128, 128, 2, 2>(a, epi, stream);
   return hipErrorInvalidValue;
 }
