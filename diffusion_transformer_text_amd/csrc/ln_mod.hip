@@ -3,85 +3,100 @@
 // The fusion of LayerNorm with the "* (1 + scale)" modulation is the one the Qwen-Image 2.1 cookbook
 // describes for its single-stream DiT ("Lossless LayerNorm modulation"); MOSS-Image's joint blocks
 // take (shift, scale) from the per-block modulation layer. One wave normalises one row: the row is
-// read once from HBM into registers (8-byte loads, 512 contiguous bytes per wave instruction), mean
-// and then the centred variance are reduced across the wave in fp32, and the modulated row is
-// written once. The kernel is HBM-bound: 2 * D bytes read + 2 * D bytes written per row.
+// read once from HBM into registers (16-byte loads, 1 KB contiguous per wave instruction, when the
+// width allows), mean and then the centred variance are reduced across the wave in fp32, and the
+// modulated row is written once. The kernel is HBM-bound: 2 * D bytes read + 2 * D bytes written per row.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moss {
 namespace {
 
-constexpr int kMaxChunks = 16;   // D <= 16 * 256
+constexpr int kMaxElems = 64;   // elements per lane: D <= 64 * 64
 
+// E elements per lane per chunk (E = 8: 16-byte loads, D % 512 == 0; E = 4: 8-byte loads), NCH chunks
+// (D = 64 E NCH, a compile-time count so the row stays in exactly 3 NCH E / 2 registers). The
+// modulation rows (shift, scale; served from L2) are requested together with the activation row, so
+// their latency overlaps the row's HBM read instead of following the two reductions. The row is kept
+// as packed bf16 and unpacked in each pass (two VALU per pair) to keep occupancy up.
+template <int E, int NCH>
 __global__ __launch_bounds__(256) void ln_mod_kernel(LnModArgs p) {
+  typedef uint32_t words __attribute__((ext_vector_type(E / 2)));
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + wave;
   if (r >= p.rows) return;
-  const int nch = p.D >> 8;
+  constexpr int D = 64 * E * NCH;
   const long in_row = (long)(r / p.seg) * p.seg_stride + p.seg_off + r % p.seg;
-  const uint16_t* xr = p.x + in_row * p.D;
-
-  float v[kMaxChunks][4];
-  float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    if (c < nch) {
-      const uint2 u = *reinterpret_cast<const uint2*>(xr + (c * 64 + lane) * 4);
-      v[c][0] = __uint_as_float(u.x << 16);
-      v[c][1] = __uint_as_float(u.x & 0xffff0000u);
-      v[c][2] = __uint_as_float(u.y << 16);
-      v[c][3] = __uint_as_float(u.y & 0xffff0000u);
-      s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
-    }
-  }
-  const float inv_d = 1.0f / (float)p.D;
-  const float mean = wave_sum(s) * inv_d;
-  float q = 0.f;
-#pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    if (c < nch) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float d = v[c][e] - mean;
-        q += d * d;
-      }
-    }
-  }
-  const float var = wave_sum(q) * inv_d;
-  const float rstd = 1.0f / sqrtf(var + p.eps);
-
+  const uint16_t* xr = p.x + in_row * D;
   const long b = r / p.rows_per_sample;
   const uint16_t* sh = p.shift + b * p.mod_stride;
   const uint16_t* sc = p.scale + b * p.mod_stride;
-  uint16_t* o = p.out + (long)r * p.D;
+
+  words xw[NCH], sw[NCH], cw[NCH];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    if (c < nch) {
-      const int i0 = (c * 64 + lane) * 4;
-      const uint2 su = *reinterpret_cast<const uint2*>(sh + i0);
-      const uint2 cu = *reinterpret_cast<const uint2*>(sc + i0);
-      const float shv[4] = {__uint_as_float(su.x << 16), __uint_as_float(su.x & 0xffff0000u),
-                            __uint_as_float(su.y << 16), __uint_as_float(su.y & 0xffff0000u)};
-      const float scv[4] = {__uint_as_float(cu.x << 16), __uint_as_float(cu.x & 0xffff0000u),
-                            __uint_as_float(cu.y << 16), __uint_as_float(cu.y & 0xffff0000u)};
-      float y[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = (v[c][e] - mean) * rstd * (1.0f + scv[e]) + shv[e];
-      uint2 w;
-      w.x = pack2_bf16(y[0], y[1]);
-      w.y = pack2_bf16(y[2], y[3]);
-      *reinterpret_cast<uint2*>(o + i0) = w;
-    }
+  for (int c = 0; c < NCH; ++c) {
+    const int i0 = (c * 64 + lane) * E;
+    xw[c] = *reinterpret_cast<const words*>(xr + i0);
+    sw[c] = *reinterpret_cast<const words*>(sh + i0);
+    cw[c] = *reinterpret_cast<const words*>(sc + i0);
   }
+  auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+  auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int h = 0; h < E / 2; ++h) s += lo(xw[c][h]) + hi(xw[c][h]);
+  constexpr float inv_d = 1.0f / (float)D;
+  const float mean = wave_sum(s) * inv_d;
+  float q = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int h = 0; h < E / 2; ++h) {
+      const float d0 = lo(xw[c][h]) - mean, d1 = hi(xw[c][h]) - mean;
+      q += d0 * d0 + d1 * d1;
+    }
+  const float var = wave_sum(q) * inv_d;
+  const float rstd = 1.0f / sqrtf(var + p.eps);
+
+  uint16_t* o = p.out + (long)r * D;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    words w;
+#pragma unroll
+    for (int h = 0; h < E / 2; ++h) {
+      const float y0 = (lo(xw[c][h]) - mean) * rstd * (1.0f + lo(cw[c][h])) + lo(sw[c][h]);
+      const float y1 = (hi(xw[c][h]) - mean) * rstd * (1.0f + hi(cw[c][h])) + hi(sw[c][h]);
+      w[h] = pack2_bf16(y0, y1);
+    }
+    *reinterpret_cast<words*>(o + (c * 64 + lane) * E) = w;
+  }
+}
+
+template <int E, int NCH>
+void launch_ln_n(const LnModArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((ln_mod_kernel<E, NCH>), dim3((a.rows + 3) / 4), dim3(256), 0, stream, a);
+}
+
+template <int E, int... N>
+bool launch_ln_any(const LnModArgs& a, hipStream_t stream, std::integer_sequence<int, N...>) {
+  const int nch = a.D / (64 * E);
+  bool done = false;
+  ((nch == N + 1 ? (launch_ln_n<E, N + 1>(a, stream), done = true) : false), ...);
+  return done;
 }
 
 }  // namespace
 
 hipError_t launch_ln_mod(const LnModArgs& a, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  if (a.D % 256 != 0 || a.D > kMaxChunks * 256 || a.seg <= 0 || a.rows_per_sample <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(ln_mod_kernel, dim3((a.rows + 3) / 4), dim3(256), 0, stream, a);
+  if (a.D % 256 != 0 || a.D > kMaxElems * 64 || a.seg <= 0 || a.rows_per_sample <= 0) return hipErrorInvalidValue;
+  const bool ok = (a.D % 512 == 0) ? launch_ln_any<8>(a, stream, std::make_integer_sequence<int, kMaxElems / 8>{})
+                                   : launch_ln_any<4>(a, stream, std::make_integer_sequence<int, kMaxElems / 4>{});
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
