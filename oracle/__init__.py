@@ -21,6 +21,9 @@ Parity status of each function (pins in tests/test_oracle_pins.py):
   forward                     skip == zeroed gate rows (bitwise), per-sample independence
   cfg_combine, euler_step,    pinned: CFG identities, telescoping under constant v, point-mass field
   sample_step                 lands exactly on x*, cfg = 1 runs no negative pass
+  text_refine                 pinned: projection vs a scalar brute force (blocks made identities by
+                              zero branch weights), permutation equivariance (no RoPE, no mask on
+                              text rows), equal rows stay equal
   negative_pass_runs          pinned: hand table of the truncation boundary (X * steps, steps from 0)
   guidance_combine            pinned: hand values of each term, v_s = v_c leaves the two-pass result,
                               linearity in slg_scale
@@ -32,6 +35,6 @@ Parity status of each function (pins in tests/test_oracle_pins.py):
 from .moss_oracle import *  # noqa: F401,F403
 from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, embed, euler_step,  # noqa
                           final_layer, forward, from_bf16_bits, guidance_combine, layernorm, ln_modulate,
-                          modulation, negative_pass_runs,
+                          modulation, negative_pass_runs, text_refine,
                           patchify, rope_angles, apply_rope, rope_rows, sample_step, sigmas, silu,
                           slg_active, time_features, unpatchify, weights_to_f64)

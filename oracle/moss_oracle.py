@@ -71,8 +71,9 @@ def silu(x):
 @dataclass(frozen=True)
 class Config:
     """[WP] "Architecture and specs": 42 joint blocks, hidden 3072, 24 heads of 128, FFN 8192,
-    32 latent channels, 2x2 latent patches. temb_dim, rope_theta, norm_eps and flow_multiplier are
-    readings (the pages do not give them)."""
+    32 latent channels, 2x2 latent patches, two text-only blocks after the text projection. temb_dim,
+    rope_theta, norm_eps, flow_multiplier and text_dim (the encoder's state width) are readings (the
+    pages do not give them)."""
     num_layers: int = 42
     hidden: int = 3072
     num_heads: int = 24
@@ -84,6 +85,8 @@ class Config:
     rope_theta: float = 1.0e4
     norm_eps: float = 1.0e-6
     flow_multiplier: float = 1000.0
+    text_dim: int = 4096
+    refiner_layers: int = 2
 
     @property
     def patch_dim(self) -> int:
@@ -308,6 +311,31 @@ def block(x: np.ndarray, m: np.ndarray, W: Dict, l: int, cfg: Config, text_len: 
 
 
 # ----------------------------------------------------------------------------------------------
+# text refiner (runs once per prompt, before the denoising loop)
+# ----------------------------------------------------------------------------------------------
+
+def text_refine(enc: np.ndarray, W: Dict, cfg: Config, mirror: bool = False) -> np.ndarray:
+    """The step before the DiT on the text side ([WP] "Architecture and specs": the encoder's
+    final-layer states go through a projection and two text-only blocks). enc [T, text_dim] -> [T, D].
+
+    Readings (the pages give no more): the projection is a linear map text_dim -> hidden without bias
+    (no linear mentions one); the text-only blocks are joint blocks of the same widths applied to the
+    text rows alone, without timestep modulation (LN(x) unmodulated, gates 1: they depend on the
+    prompt only and run once per prompt), and without RoPE (text rows are never rotated)."""
+    D = cfg.hidden
+    x = _store(_store(enc, mirror) @ W["text_proj_w"].T, mirror)
+    m = np.zeros((6, D))
+    m[2] = 1.0                                            # gate1
+    m[5] = 1.0                                            # gate2
+    Wr = {"qkv_w": W["refiner_qkv_w"], "out_w": W["refiner_out_w"], "gate_up_w": W["refiner_gate_up_w"],
+          "down_w": W["refiner_down_w"]}
+    T = x.shape[0]
+    for l in range(len(Wr["qkv_w"])):
+        x = block(x, m, Wr, l, cfg, T, 1, mirror=mirror)   # text_len = T: no row is rotated
+    return x
+
+
+# ----------------------------------------------------------------------------------------------
 # A3..A11  one DiT forward
 # ----------------------------------------------------------------------------------------------
 
@@ -433,9 +461,15 @@ def sample_step(x: np.ndarray, text_cond: np.ndarray, text_uncond: Optional[np.n
 
 
 def weights_to_f64(w) -> Dict:
-    """bf16 bit-pattern weights (an object with the C ABI's field names) -> float64 arrays."""
+    """bf16 bit-pattern weights (an object with the C ABI's field names) -> float64 arrays. The text
+    refiner's weights are converted when present."""
     get = (lambda k: w[k]) if isinstance(w, dict) else (lambda k: getattr(w, k))
+    has = (lambda k: k in w) if isinstance(w, dict) else (lambda k: getattr(w, k, None) is not None)
     out = {k: from_bf16_bits(get(k)) for k in ("t_w1", "t_w2", "x_embed_w", "final_mod_w", "final_w")}
     for k in ("mod_w", "qkv_w", "out_w", "gate_up_w", "down_w"):
         out[k] = [from_bf16_bits(a) for a in get(k)]
+    if has("text_proj_w"):
+        out["text_proj_w"] = from_bf16_bits(get("text_proj_w"))
+        for k in ("refiner_qkv_w", "refiner_out_w", "refiner_gate_up_w", "refiner_down_w"):
+            out[k] = [from_bf16_bits(a) for a in get(k)]
     return out

@@ -544,6 +544,85 @@ def test_three_pass_slg_and_truncation_paths():
     np.testing.assert_allclose((trs - x) / (sig[2] - sig[1]), 3.0 * v_c - 2.0 * v_s, atol=1e-10)
 
 
+def _refiner_weights(cfg, rng, text_dim, zero_branches=False):
+    D, F = cfg.hidden, cfg.ffn_hidden
+    L = 2
+    W = {"text_proj_w": rng.standard_normal((D, text_dim)) * 0.05,
+         "refiner_qkv_w": [rng.standard_normal((3 * D, D)) * 0.05 for _ in range(L)],
+         "refiner_out_w": [rng.standard_normal((D, D)) * 0.05 for _ in range(L)],
+         "refiner_gate_up_w": [rng.standard_normal((2 * F, D)) * 0.05 for _ in range(L)],
+         "refiner_down_w": [rng.standard_normal((D, F)) * 0.05 for _ in range(L)]}
+    if zero_branches:
+        W["refiner_out_w"] = [np.zeros((D, D)) for _ in range(L)]
+        W["refiner_down_w"] = [np.zeros((D, F)) for _ in range(L)]
+    return W
+
+
+def test_text_refine_projection_bruteforce():
+    # with zero output projections in both blocks every branch adds 0, so the refiner is the bare
+    # projection; checked against a scalar loop (no bias), with and without the bf16 storage points
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(31)
+    E = 48
+    W = _refiner_weights(cfg, rng, E, zero_branches=True)
+    enc = rng.standard_normal((5, E))
+    ref = np.zeros((5, cfg.hidden))
+    for t in range(5):
+        for o in range(cfg.hidden):
+            acc = 0.0
+            for i in range(E):
+                acc += enc[t, i] * W["text_proj_w"][o, i]
+            ref[t, o] = acc
+    np.testing.assert_allclose(O.text_refine(enc, W, cfg), ref, rtol=1e-12, atol=1e-12)
+    got = O.text_refine(enc, W, cfg, mirror=True)
+    np.testing.assert_array_equal(got, O.bf16_round(O.bf16_round(enc) @ W["text_proj_w"].T))
+
+
+def test_text_refine_permutation_equivariant():
+    # no positional rotation and no mask on text rows: permuting the prompt's rows permutes the output
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(32)
+    W = _refiner_weights(cfg, rng, 40)
+    enc = rng.standard_normal((7, 40))
+    perm = rng.permutation(7)
+    a = O.text_refine(enc, W, cfg)
+    b = O.text_refine(enc[perm], W, cfg)
+    np.testing.assert_allclose(b, a[perm], rtol=1e-10, atol=1e-12)
+    assert not np.allclose(a, O.text_refine(enc[:, ::-1].copy(), W, cfg))
+    # equal rows stay equal (each row attends to the same key set with the same scores)
+    enc2 = enc.copy()
+    enc2[3] = enc2[1]
+    c = O.text_refine(enc2, W, cfg)
+    np.testing.assert_allclose(c[3], c[1], rtol=1e-12, atol=1e-12)
+
+
+def test_text_refine_blocks_are_unmodulated_joint_blocks():
+    # one refiner block equals the generic joint block with shift = scale = 0 and gate = 1, and a
+    # block whose gate is 1 is not the identity (the branch outputs are added at full weight)
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(33)
+    W = _refiner_weights(cfg, rng, 32)
+    W1 = dict(W)
+    for k in ("refiner_qkv_w", "refiner_out_w", "refiner_gate_up_w", "refiner_down_w"):
+        W1[k] = W[k][:1]
+    enc = rng.standard_normal((6, 32))
+    x0 = enc @ W["text_proj_w"].T
+    # scalar brute force of LN without modulation on row 0
+    row = x0[0]
+    mu = sum(row) / len(row)
+    var = sum((v - mu) ** 2 for v in row) / len(row)
+    np.testing.assert_allclose(O.ln_modulate(x0, np.zeros(cfg.hidden), np.zeros(cfg.hidden), cfg.norm_eps)[0],
+                               (row - mu) / math.sqrt(var + cfg.norm_eps), rtol=1e-12)
+    taps = {}
+    m = np.zeros((6, cfg.hidden))
+    m[2] = m[5] = 1.0
+    Wb = {"qkv_w": W["refiner_qkv_w"], "out_w": W["refiner_out_w"], "gate_up_w": W["refiner_gate_up_w"],
+          "down_w": W["refiner_down_w"]}
+    x1 = O.block(x0, m, Wb, 0, cfg, 6, 1, taps=taps)
+    np.testing.assert_allclose(x1, x0 + taps["attn_out"] + taps["ffn_out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.text_refine(enc, W1, cfg), x1, rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------------------------------------
 # dimension pins (the SwiGLU / shape readings against the pages' printed sizes)
 # ------------------------------------------------------------------------------------------------
