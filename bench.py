@@ -139,6 +139,8 @@ def main():
                     help="steps timed for each guidance variant (three-pass SLG, CFG truncation; 0 = skip)")
     ap.add_argument("--steps-2048", type=int, default=2,
                     help="window steps timed at 2048^2 with 4096 text tokens, for its s/image (0 = skip)")
+    ap.add_argument("--refiner-reps", type=int, default=3,
+                    help="timed text-refiner calls per prompt length (256 and 4096 tokens; 0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="MiB of a plain device-to-device copy run once before the steps (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -178,6 +180,7 @@ def main():
     t0 = time.time()
     log(f"[bench] drawing random bf16 weights (42 blocks, hidden 3072, FFN 8192) on the GPU")
     weights = synth.torch_weights(synth.FULL, seed=0, device="cuda")
+    weights.update(synth.torch_refiner_weights(synth.FULL, seed=100, device="cuda"))
     cfg = dt.moss_dit_config_init()
     model = dt.MossDiT(cfg, weights)
     log(f"[bench] model created in {time.time() - t0:.1f} s")
@@ -321,6 +324,20 @@ def main():
         log(f"[bench] 2048^2: {json.dumps(big)}")
         del tc2, tu2, x2
 
+    # ---- text refiner (projection 4096 -> 3072 + two text-only blocks), once per prompt ----
+    refiner = None
+    if args.refiner_reps > 0:
+        refiner = {}
+        E = synth.FULL.text_dim
+        for Tr in (256, 4096):
+            enc = torch.randn((1, Tr, E), generator=g, device="cuda", dtype=torch.float32)
+            outr = torch.empty((1, Tr, D), device="cuda", dtype=torch.float32)
+            msr = timed(lambda k: model.moss_text_refine(enc, outr), args.refiner_reps)
+            fr = 2.0 * Tr * E * D + synth.FULL.refiner_layers * (block_linear_flops(Tr, D, F) + attention_flops(1, Tr, D))
+            refiner[f"prompt_{Tr}"] = {"ms": round(msr, 3), "tflops": round(fr / (msr * 1e-3) / 1e12, 1)}
+            del enc, outr
+        log(f"[bench] text refiner: {json.dumps(refiner)}")
+
     cpu = None
     if args.cpu_baseline_blocks > 0:
         log(f"[bench] cpu_baseline: oracle on {args.cpu_baseline_blocks} block(s) of one sample")
@@ -343,6 +360,7 @@ def main():
         "kernels": kernels,
         "guidance_variants": variants,
         "sampling_2048": big,
+        "text_refiner": refiner,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -41,14 +41,16 @@ class moss_dit_config(C.Structure):
                 ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_hidden", C.c_int32),
                 ("latent_channels", C.c_int32), ("patch", C.c_int32), ("temb_dim", C.c_int32),
                 ("qk_norm", C.c_int32), ("rope_theta", C.c_float), ("norm_eps", C.c_float),
-                ("flow_multiplier", C.c_float)]
+                ("flow_multiplier", C.c_float), ("text_dim", C.c_int32), ("refiner_layers", C.c_int32)]
 
 
 class moss_dit_weights(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("t_w1", C.c_void_p), ("t_w2", C.c_void_p), ("x_embed_w", C.c_void_p),
                 ("mod_w", C.POINTER(C.c_void_p)), ("qkv_w", C.POINTER(C.c_void_p)), ("out_w", C.POINTER(C.c_void_p)),
                 ("gate_up_w", C.POINTER(C.c_void_p)), ("down_w", C.POINTER(C.c_void_p)),
-                ("final_mod_w", C.c_void_p), ("final_w", C.c_void_p)]
+                ("final_mod_w", C.c_void_p), ("final_w", C.c_void_p), ("text_proj_w", C.c_void_p),
+                ("refiner_qkv_w", C.POINTER(C.c_void_p)), ("refiner_out_w", C.POINTER(C.c_void_p)),
+                ("refiner_gate_up_w", C.POINTER(C.c_void_p)), ("refiner_down_w", C.POINTER(C.c_void_p))]
 
 
 class moss_forward_args(C.Structure):
@@ -100,6 +102,7 @@ _sig("moss_guidance_euler", C.c_int, _P, _P, _P, _P, C.c_int64, C.c_float, C.c_f
 _sig("moss_dit_modulation", C.c_int, _P, C.POINTER(C.c_float), C.c_int32, _P, _P)
 _sig("moss_dit_block", C.c_int, _P, C.c_int32, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64,
      C.POINTER(moss_block_taps), _P)
+_sig("moss_text_refine", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, _P)
 _sig("moss_attention", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_gemm_bf16", C.c_int, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_dit_profile_enable", C.c_int, _P, C.c_int32)
@@ -113,7 +116,7 @@ EXPORTED = ["moss_dit_abi_version", "moss_status_string", "moss_dit_last_error",
             "moss_dit_weights_init", "moss_dit_create", "moss_dit_destroy", "moss_forward_args_init",
             "moss_dit_forward", "moss_validate_forward_args", "moss_sigmas", "moss_step_args_init",
             "moss_sample_step", "moss_validate_step_args", "moss_cfg_euler", "moss_guidance_euler",
-            "moss_dit_modulation",
+            "moss_text_refine", "moss_dit_modulation",
             "moss_block_taps_init", "moss_dit_block", "moss_attention", "moss_gemm_bf16",
             "moss_dit_profile_enable", "moss_dit_profile_read"]
 
@@ -265,9 +268,13 @@ class MossDiT:
         for k in ("t_w1", "t_w2", "x_embed_w", "final_mod_w", "final_w"):
             setattr(w, k, p(weights[k]))
         arrays = {}
-        for k in ("mod_w", "qkv_w", "out_w", "gate_up_w", "down_w"):
+        per_block = ["mod_w", "qkv_w", "out_w", "gate_up_w", "down_w"]
+        if weights.get("text_proj_w") is not None:           # optional text refiner
+            w.text_proj_w = p(weights["text_proj_w"])
+            per_block += ["refiner_qkv_w", "refiner_out_w", "refiner_gate_up_w", "refiner_down_w"]
+        for k in per_block:
             lst = weights[k]
-            arr = (C.c_void_p * len(lst))(*[p(t) for t in lst])
+            arr = (C.c_void_p * max(1, len(lst)))(*[p(t) for t in lst])
             arrays[k] = arr
             setattr(w, k, C.cast(arr, C.POINTER(C.c_void_p)))
         self.cfg = cfg
@@ -344,6 +351,16 @@ class MossDiT:
         a.n_skip = len(uncond_skip_layers)
         a.slg_scale, a.cfg_truncation = slg_scale, cfg_truncation
         _check(_lib.moss_sample_step(self.handle, C.byref(a), _stream(stream)), self.handle)
+
+    def moss_text_refine(self, enc, out, stream=None):
+        """enc: fp32 [batch, text_len, text_dim] on the GPU -> out: fp32 [batch, text_len, hidden]."""
+        import torch
+        _check_dev(enc, torch.float32, "enc")
+        _check_dev(out, torch.float32, "out")
+        B, T, E = enc.shape
+        if E != self.cfg.text_dim or tuple(out.shape) != (B, T, self.cfg.hidden):
+            raise ValueError("enc must be [B, T, text_dim] and out [B, T, hidden]")
+        _check(_lib.moss_text_refine(self.handle, B, T, _ptr(enc), _ptr(out), _stream(stream)), self.handle)
 
     def moss_dit_modulation(self, sigma: Sequence[float], mod, stream=None):
         import torch

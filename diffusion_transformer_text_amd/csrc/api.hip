@@ -108,6 +108,11 @@ struct moss_dit {
   uint16_t* wbuf = nullptr;
   uint16_t *t_w1 = nullptr, *t_w2 = nullptr, *x_embed = nullptr, *mod_all = nullptr, *final_w = nullptr;
   std::vector<uint16_t*> qkv, out, gu, down;
+  // text refiner (empty when created without its weights); const_mod = one unmodulated block's
+  // (shift1, scale1, gate1, shift2, scale2, gate2) = (0, 0, 1, 0, 0, 1), bf16 [6 * hidden]
+  uint16_t* text_proj = nullptr;
+  std::vector<uint16_t*> rqkv, rout, rgu, rdown;
+  uint16_t* const_mod = nullptr;
   float* rope = nullptr;   // [2][256][32]
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -190,6 +195,12 @@ int check_config(const moss_dit_config* c, std::string& msg) {
       c->num_layers > 64 || c->qk_norm != 0 || c->latent_channels * 4 % 128 != 0) {
     msg = fmt("unsupported configuration (need head_dim 128, hidden = heads*128, hidden %% 256 == 0 and <= 4096, "
               "ffn %% 64 == 0, temb 256, patch 2, channels*4 %% 128 == 0, <= 64 layers, no qk_norm)");
+    return MOSS_ERR_NOT_SUPPORTED;
+  }
+  if (c->text_dim < 64 || c->text_dim > 16384 || c->text_dim % 64 != 0 || c->refiner_layers < 0 ||
+      c->refiner_layers > 8) {
+    msg = fmt("unsupported text refiner configuration (need text_dim %% 64 == 0 in [64, 16384], 0..8 refiner layers; "
+              "got %d, %d)", c->text_dim, c->refiner_layers);
     return MOSS_ERR_NOT_SUPPORTED;
   }
   return MOSS_OK;
@@ -405,11 +416,19 @@ LnModArgs ln_args(const uint16_t* x, uint16_t* out, int rows, int D, int rows_pe
 }
 
 // One joint block on nb consecutive samples of a residual stream x [nb*S, D].
-int run_block(moss_dit* H, int l, uint16_t* x, int nb, int T, int gw, int S, const uint16_t* mod, long mod_stride,
-              const Carve& c, const moss_block_taps* taps, hipStream_t st) {
+// The weights of one joint block (a DiT block or a text-refiner block).
+struct BlockW {
+  const uint16_t *qkv, *out, *gu, *down;
+};
+
+BlockW dit_block(const moss_dit* H, int l) { return {H->qkv[l], H->out[l], H->gu[l], H->down[l]}; }
+
+// One joint block on nb samples of S rows each (x [nb * S, D], in place). m: the block's six modulation
+// vectors of the first sample ([6 * D]); sample b's are at m + b * mod_stride (stride 0: all share).
+int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, int S, const uint16_t* m,
+              long mod_stride, const Carve& c, const moss_block_taps* taps, hipStream_t st) {
   const moss_dit_config& k = H->cfg;
   const int D = k.hidden, F = k.ffn_hidden, M = nb * S;
-  const uint16_t* m = mod + (long)l * 6 * D;
   auto tap_copy = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
     if (!taps || !dst) return hipSuccess;
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
@@ -421,7 +440,7 @@ int run_block(moss_dit* H, int l, uint16_t* x, int nb, int T, int gw, int S, con
   }
   HIP_TRY(H, tap_copy(taps ? taps->a : nullptr, c.a, (size_t)M * D * 2));
   // A5: QKV projection, RoPE on image rows of q and k
-  GemmArgs g = gemm_args(c.a, H->qkv[l], M, 3 * D, D, c.qkv, 3 * D);
+  GemmArgs g = gemm_args(c.a, w.qkv, M, 3 * D, D, c.qkv, 3 * D);
   g.rope_cos = H->rope;
   g.rope_sin = H->rope + kRopeMaxPos * (kHeadDim / 4);
   g.S = S;
@@ -449,8 +468,8 @@ int run_block(moss_dit* H, int l, uint16_t* x, int nb, int T, int gw, int S, con
   }
   HIP_TRY(H, tap_copy(taps ? taps->o : nullptr, c.o, (size_t)M * D * 2));
   // A7: out projection + gated residual
-  if (taps && taps->attn) HIP_TRY(H, launch_gemm(gemm_args(c.o, H->out[l], M, D, D, taps->attn, D), EPI_F32, st));
-  g = gemm_args(c.o, H->out[l], M, D, D, x, D);
+  if (taps && taps->attn) HIP_TRY(H, launch_gemm(gemm_args(c.o, w.out, M, D, D, taps->attn, D), EPI_F32, st));
+  g = gemm_args(c.o, w.out, M, D, D, x, D);
   g.gate = m + 2 * D;
   g.rows_per_sample = S;
   g.gate_stride = mod_stride;
@@ -468,12 +487,12 @@ int run_block(moss_dit* H, int l, uint16_t* x, int nb, int T, int gw, int S, con
   // A9: gate/up projection + SiLU * mul
   {
     ProfScope ps(H, PC_GATE_UP, st);
-    HIP_TRY(H, launch_gemm(gemm_args(c.a, H->gu[l], M, 2 * F, D, c.h, F), EPI_SWIGLU, st));
+    HIP_TRY(H, launch_gemm(gemm_args(c.a, w.gu, M, 2 * F, D, c.h, F), EPI_SWIGLU, st));
   }
   HIP_TRY(H, tap_copy(taps ? taps->h : nullptr, c.h, (size_t)M * F * 2));
   // A10: down projection + gated residual
-  if (taps && taps->ffn) HIP_TRY(H, launch_gemm(gemm_args(c.h, H->down[l], M, D, F, taps->ffn, D), EPI_F32, st));
-  g = gemm_args(c.h, H->down[l], M, D, F, x, D);
+  if (taps && taps->ffn) HIP_TRY(H, launch_gemm(gemm_args(c.h, w.down, M, D, F, taps->ffn, D), EPI_F32, st));
+  g = gemm_args(c.h, w.down, M, D, F, x, D);
   g.gate = m + 5 * D;
   g.rows_per_sample = S;
   g.gate_stride = mod_stride;
@@ -534,7 +553,8 @@ int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st) {
       }
       int e = b;
       while (e < B && !((p.skip[e] >> l) & 1ULL)) ++e;
-      if ((s = run_block(H, l, c.x + (size_t)b * S * D, e - b, p.T, gw, S, c.mod + (size_t)b * mstride, mstride, c,
+      if ((s = run_block(H, dit_block(H, l), c.x + (size_t)b * S * D, e - b, p.T, gw, S,
+                         c.mod + (size_t)b * mstride + (size_t)l * 6 * D, mstride, c,
                          nullptr, st)))
         return s;
       b = e;
@@ -613,6 +633,8 @@ void moss_dit_config_init(moss_dit_config* c, uint32_t size) {
   d.rope_theta = 1.0e4f;
   d.norm_eps = 1.0e-6f;
   d.flow_multiplier = 1000.f;
+  d.text_dim = 4096;
+  d.refiner_layers = 2;
   memcpy(c, &d, size < sizeof d ? size : sizeof d);
 }
 
@@ -711,10 +733,20 @@ int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int w
     if (!w->mod_w[l] || !w->qkv_w[l] || !w->out_w[l] || !w->gate_up_w[l] || !w->down_w[l])
       return fail(nullptr, MOSS_ERR_INVALID_ARGUMENT, fmt("a weight pointer of block %d is NULL", l));
 
+  const bool refiner = w->text_proj_w != nullptr;
+  const int RL = refiner ? cfg->refiner_layers : 0;
+  if (refiner && RL > 0 && (!w->refiner_qkv_w || !w->refiner_out_w || !w->refiner_gate_up_w || !w->refiner_down_w))
+    return fail(nullptr, MOSS_ERR_INVALID_ARGUMENT, "text_proj_w is set but a refiner weight array is NULL");
+  for (int l = 0; l < RL; ++l)
+    if (!w->refiner_qkv_w[l] || !w->refiner_out_w[l] || !w->refiner_gate_up_w[l] || !w->refiner_down_w[l])
+      return fail(nullptr, MOSS_ERR_INVALID_ARGUMENT, fmt("a weight pointer of refiner block %d is NULL", l));
+
   moss_dit* H = new moss_dit();
   H->cfg = *cfg;
   hipStream_t st = (hipStream_t)stream;
+  uint16_t* stage = nullptr;   // staging for host gate/up weights (interleaved on the device)
   auto bail = [&](int status, const std::string& m) {
+    if (stage) hipFree(stage);
     if (H->wbuf) hipFree(H->wbuf);
     delete H;
     return fail(nullptr, status, m);
@@ -724,7 +756,8 @@ int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int w
   const size_t D = cfg->hidden, F = cfg->ffn_hidden, E = cfg->temb_dim, P = (size_t)cfg->latent_channels * 4;
   const size_t n_t1 = E * kSinusoidDim, n_t2 = E * E, n_xe = D * P, n_mod = (size_t)H->mod_rows() * E, n_fin = P * D;
   const size_t n_layer = 3 * D * D + D * D + 2 * F * D + D * F;
-  const size_t total = n_t1 + n_t2 + n_xe + n_mod + n_fin + (size_t)L * n_layer;
+  const size_t n_proj = refiner ? D * (size_t)cfg->text_dim : 0, n_cmod = refiner ? 6 * D : 0;
+  const size_t total = n_t1 + n_t2 + n_xe + n_mod + n_fin + (size_t)L * n_layer + n_proj + n_cmod + (size_t)RL * n_layer;
   void* p = nullptr;
   hipError_t e = dev_alloc(&p, total * 2);
   if (e != hipSuccess) {
@@ -749,6 +782,16 @@ int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int w
     H->gu.push_back(next(2 * F * D));
     H->down.push_back(next(D * F));
   }
+  if (refiner) {
+    H->text_proj = next(n_proj);
+    H->const_mod = next(n_cmod);
+    for (int l = 0; l < RL; ++l) {
+      H->rqkv.push_back(next(3 * D * D));
+      H->rout.push_back(next(D * D));
+      H->rgu.push_back(next(2 * F * D));
+      H->rdown.push_back(next(D * F));
+    }
+  }
   const hipMemcpyKind kind = weights_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
   auto cp = [&](void* dst, const void* src, size_t n) { return hipMemcpyAsync(dst, src, n * 2, kind, st); };
 #define CREATE_TRY(expr)                                                                   \
@@ -764,7 +807,6 @@ int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int w
   CREATE_TRY(cp(H->final_w, w->final_w, n_fin));
   // gate/up rows are interleaved in 32-row groups for the SwiGLU epilogue; host weights go through
   // a staging buffer (the workspace allocation, freed below).
-  uint16_t* stage = nullptr;
   if (!weights_on_device) {
     void* sp = nullptr;
     if (dev_alloc(&sp, 2 * F * D * 2) != hipSuccess) {
@@ -784,6 +826,26 @@ int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int w
     }
     CREATE_TRY(launch_interleave_gate_up(src, H->gu[l], (int)F, (int)D, st));
     if (stage) CREATE_TRY(hipStreamSynchronize(st));   // the staging buffer is reused next layer
+  }
+  std::vector<uint16_t> cmod;
+  if (refiner) {
+    CREATE_TRY(cp(H->text_proj, w->text_proj_w, n_proj));
+    for (int l = 0; l < RL; ++l) {
+      CREATE_TRY(cp(H->rqkv[l], w->refiner_qkv_w[l], 3 * D * D));
+      CREATE_TRY(cp(H->rout[l], w->refiner_out_w[l], D * D));
+      CREATE_TRY(cp(H->rdown[l], w->refiner_down_w[l], D * F));
+      const uint16_t* src = (const uint16_t*)w->refiner_gate_up_w[l];
+      if (stage) {
+        CREATE_TRY(cp(stage, src, 2 * F * D));
+        src = stage;
+      }
+      CREATE_TRY(launch_interleave_gate_up(src, H->rgu[l], (int)F, (int)D, st));
+      if (stage) CREATE_TRY(hipStreamSynchronize(st));
+    }
+    // unmodulated block: shift = scale = 0, gate = 1 (bf16 0x3f80)
+    cmod.assign(6 * D, 0);
+    for (size_t i = 0; i < D; ++i) cmod[2 * D + i] = cmod[5 * D + i] = 0x3f80;
+    CREATE_TRY(hipMemcpyAsync(H->const_mod, cmod.data(), n_cmod * 2, hipMemcpyHostToDevice, st));
   }
   CREATE_TRY(hipStreamSynchronize(st));
   if (stage) hipFree(stage);
@@ -885,6 +947,47 @@ int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream) {
   return MOSS_OK;
 }
 
+int moss_text_refine(moss_dit* h, int32_t batch, int32_t text_len, const float* enc, float* out, void* stream) {
+  int s = enter(h);
+  if (s) return s;
+  if (!h->text_proj) return fail(h, MOSS_ERR_NOT_SUPPORTED, "the handle was created without text refiner weights");
+  std::string msg;
+  if (batch < 1 || batch > kMaxBatch) return fail(h, MOSS_ERR_INVALID_ARGUMENT, fmt("batch %d out of range [1, %d]", batch, kMaxBatch));
+  if ((s = check_text_len(text_len, msg))) return fail(h, s, msg);
+  if (!enc || !out) return fail(h, MOSS_ERR_INVALID_ARGUMENT, "enc and out must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(enc) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(h, MOSS_ERR_INVALID_ARGUMENT, "enc and out must be 16-byte aligned");
+  const moss_dit_config& k = h->cfg;
+  const int D = k.hidden, E = k.text_dim, T = text_len, M = batch * text_len;
+  hipStream_t st = (hipStream_t)stream;
+  // workspace: the block buffers for [batch, T] rows, then the bf16 copy of the encoder states
+  const size_t base = carve(h, batch, T, 0, 0, nullptr, nullptr);
+  const size_t enc_bytes = (size_t)M * E * 2;
+  if ((s = ensure_ws(h, base + enc_bytes))) return s;
+  Carve c;
+  carve(h, batch, T, 0, 0, (char*)h->ws, &c);
+  uint16_t* encb = (uint16_t*)((char*)h->ws + base);
+  {
+    ProfScope ps(h, PC_EMBED, st);
+    PtrBatch pb;
+    for (int b = 0; b < batch; ++b) pb.p[b] = enc + (size_t)b * T * E;
+    HIP_TRY(h, launch_text_cast(pb, batch, T, E, T, encb, st));
+    GemmArgs g = gemm_args(encb, h->text_proj, M, D, E, c.x, D);
+    g.seg = M;   // no row remap
+    g.seg_stride = 0;
+    g.seg_off = 0;
+    HIP_TRY(h, launch_gemm(g, EPI_BF16, st));
+  }
+  for (int l = 0; l < k.refiner_layers; ++l) {
+    // text rows only (T = S: no RoPE), one shared unmodulated modulation vector (stride 0)
+    if ((s = run_block(h, {h->rqkv[l], h->rout[l], h->rgu[l], h->rdown[l]}, c.x, batch, T, 1, T, h->const_mod, 0, c,
+                       nullptr, st)))
+      return s;
+  }
+  HIP_TRY(h, launch_bf16_to_f32(c.x, out, (long)M * D, st));
+  return MOSS_OK;
+}
+
 int moss_cfg_euler(const float* v_cond, const float* v_uncond, float* x, int64_t n, float cfg, float sigma,
                    float sigma_next, void* stream) {
   if (!v_cond || !x || n < 0 || !std::isfinite(cfg) || cfg < 1.f || (!v_uncond && cfg != 1.f)) {
@@ -951,7 +1054,8 @@ int moss_dit_block(moss_dit* h, int32_t layer, void* x, int32_t batch, int32_t t
   if ((s = ensure_ws(h, carve(h, batch, S, N, 4, nullptr, nullptr)))) return s;
   Carve c;
   carve(h, batch, S, N, 4, (char*)h->ws, &c);
-  return run_block(h, layer, (uint16_t*)x, batch, text_len, grid_w, S, (const uint16_t*)mod, (long)mod_stride, c, taps,
+  return run_block(h, dit_block(h, layer), (uint16_t*)x, batch, text_len, grid_w, S,
+                   (const uint16_t*)mod + (size_t)layer * 6 * h->cfg.hidden, (long)mod_stride, c, taps,
                    (hipStream_t)stream);
 }
 

@@ -106,6 +106,8 @@ hipError_t launch_text_cast(PtrBatch text, int B, int T, int D, int S, uint16_t*
 // x = x + (sigma_next - sigma) * (v_u + cfg * (v_c - v_u)); v_u == nullptr means v = v_c.
 hipError_t launch_cfg_euler(const float* v_c, const float* v_u, float* x, long n, float cfg, float sigma,
                             float sigma_next, hipStream_t stream);
+// dst = float(src) for n bf16 values (src 8-byte, dst 16-byte aligned).
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, long n, hipStream_t stream);
 // As above plus slg * (v_c - v_s) when v_s != nullptr (the skipped conditional prediction).
 hipError_t launch_guidance_euler(const float* v_c, const float* v_u, const float* v_s, float* x, long n, float cfg,
                                  float slg, float sigma, float sigma_next, hipStream_t stream);

@@ -146,6 +146,17 @@ __global__ void guidance_euler_kernel(const float* __restrict__ vc, const float*
   }
 }
 
+// fp32 copy of a bf16 tensor (exact), 4 elements per lane.
+__global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, float* __restrict__ dst, long n) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += stride) {
+    const uint2 u = reinterpret_cast<const uint2*>(src)[i];
+    reinterpret_cast<float4*>(dst)[i] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                                                    __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+  for (long i = (n / 4) * 4 + (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = bf16_to_f32(src[i]);
+}
+
 }  // namespace
 
 hipError_t launch_time_mlp(SigmaBatch sigma, int B, const uint16_t* t_w1, const uint16_t* t_w2,
@@ -201,6 +212,16 @@ hipError_t launch_guidance_euler(const float* v_c, const float* v_u, const float
 hipError_t launch_cfg_euler(const float* v_c, const float* v_u, float* x, long n, float cfg, float sigma,
                             float sigma_next, hipStream_t stream) {
   return launch_guidance_euler(v_c, v_u, nullptr, x, n, cfg, 0.f, sigma, sigma_next, stream);
+}
+
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, long n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if ((reinterpret_cast<uintptr_t>(src) & 7) || (reinterpret_cast<uintptr_t>(dst) & 15)) return hipErrorInvalidValue;
+  long grid = (n / 4 + 255) / 256;
+  if (grid < 1) grid = 1;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
 }
 
 }  // namespace moss

@@ -60,14 +60,19 @@ const char* moss_dit_last_error(const moss_dit* h);
  * Model configuration. Defaults (moss_dit_config_init) are MOSS-Image's: 42 layers, hidden 3072,
  * 24 heads of 128, FFN 8192, 32 latent channels, 2x2 patches ("Architecture and specs"), and the
  * readings where the pages are silent: time-embedding width 256, RoPE theta 1e4, LayerNorm eps 1e-6,
- * flow multiplier 1000 (t = 1000 * sigma), no QK-norm.
+ * flow multiplier 1000 (t = 1000 * sigma), no QK-norm; for the text refiner (the text encoder's
+ * final-layer states go through a projection and two text-only blocks, "Architecture and specs"):
+ * encoder state width 4096 and 2 refiner blocks.
  * Supported: head_dim == 128, hidden == num_heads * 128, hidden % 256 == 0, hidden <= 4096,
- * ffn_hidden % 64 == 0, temb_dim == 256, patch == 2, 1 <= num_layers <= 64, qk_norm == 0;
+ * ffn_hidden % 64 == 0, temb_dim == 256, patch == 2, 1 <= num_layers <= 64, qk_norm == 0,
+ * text_dim % 64 == 0 and 64 <= text_dim <= 16384, 0 <= refiner_layers <= 8;
  * anything else -> MOSS_ERR_NOT_SUPPORTED. */
 typedef struct {
   uint32_t struct_size;
   int32_t num_layers, hidden, num_heads, head_dim, ffn_hidden, latent_channels, patch, temb_dim, qk_norm;
   float rope_theta, norm_eps, flow_multiplier;
+  int32_t text_dim;                /* width of the text encoder's states (input of the text refiner)   */
+  int32_t refiner_layers;          /* text-only blocks after the text projection                       */
 } moss_dit_config;
 void moss_dit_config_init(moss_dit_config* c, uint32_t size);
 
@@ -87,6 +92,13 @@ typedef struct {
   const void* const* down_w;       /* L x [hidden, ffn]                                                */
   const void* final_mod_w;         /* [2*hidden, temb]: (shift_f, scale_f)                              */
   const void* final_w;             /* [C*p*p, hidden] output projection                                */
+  /* Text refiner (optional: text_proj_w == NULL leaves it out and moss_text_refine returns
+   * MOSS_ERR_NOT_SUPPORTED). The refiner blocks have the joint blocks' layout and widths. */
+  const void* text_proj_w;                 /* [hidden, text_dim]                                      */
+  const void* const* refiner_qkv_w;        /* refiner_layers x [3*hidden, hidden]                     */
+  const void* const* refiner_out_w;        /* refiner_layers x [hidden, hidden]                       */
+  const void* const* refiner_gate_up_w;    /* refiner_layers x [2*ffn, hidden]: rows [gate | up]      */
+  const void* const* refiner_down_w;       /* refiner_layers x [hidden, ffn]                          */
 } moss_dit_weights;
 void moss_dit_weights_init(moss_dit_weights* w, uint32_t size);
 
@@ -119,6 +131,19 @@ void moss_forward_args_init(moss_forward_args* a, uint32_t size);
 int moss_dit_forward(moss_dit* h, const moss_forward_args* a, void* stream);
 /* Host-only check of forward arguments (no GPU needed). msg (may be NULL) receives the reason. */
 int moss_validate_forward_args(const moss_dit_config* cfg, const moss_forward_args* a, char* msg, int32_t msg_len);
+
+/* ---------------------------------------------------------------------------------------------
+ * Text refiner: out = refine(enc), run once per prompt before the denoising loop; `out` is what
+ * moss_dit_forward / moss_sample_step take as text states. The text encoder's final-layer states go
+ * through a projection and two text-only blocks ("MOSS-Image: specs, settings, VRAM and text rendering
+ * tested", "Architecture and specs"). Readings (the pages say no more): the projection has no bias;
+ * the text-only blocks are joint blocks of the same widths run on the text rows alone, without
+ * timestep modulation (unmodulated LayerNorm, gates 1: they depend on the prompt only) and without
+ * RoPE. bf16 storage as in the DiT; the result is written as fp32 (exact bf16 values).
+ *   enc: device fp32 [batch, text_len, text_dim], 16-byte aligned; out: device fp32
+ *   [batch, text_len, hidden]. 1 <= batch <= 8, 1 <= text_len <= 4096. Samples are independent.
+ * Returns MOSS_ERR_NOT_SUPPORTED when the handle was created without refiner weights. */
+int moss_text_refine(moss_dit* h, int32_t batch, int32_t text_len, const float* enc, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Sigma schedule: sigmas[i] = shift*s/(1 + (shift-1)*s), s = (num_steps - i)/num_steps, i = 0..num_steps

@@ -35,6 +35,8 @@ class Shape:
     latent_channels: int = 32
     patch: int = 2
     temb_dim: int = 256
+    text_dim: int = 4096          # width of the text encoder's states (input of the text refiner)
+    refiner_layers: int = 2
 
     @property
     def patch_dim(self) -> int:
@@ -44,7 +46,7 @@ class Shape:
 FULL = Shape()
 # Tiny single-stream DiT: 2 blocks, hidden 256, 2 heads x 128, FFN 704 (the 8/3 rule rounded up to a
 # multiple of 64), 32 latent channels, 2x2 patches.
-TINY = Shape(num_layers=2, hidden=256, num_heads=2, head_dim=128, ffn_hidden=704)
+TINY = Shape(num_layers=2, hidden=256, num_heads=2, head_dim=128, ffn_hidden=704, text_dim=320)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -162,4 +164,40 @@ def torch_weights(shape: Shape, seed: int, device, std: float = 0.02, mod_scale:
         out["down_w"].append(draw(D, F, std))
     out["final_mod_w"] = draw(2 * D, E, std * mod_scale)
     out["final_w"] = draw(shape.patch_dim, D, std)
+    return out
+
+
+# Text refiner weights (projection text_dim -> hidden and the refiner blocks), drawn from their own
+# seeded stream so the DiT's weights and inputs above stay as they are: bf16 bit patterns (numpy) for
+# the small shapes, bf16 tensors on the device (torch's generator) for the full size. Encoder states
+# are N(0, 1) fp32 [B, T, text_dim].
+def refiner_weights(shape: Shape, seed: int = 100, std: float = 0.02) -> Dict[str, object]:
+    rng = np.random.default_rng(seed)
+    D, F = shape.hidden, shape.ffn_hidden
+    out: Dict[str, object] = {"text_proj_w": _bf16_normal(rng, (D, shape.text_dim), std),
+                              "refiner_qkv_w": [], "refiner_out_w": [], "refiner_gate_up_w": [], "refiner_down_w": []}
+    for _ in range(shape.refiner_layers):
+        out["refiner_qkv_w"].append(_bf16_normal(rng, (3 * D, D), std))
+        out["refiner_out_w"].append(_bf16_normal(rng, (D, D), std))
+        out["refiner_gate_up_w"].append(_bf16_normal(rng, (2 * F, D), std))
+        out["refiner_down_w"].append(_bf16_normal(rng, (D, F), std))
+    return out
+
+
+def torch_refiner_weights(shape: Shape, seed: int, device, std: float = 0.02) -> Dict[str, object]:
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    D, F = shape.hidden, shape.ffn_hidden
+
+    def draw(rows, cols):
+        return (torch.randn((rows, cols), generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    out: Dict[str, object] = {"text_proj_w": draw(D, shape.text_dim), "refiner_qkv_w": [], "refiner_out_w": [],
+                              "refiner_gate_up_w": [], "refiner_down_w": []}
+    for _ in range(shape.refiner_layers):
+        out["refiner_qkv_w"].append(draw(3 * D, D))
+        out["refiner_out_w"].append(draw(D, D))
+        out["refiner_gate_up_w"].append(draw(2 * F, D))
+        out["refiner_down_w"].append(draw(D, F))
     return out

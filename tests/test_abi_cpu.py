@@ -68,6 +68,8 @@ def test_config_defaults_are_the_pages():
     o = O.Config()
     assert (c.temb_dim, c.rope_theta, c.norm_eps, c.flow_multiplier) == (o.temb_dim, o.rope_theta,
                                                                           np.float32(o.norm_eps), o.flow_multiplier)
+    # the refiner: two text-only blocks ("Architecture and specs"); the state width is a reading
+    assert c.refiner_layers == a["refiner_blocks"] == o.refiner_layers and c.text_dim == o.text_dim
 
 
 def test_step_defaults_are_the_pages():
@@ -167,7 +169,8 @@ def test_validate_step_null_pointers_and_cfg1():
 
 
 def test_validate_unsupported_config():
-    for kw in ({"head_dim": 64}, {"hidden": 3000}, {"ffn_hidden": 8200}, {"qk_norm": 1}, {"num_layers": 65}):
+    for kw in ({"head_dim": 64}, {"hidden": 3000}, {"ffn_hidden": 8200}, {"qk_norm": 1}, {"num_layers": 65},
+               {"text_dim": 100}, {"text_dim": 32}, {"refiner_layers": 9}):
         cfg = dt.moss_dit_config_init(**kw)
         a, keep = _valid_step(cfg)
         st, msg = dt.moss_validate_step_args(cfg, a)
