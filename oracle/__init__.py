@@ -24,6 +24,10 @@ Parity status of each function (pins in tests/test_oracle_pins.py):
   text_refine                 pinned: projection vs a scalar brute force (blocks made identities by
                               zero branch weights), permutation equivariance (no RoPE, no mask on
                               text rows), equal rows stay equal
+  first_block_change,         pinned: hand values of the change measure; threshold 0 gives the plain
+  forward_cached,             forward/step bit for bit; with blocks 1.. made identities (zero gates)
+  sample_step_cached          a reused call equals the full call bit for bit; step 0 and a new row
+                              plan restart the cache
   negative_pass_runs          pinned: hand table of the truncation boundary (X * steps, steps from 0)
   guidance_combine            pinned: hand values of each term, v_s = v_c leaves the two-pass result,
                               linearity in slg_scale
@@ -35,6 +39,7 @@ Parity status of each function (pins in tests/test_oracle_pins.py):
 from .moss_oracle import *  # noqa: F401,F403
 from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, embed, euler_step,  # noqa
                           final_layer, forward, from_bf16_bits, guidance_combine, layernorm, ln_modulate,
-                          modulation, negative_pass_runs, text_refine,
+                          modulation, negative_pass_runs, text_refine, StepCache,
+                          first_block_change, forward_cached, sample_step_cached,
                           patchify, rope_angles, apply_rope, rope_rows, sample_step, sigmas, silu,
                           slg_active, time_features, unpatchify, weights_to_f64)

@@ -623,6 +623,67 @@ def test_text_refine_blocks_are_unmodulated_joint_blocks():
     np.testing.assert_allclose(O.text_refine(enc, W1, cfg), x1, rtol=1e-12, atol=1e-12)
 
 
+def test_first_block_change_hand_values():
+    r_prev = np.array([[1.0, -2.0], [0.5, 0.5]])
+    r = np.array([[1.5, -2.0], [0.5, 0.0]])
+    assert O.first_block_change(r, r_prev) == (0.5 + 0.5) / 4.0
+    assert O.first_block_change(r_prev, r_prev) == 0.0
+
+
+def _cache_run(W, cfg, x, tc, tu, sig, threshold, skip=()):
+    cache = O.StepCache()
+    xs, xu = [], []
+    xa, xb = x.copy(), x.copy()
+    for i in range(len(sig) - 1):
+        xa = O.sample_step_cached(xa, tc, tu, W, cfg, i, sig, cache, threshold, 3.0, skip)
+        xb = O.sample_step(xb, tc, tu, W, cfg, i, sig, 3.0, skip)
+        xs.append(xa.copy()), xu.append(xb.copy())
+    return cache, xs, xu
+
+
+def test_step_cache_threshold_zero_is_the_plain_step():
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(41)
+    W = _tiny_weights(cfg, rng)
+    x = rng.standard_normal((1, 32, 4, 4))
+    tc, tu = rng.standard_normal((1, 3, cfg.hidden)), np.zeros((1, 3, cfg.hidden))
+    sig = O.sigmas(3, 5.0)
+    cache, xs, xu = _cache_run(W, cfg, x, tc, tu, sig, 0.0)
+    for a, b in zip(xs, xu):
+        np.testing.assert_array_equal(a, b)
+    assert (cache.full_calls, cache.reused_calls) == (3, 0)
+    assert np.isfinite(cache.last_change) and cache.last_change > 0
+
+
+def test_step_cache_reuse_composes_block0_and_the_cached_rest():
+    # with the gates of every block after block 0 zeroed, blocks 1.. are identities: the cached rest
+    # is 0 and a reused call must give the full call's result bit for bit; with a huge threshold every
+    # call after the first reuses, except where the row plan changes (the negative pass starts skipping
+    # block 1 at step 1 of 3, which restarts the cache)
+    cfg = _tiny_cfg()
+    rng = np.random.default_rng(42)
+    W = _tiny_weights(cfg, rng)
+    for l in range(1, cfg.num_layers):
+        W["mod_w"][l][2 * cfg.hidden:3 * cfg.hidden] = 0.0
+        W["mod_w"][l][5 * cfg.hidden:] = 0.0
+    x = rng.standard_normal((1, 32, 4, 4))
+    tc, tu = rng.standard_normal((1, 3, cfg.hidden)), np.zeros((1, 3, cfg.hidden))
+    sig = O.sigmas(3, 5.0)
+    cache, xs, xu = _cache_run(W, cfg, x, tc, tu, sig, 1e9)
+    for a, b in zip(xs, xu):
+        np.testing.assert_array_equal(a, b)
+    assert (cache.full_calls, cache.reused_calls) == (1, 2)
+    cache, xs, xu = _cache_run(W, cfg, x, tc, tu, sig, 1e9, skip=(1,))
+    assert (cache.full_calls, cache.reused_calls) == (2, 1)
+    for a, b in zip(xs, xu):
+        np.testing.assert_array_equal(a, b)
+    # with live blocks a reused call differs from the full one (the cache is lossy)
+    W2 = _tiny_weights(cfg, np.random.default_rng(42))
+    cache, xs, xu = _cache_run(W2, cfg, x, tc, tu, sig, 1e9)
+    assert cache.reused_calls == 2 and not np.array_equal(xs[2], xu[2])
+    np.testing.assert_array_equal(xs[0], xu[0])
+
+
 # ------------------------------------------------------------------------------------------------
 # dimension pins (the SwiGLU / shape readings against the pages' printed sizes)
 # ------------------------------------------------------------------------------------------------
