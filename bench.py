@@ -139,6 +139,8 @@ def main():
                     help="steps timed for each guidance variant (three-pass SLG, CFG truncation; 0 = skip)")
     ap.add_argument("--steps-2048", type=int, default=2,
                     help="window steps timed at 2048^2 with 4096 text tokens, for its s/image (0 = skip)")
+    ap.add_argument("--step-cache-threshold", type=float, default=0.02,
+                    help="a 50-step image with the step cache at this threshold (0 = skip)")
     ap.add_argument("--refiner-reps", type=int, default=3,
                     help="timed text-refiner calls per prompt length (256 and 4096 tokens; 0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -280,6 +282,29 @@ def main():
         end.synchronize()
         return start.elapsed_time(end) / n
 
+    # ---- the same 50-step image with the step cache (First-Block Cache; lossy, opt-in): at the given
+    # threshold, and at an unreachable one (every call after the cache's first full call of a row plan
+    # reuses), which times the reused calls themselves ----
+    cached = None
+    if args.step_cache_threshold > 0 and args.image_steps > 0:
+        cached = []
+        for thr in (args.step_cache_threshold, 1.0e30):
+            x.copy_(x0)
+            sig_i = dt.moss_sigmas(args.image_steps, 5.0)
+            torch.cuda.synchronize()
+            start.record()
+            for i in range(args.image_steps):
+                model.moss_sample_step(x, text_cond, text_uncond, sig_i, i, cfg_scale=3.0, uncond_skip_layers=[22],
+                                       step_cache=True, step_cache_threshold=thr)
+            end.record()
+            end.synchronize()
+            full_c, reused_c, _ = model.moss_step_cache_stats()
+            assert torch.isfinite(x).all().item()
+            cached.append({"threshold": thr, "s_per_image": round(start.elapsed_time(end) / 1000.0, 3),
+                           "full_calls": full_c, "reused_calls": reused_c})
+        log(f"[bench] step cache (random N(0, 0.02) weights: the reuse rate says nothing about a trained model's): "
+            f"{json.dumps(cached)}")
+
     # ---- guidance variants at the same size: three-pass skip-layer guidance inside the window (rows
     # cond, uncond skipping 22, cond skipping 22) and a CFG-truncated step (the conditional row only) ----
     variants = None
@@ -358,6 +383,7 @@ def main():
         "step_tflop": round(step_flops / 1e12, 2),
         "roofline": roof,
         "kernels": kernels,
+        "step_cache": cached,
         "guidance_variants": variants,
         "sampling_2048": big,
         "text_refiner": refiner,

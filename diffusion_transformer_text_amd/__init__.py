@@ -66,7 +66,7 @@ class moss_step_args(C.Structure):
                 ("text_cond", C.c_void_p), ("text_uncond", C.c_void_p), ("sigmas", C.POINTER(C.c_float)),
                 ("cfg_scale", C.c_float), ("slg_start", C.c_float), ("slg_stop", C.c_float),
                 ("uncond_skip_layers", C.POINTER(C.c_int32)), ("n_skip", C.c_int32), ("slg_scale", C.c_float),
-                ("cfg_truncation", C.c_float)]
+                ("cfg_truncation", C.c_float), ("step_cache", C.c_int32), ("step_cache_threshold", C.c_float)]
 
 
 class moss_block_taps(C.Structure):
@@ -102,6 +102,7 @@ _sig("moss_guidance_euler", C.c_int, _P, _P, _P, _P, C.c_int64, C.c_float, C.c_f
 _sig("moss_dit_modulation", C.c_int, _P, C.POINTER(C.c_float), C.c_int32, _P, _P)
 _sig("moss_dit_block", C.c_int, _P, C.c_int32, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64,
      C.POINTER(moss_block_taps), _P)
+_sig("moss_step_cache_stats", C.c_int, _P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_float))
 _sig("moss_text_refine", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, _P)
 _sig("moss_attention", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_gemm_bf16", C.c_int, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P)
@@ -116,7 +117,7 @@ EXPORTED = ["moss_dit_abi_version", "moss_status_string", "moss_dit_last_error",
             "moss_dit_weights_init", "moss_dit_create", "moss_dit_destroy", "moss_forward_args_init",
             "moss_dit_forward", "moss_validate_forward_args", "moss_sigmas", "moss_step_args_init",
             "moss_sample_step", "moss_validate_step_args", "moss_cfg_euler", "moss_guidance_euler",
-            "moss_text_refine", "moss_dit_modulation",
+            "moss_text_refine", "moss_step_cache_stats", "moss_dit_modulation",
             "moss_block_taps_init", "moss_dit_block", "moss_attention", "moss_gemm_bf16",
             "moss_dit_profile_enable", "moss_dit_profile_read"]
 
@@ -332,7 +333,8 @@ class MossDiT:
 
     def moss_sample_step(self, x, text_cond, text_uncond, sigmas: np.ndarray, step: int, cfg_scale: float = 3.0,
                          uncond_skip_layers: Sequence[int] = (22,), slg_start: float = 0.01, slg_stop: float = 1.0,
-                         slg_scale: float = 0.0, cfg_truncation: float = 1.0, stream=None):
+                         slg_scale: float = 0.0, cfg_truncation: float = 1.0, step_cache: bool = False,
+                         step_cache_threshold: float = 0.0, stream=None):
         import torch
         _check_dev(x, torch.float32, "x")
         _check_dev(text_cond, torch.float32, "text_cond")
@@ -350,7 +352,14 @@ class MossDiT:
         a.uncond_skip_layers = C.cast(sk, C.POINTER(C.c_int32))
         a.n_skip = len(uncond_skip_layers)
         a.slg_scale, a.cfg_truncation = slg_scale, cfg_truncation
+        a.step_cache, a.step_cache_threshold = int(step_cache), step_cache_threshold
         _check(_lib.moss_sample_step(self.handle, C.byref(a), _stream(stream)), self.handle)
+
+    def moss_step_cache_stats(self):
+        """(full_calls, reused_calls, last_change) of the current sampling run's step cache."""
+        f, r, c = C.c_int32(), C.c_int32(), C.c_float()
+        _check(_lib.moss_step_cache_stats(self.handle, C.byref(f), C.byref(r), C.byref(c)), self.handle)
+        return f.value, r.value, c.value
 
     def moss_text_refine(self, enc, out, stream=None):
         """enc: fp32 [batch, text_len, text_dim] on the GPU -> out: fp32 [batch, text_len, hidden]."""

@@ -113,6 +113,18 @@ struct moss_dit {
   uint16_t* text_proj = nullptr;
   std::vector<uint16_t*> rqkv, rout, rgu, rdown;
   uint16_t* const_mod = nullptr;
+  // step cache (First-Block Cache) of the current sampling run, in its own allocation
+  struct StepCache {
+    bool valid = false;                  // r_prev / rest hold the last full call of this row plan
+    int B = 0, T = 0, lat_h = 0, lat_w = 0;
+    uint64_t skip[kMaxBatch] = {};
+    void* mem = nullptr;
+    size_t cap = 0;                      // elements (rows * hidden) the buffers hold
+    float *r_prev = nullptr, *r_cur = nullptr, *rest = nullptr, *partial = nullptr, *sums = nullptr;
+    uint16_t *x0 = nullptr, *x1 = nullptr;
+    int full = 0, reused = 0;
+    float last_change = NAN;
+  } fbc;
   float* rope = nullptr;   // [2][256][32]
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -299,6 +311,10 @@ int validate_step(const moss_dit_config* c, const moss_step_args* a, std::string
   }
   if (!std::isfinite(a->cfg_truncation) || a->cfg_truncation < 0.f || a->cfg_truncation > 1.f) {
     msg = "cfg_truncation must be in [0, 1] (1 = off)";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if ((a->step_cache != 0 && a->step_cache != 1) || !std::isfinite(a->step_cache_threshold)) {
+    msg = "step_cache must be 0 (off) or 1 (First-Block Cache) and step_cache_threshold finite";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   if (!a->x || !a->text_cond || !a->sigmas) {
@@ -522,7 +538,46 @@ struct FwdPlan {
   uint16_t* dump; // optional [L + 1, B, S, D]
 };
 
-int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st) {
+int ensure_fbc(moss_dit* H, size_t elems) {
+  auto& f = H->fbc;
+  if (elems <= f.cap) return MOSS_OK;
+  if (f.mem) {
+    HIP_TRY(H, hipDeviceSynchronize());
+    HIP_TRY(H, hipFree(f.mem));
+    f.mem = nullptr;
+    f.cap = 0;
+  }
+  f.valid = false;
+  const size_t bytes = align_up(elems * 4) * 3 + align_up(elems * 2) * 2 + align_up(2 * kFbcPartials * 4) + 256;
+  void* m = nullptr;
+  if (dev_alloc(&m, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(H, MOSS_ERR_OUT_OF_MEMORY, fmt("step-cache allocation of %zu bytes failed", bytes));
+  }
+  char* q = (char*)m;
+  auto take = [&](size_t b) {
+    char* r = q;
+    q += align_up(b);
+    return r;
+  };
+  f.mem = m;
+  f.cap = elems;
+  f.r_prev = (float*)take(elems * 4);
+  f.r_cur = (float*)take(elems * 4);
+  f.rest = (float*)take(elems * 4);
+  f.x0 = (uint16_t*)take(elems * 2);
+  f.x1 = (uint16_t*)take(elems * 2);
+  f.partial = (float*)take(2 * kFbcPartials * 4);
+  f.sums = (float*)take(256);
+  return MOSS_OK;
+}
+
+// step cache of one call: nullptr = off
+struct FbcCall {
+  float threshold;
+};
+
+int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st, const FbcCall* fbc = nullptr) {
   const moss_dit_config& k = H->cfg;
   const int D = k.hidden, L = k.num_layers, P = k.latent_channels * 4;
   const int gh = p.lat_h / 2, gw = p.lat_w / 2, N = gh * gw, S = p.T + N, B = p.B;
@@ -544,7 +599,7 @@ int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st) {
   const size_t stream_bytes = (size_t)B * S * D * 2;
   if (p.dump) HIP_TRY(H, hipMemcpyAsync(p.dump, c.x, stream_bytes, hipMemcpyDeviceToDevice, st));
   // A4..A10 x L, skipped blocks leave their samples' rows untouched
-  for (int l = 0; l < L; ++l) {
+  auto run_layer = [&](int l) -> int {
     int b = 0;
     while (b < B) {
       if ((p.skip[b] >> l) & 1ULL) {
@@ -553,14 +608,57 @@ int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st) {
       }
       int e = b;
       while (e < B && !((p.skip[e] >> l) & 1ULL)) ++e;
-      if ((s = run_block(H, dit_block(H, l), c.x + (size_t)b * S * D, e - b, p.T, gw, S,
-                         c.mod + (size_t)b * mstride + (size_t)l * 6 * D, mstride, c,
-                         nullptr, st)))
-        return s;
+      int s2 = run_block(H, dit_block(H, l), c.x + (size_t)b * S * D, e - b, p.T, gw, S,
+                         c.mod + (size_t)b * mstride + (size_t)l * 6 * D, mstride, c, nullptr, st);
+      if (s2) return s2;
       b = e;
     }
     if (p.dump)
       HIP_TRY(H, hipMemcpyAsync(p.dump + (size_t)(l + 1) * B * S * D, c.x, stream_bytes, hipMemcpyDeviceToDevice, st));
+    return MOSS_OK;
+  };
+  int first = 0;
+  bool reused = false;
+  const long n = (long)B * S * D;
+  auto& f = H->fbc;
+  if (fbc) {
+    // step cache: block 0, then block 0's residual against the last full call's
+    HIP_TRY(H, hipMemcpyAsync(f.x0, c.x, stream_bytes, hipMemcpyDeviceToDevice, st));
+    if ((s = run_layer(0))) return s;
+    bool same = f.valid && f.B == B && f.T == p.T && f.lat_h == p.lat_h && f.lat_w == p.lat_w;
+    for (int b = 0; same && b < B; ++b) same = f.skip[b] == p.skip[b];
+    HIP_TRY(H, launch_fbc_change(c.x, f.x0, same ? f.r_prev : nullptr, f.r_cur, n, f.partial, f.sums, st));
+    if (same) {
+      float sums[2] = {0.f, 0.f};
+      HIP_TRY(H, hipMemcpyAsync(sums, f.sums, sizeof sums, hipMemcpyDeviceToHost, st));
+      HIP_TRY(H, hipStreamSynchronize(st));
+      f.last_change = sums[0] / sums[1];
+      reused = f.last_change < fbc->threshold;   // NaN (no residual at all) runs in full
+    }
+    if (reused) {
+      HIP_TRY(H, launch_fbc_apply(c.x, f.rest, n, st));
+      first = L;
+    } else {
+      HIP_TRY(H, hipMemcpyAsync(f.x1, c.x, stream_bytes, hipMemcpyDeviceToDevice, st));
+      first = 1;
+    }
+  }
+  for (int l = first; l < L; ++l)
+    if ((s = run_layer(l))) return s;
+  if (fbc) {
+    if (reused) {
+      ++f.reused;
+    } else {
+      HIP_TRY(H, launch_fbc_rest(c.x, f.x1, f.rest, n, st));
+      std::swap(f.r_prev, f.r_cur);
+      f.valid = true;
+      f.B = B;
+      f.T = p.T;
+      f.lat_h = p.lat_h;
+      f.lat_w = p.lat_w;
+      for (int b = 0; b < kMaxBatch; ++b) f.skip[b] = b < B ? p.skip[b] : 0;
+      ++f.full;
+    }
   }
   // A11: final LN-mod on the image rows, output projection, unpatchify to fp32 velocity
   LnModArgs ln = ln_args(c.x, c.a, B * N, D, N, c.mod + (long)L * 6 * D, c.mod + (long)L * 6 * D + D, mstride,
@@ -675,6 +773,8 @@ void moss_step_args_init(moss_step_args* a, uint32_t size) {
   d.n_skip = 1;
   d.slg_scale = 0.0f;
   d.cfg_truncation = 1.0f;
+  d.step_cache = 0;
+  d.step_cache_threshold = 0.0f;
   memcpy(a, &d, size < sizeof d ? size : sizeof d);
 }
 
@@ -862,6 +962,7 @@ void moss_dit_destroy(moss_dit* h) {
   (void)hipSetDevice(h->device);
   (void)hipDeviceSynchronize();
   if (h->ws) (void)hipFree(h->ws);
+  if (h->fbc.mem) (void)hipFree(h->fbc.mem);
   if (h->wbuf) (void)hipFree(h->wbuf);
   for (auto& pool : h->prof_ev)
     for (auto& e : pool) {
@@ -937,13 +1038,31 @@ int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream) {
     p.skip[r] = r == 0 ? 0 : mask;
   }
   p.vel = c.vel;
-  if ((s = run_forward(h, p, c, (hipStream_t)stream))) return s;
+  FbcCall fc{a->step_cache_threshold > 0.f ? a->step_cache_threshold : 0.02f};
+  if (a->step == 0 || !a->step_cache) {      // a new sampling run, or the cache is off: start over
+    h->fbc.valid = false;
+    h->fbc.full = h->fbc.reused = 0;
+    h->fbc.last_change = NAN;
+  }
+  if (a->step_cache && (s = ensure_fbc(h, (size_t)B * S * k.hidden))) return s;
+  if ((s = run_forward(h, p, c, (hipStream_t)stream, a->step_cache ? &fc : nullptr))) return s;
   // A12: FP32 guidance combine + Euler, in place on x
   ProfScope ps(h, PC_CFG, (hipStream_t)stream);
   const float* v_u = neg ? c.vel + lat : nullptr;
   const float* v_s = third ? c.vel + (long)(B - 1) * lat : nullptr;
   HIP_TRY(h, launch_guidance_euler(c.vel, v_u, v_s, a->x, lat, a->cfg_scale, a->slg_scale, sig, sig_next,
                                    (hipStream_t)stream));
+  return MOSS_OK;
+}
+
+int moss_step_cache_stats(const moss_dit* h, int32_t* full_calls, int32_t* reused_calls, float* last_change) {
+  if (!h) {
+    g_thread_error = "handle is NULL";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (full_calls) *full_calls = h->fbc.full;
+  if (reused_calls) *reused_calls = h->fbc.reused;
+  if (last_change) *last_change = h->fbc.last_change;
   return MOSS_OK;
 }
 

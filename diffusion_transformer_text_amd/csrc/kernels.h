@@ -106,6 +106,15 @@ hipError_t launch_text_cast(PtrBatch text, int B, int T, int D, int S, uint16_t*
 // x = x + (sigma_next - sigma) * (v_u + cfg * (v_c - v_u)); v_u == nullptr means v = v_c.
 hipError_t launch_cfg_euler(const float* v_c, const float* v_u, float* x, long n, float cfg, float sigma,
                             float sigma_next, hipStream_t stream);
+// Step cache (First-Block Cache): r_cur = x1 - x0 (fp32); with r_prev also sums[0] = sum|r_cur - r_prev|
+// and sums[1] = sum|r_prev| (fixed-order reduction through `partial`, 2 * 1024 floats).
+hipError_t launch_fbc_change(const uint16_t* x1, const uint16_t* x0, const float* r_prev, float* r_cur, long n,
+                             float* partial, float* sums, hipStream_t stream);
+// rest = xl - x1 (fp32)
+hipError_t launch_fbc_rest(const uint16_t* xl, const uint16_t* x1, float* rest, long n, hipStream_t stream);
+// x = bf16(x + rest)
+hipError_t launch_fbc_apply(uint16_t* x, const float* rest, long n, hipStream_t stream);
+constexpr int kFbcPartials = 1024;
 // dst = float(src) for n bf16 values (src 8-byte, dst 16-byte aligned).
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, long n, hipStream_t stream);
 // As above plus slg * (v_c - v_s) when v_s != nullptr (the skipped conditional prediction).

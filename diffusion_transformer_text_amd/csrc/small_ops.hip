@@ -146,6 +146,78 @@ __global__ void guidance_euler_kernel(const float* __restrict__ vc, const float*
   }
 }
 
+// ---- step cache (First-Block Cache) ----
+constexpr int kFbcBlocks = 1024;   // partial sums of the change measure: one pair per workgroup
+
+// r_cur = float(x1) - float(x0) (block 0's residual); with r_prev, partial sums of |r_cur - r_prev|
+// and |r_prev| per workgroup (written, not accumulated: a fixed-order reduction follows).
+__global__ __launch_bounds__(256) void fbc_residual_kernel(const uint16_t* __restrict__ x1, const uint16_t* __restrict__ x0,
+                                                           const float* __restrict__ r_prev, float* __restrict__ r_cur,
+                                                           long n, float* __restrict__ partial) {
+  float d = 0.f, a = 0.f;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float r = bf16_to_f32(x1[i]) - bf16_to_f32(x0[i]);
+    r_cur[i] = r;
+    if (r_prev != nullptr) {
+      d += fabsf(r - r_prev[i]);
+      a += fabsf(r_prev[i]);
+    }
+  }
+  if (r_prev == nullptr) return;
+  __shared__ float sd[4], sa[4];
+  d = wave_sum(d);
+  a = wave_sum(a);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    sd[wave] = d;
+    sa[wave] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    partial[2 * blockIdx.x] = (sd[0] + sd[1]) + (sd[2] + sd[3]);
+    partial[2 * blockIdx.x + 1] = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+  }
+}
+
+// sums[0..1] = the workgroup partials added in a fixed order (one workgroup of 256 lanes)
+__global__ __launch_bounds__(256) void fbc_sum_kernel(const float* __restrict__ partial, int nparts,
+                                                      float* __restrict__ sums) {
+  float d = 0.f, a = 0.f;
+  for (int i = threadIdx.x; i < nparts; i += 256) {
+    d += partial[2 * i];
+    a += partial[2 * i + 1];
+  }
+  __shared__ float sd[4], sa[4];
+  d = wave_sum(d);
+  a = wave_sum(a);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    sd[wave] = d;
+    sa[wave] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    sums[0] = (sd[0] + sd[1]) + (sd[2] + sd[3]);
+    sums[1] = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+  }
+}
+
+// rest = float(xL) - float(x1): what blocks 1.. added at a full call
+__global__ void fbc_rest_kernel(const uint16_t* __restrict__ xl, const uint16_t* __restrict__ x1,
+                                float* __restrict__ rest, long n) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    rest[i] = bf16_to_f32(xl[i]) - bf16_to_f32(x1[i]);
+}
+
+// x = bf16(float(x) + rest): a reused call's stream after the last block
+__global__ void fbc_apply_kernel(uint16_t* __restrict__ x, const float* __restrict__ rest, long n) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    x[i] = f32_to_bf16(bf16_to_f32(x[i]) + rest[i]);
+}
+
 // fp32 copy of a bf16 tensor (exact), 4 elements per lane.
 __global__ void bf16_to_f32_kernel(const uint16_t* __restrict__ src, float* __restrict__ dst, long n) {
   const long stride = (long)gridDim.x * blockDim.x;
@@ -221,6 +293,26 @@ hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, long n, hipStream
   if (grid < 1) grid = 1;
   if (grid > 4096) grid = 4096;
   hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((unsigned)grid), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fbc_change(const uint16_t* x1, const uint16_t* x0, const float* r_prev, float* r_cur, long n,
+                             float* partial, float* sums, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fbc_residual_kernel, dim3(kFbcBlocks), dim3(256), 0, stream, x1, x0, r_prev, r_cur, n, partial);
+  if (r_prev != nullptr) hipLaunchKernelGGL(fbc_sum_kernel, dim3(1), dim3(256), 0, stream, partial, kFbcBlocks, sums);
+  return hipGetLastError();
+}
+
+hipError_t launch_fbc_rest(const uint16_t* xl, const uint16_t* x1, float* rest, long n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fbc_rest_kernel, dim3(2048), dim3(256), 0, stream, xl, x1, rest, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fbc_apply(uint16_t* x, const float* rest, long n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fbc_apply_kernel, dim3(2048), dim3(256), 0, stream, x, rest, n);
   return hipGetLastError();
 }
 

@@ -162,6 +162,15 @@ int moss_sigmas(int32_t num_steps, float shift, float* sigmas /* host [num_steps
  *     prediction"): inside the same window, a third pass runs the conditional input skipping the
  *     same uncond_skip_layers, v_s, and v += slg_scale * (v_c - v_s). The pages give no formula; this
  *     is the skip-layer guidance form. slg_scale = 0 (default) is the two-pass recipe.
+ *   - Step cache (step_cache = 1, off by default; lossy: it changes the image): the First-Block Cache
+ *     of the MossInfer integration guide ("Lossy accelerators"): blocks 1.. are reused from the last
+ *     full call while block 0's output changed by less than step_cache_threshold (<= 0: 0.02, the
+ *     base model's default). Readings: the change is sum|r - r_prev| / sum|r_prev| with r = the
+ *     residual stream after block 0 minus the one before it (all rows of the call) and r_prev the same
+ *     at the last full call; a reused call takes the stream after the last block as bf16(x after block
+ *     0 + the difference of those two streams at the last full call). A call whose rows (batch, shapes,
+ *     per-row skip sets) differ from the cached call's, and every step 0, runs in full and restarts
+ *     the cache. The cache lives in the handle; reading the change synchronises `stream` once per call.
  * All guidance arithmetic is fp32. */
 typedef struct {
   uint32_t struct_size;
@@ -176,11 +185,17 @@ typedef struct {
   int32_t n_skip;
   float slg_scale;                   /* >= 0; > 0 runs the third (skipped conditional) pass           */
   float cfg_truncation;              /* in [0, 1]; 1 = off                                            */
+  int32_t step_cache;                /* 0 = off, 1 = First-Block Cache                                */
+  float step_cache_threshold;        /* <= 0: 0.02                                                    */
 } moss_step_args;
 /* Defaults: cfg 3, slg_start 0.01, slg_stop 1.0, uncond_skip_layers = {22}, num_steps 50, step 0,
- * slg_scale 0 (two-pass), cfg_truncation 1 (off). */
+ * slg_scale 0 (two-pass), cfg_truncation 1 (off), step_cache 0 (off), step_cache_threshold 0. */
 void moss_step_args_init(moss_step_args* a, uint32_t size);
 int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream);
+/* Step-cache counters of the current sampling run (reset at step 0): calls that ran every block,
+ * calls that reused blocks 1.., and the last measured change (NaN before the first comparison).
+ * Host only; any output pointer may be NULL. */
+int moss_step_cache_stats(const moss_dit* h, int32_t* full_calls, int32_t* reused_calls, float* last_change);
 /* Host-only check of step arguments (no GPU needed). msg (may be NULL) receives the reason. */
 int moss_validate_step_args(const moss_dit_config* cfg, const moss_step_args* a, char* msg, int32_t msg_len);
 

@@ -82,6 +82,7 @@ def test_step_defaults_are_the_pages():
     assert (s.latent_h * 8, s.latent_w * 8) == (g["height"], g["width"])
     # the guidance variants are off by default: two-pass recipe, no CFG truncation
     assert s.slg_scale == 0.0 and s.cfg_truncation == 1.0
+    assert s.step_cache == 0 and s.step_cache_threshold == 0.0      # the step cache is off by default
 
 
 @pytest.mark.parametrize("N,shift", [(50, 5.0), (2, 5.0), (7, 1.0), (1000, 3.0)])
@@ -129,6 +130,8 @@ def test_validate_step_accepts_defaults_and_2048():
     ("cfg_truncation", 1.5, 1, "cfg_truncation"),
     ("cfg_truncation", -0.1, 1, "cfg_truncation"),
     ("cfg_truncation", float("nan"), 1, "cfg_truncation"),
+    ("step_cache", 2, 1, "step_cache"),
+    ("step_cache_threshold", float("nan"), 1, "step_cache"),
 ])
 def test_validate_step_errors(field, value, status, needle):
     cfg = dt.moss_dit_config_init()
