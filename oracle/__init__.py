@@ -28,6 +28,10 @@ Parity status of each function (pins in tests/test_oracle_pins.py):
   forward_cached,             forward/step bit for bit; with blocks 1.. made identities (zero gates)
   sample_step_cached          a reused call equals the full call bit for bit; step 0 and a new row
                               plan restart the cache
+  e4m3_round, mx_quantize,    pinned: E4M3 rounding against a brute force over all 256 codes decoded
+  mx_dequantize               from the bit layout (ties to even, saturation); hand MX blocks (scale
+                              exponent, saturation, zero block); exact round trip of representable
+                              values; the per-element error bound
   negative_pass_runs          pinned: hand table of the truncation boundary (X * steps, steps from 0)
   guidance_combine            pinned: hand values of each term, v_s = v_c leaves the two-pass result,
                               linearity in slg_scale
@@ -41,5 +45,6 @@ from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, emb
                           final_layer, forward, from_bf16_bits, guidance_combine, layernorm, ln_modulate,
                           modulation, negative_pass_runs, text_refine, StepCache,
                           first_block_change, forward_cached, sample_step_cached,
+                          e4m3_round, mx_quantize, mx_dequantize, E4M3_MAX, projection,
                           patchify, rope_angles, apply_rope, rope_rows, sample_step, sigmas, silu,
                           slg_active, time_features, unpatchify, weights_to_f64)

@@ -87,6 +87,7 @@ class Config:
     flow_multiplier: float = 1000.0
     text_dim: int = 4096
     refiner_layers: int = 2
+    gemm_precision: str = "bf16"        # "bf16", or "mxfp8" for the FP8 tier of the block projections
 
     @property
     def patch_dim(self) -> int:
@@ -263,6 +264,56 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, num_heads: int, head_
 
 
 # ----------------------------------------------------------------------------------------------
+# FP8 tier: OCP microscaling (MX) FP8 operands of the block projections
+# ----------------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Nearest OCP FP8 E4M3 value (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; subnormal step
+    2^-9; largest finite 448; no infinities), round half to even, saturating at +-448. Float64 values."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, E = np.frexp(a)                                   # a = f 2^E, f in [0.5, 1)
+    e = np.maximum(E - 1, -6)                            # binade exponent; subnormals share 2^-6's
+    step = np.ldexp(1.0, e - 3)
+    q = np.rint(a / step) * step                         # rint: half to even on the mantissa integer
+    return np.sign(x) * np.minimum(q, E4M3_MAX)
+
+
+def mx_quantize(x: np.ndarray, block: int = 32):
+    """OCP MX block quantization along the last axis (blocks of 32): scale exponent
+    floor(log2(amax)) - 8 (8 = E4M3's largest exponent), E8M0 range [-127, 127] (an all-zero block takes
+    -127), elements e4m3_round(x / 2^scale). Returns (codes as float64, scale exponents)."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    assert K % block == 0
+    xb = x.reshape(x.shape[:-1] + (K // block, block))
+    amax = np.abs(xb).max(axis=-1)
+    _, E = np.frexp(np.where(amax > 0, amax, 1.0))
+    ex = np.where(amax > 0, E - 1 - 8, -127)
+    ex = np.clip(ex, -127, 127)
+    q = e4m3_round(xb * np.ldexp(1.0, -ex)[..., None])
+    return q.reshape(x.shape), ex
+
+
+def mx_dequantize(x: np.ndarray, block: int = 32) -> np.ndarray:
+    """x -> its MXFP8 value (quantize then scale back)."""
+    q, ex = mx_quantize(x, block)
+    K = q.shape[-1]
+    return (q.reshape(q.shape[:-1] + (K // block, block)) * np.ldexp(1.0, ex)[..., None]).reshape(q.shape)
+
+
+def projection(a: np.ndarray, w: np.ndarray, cfg: "Config") -> np.ndarray:
+    """a w^T of a block projection: bf16 operands as they are, or both operands MXFP8-quantized along
+    the reduction axis (the FP8 tier)."""
+    if cfg.gemm_precision == "mxfp8":
+        return mx_dequantize(a) @ mx_dequantize(w).T
+    return a @ w.T
+
+
+# ----------------------------------------------------------------------------------------------
 # A4..A10  one joint block
 # ----------------------------------------------------------------------------------------------
 
@@ -289,20 +340,20 @@ def block(x: np.ndarray, m: np.ndarray, W: Dict, l: int, cfg: Config, text_len: 
 
     a_all = r(ln_modulate(x, shift1, scale1, eps))
     wqkv = W["qkv_w"][l]
-    kv = r(a_all @ wqkv[D:3 * D].T)                      # K | V for every row
+    kv = r(projection(a_all, wqkv[D:3 * D], cfg))               # K | V for every row
     k_all = r(rope_rows(kv[:, :D], text_len, grid_w, d, theta))
     v_all = kv[:, D:]
-    q = r(a_all[rows] @ wqkv[:D].T)
+    q = r(projection(a_all[rows], wqkv[:D], cfg))
     q = r(rope_rows(q, text_len, grid_w, d, theta, rows=rows))
     o = r(attention(q, k_all, v_all, H, d))
-    attn_out = o @ W["out_w"][l].T
+    attn_out = projection(o, W["out_w"][l], cfg)
     x1 = r(x[rows] + gate1 * attn_out)
     a2 = r(ln_modulate(x1, shift2, scale2, eps))
     wgu = W["gate_up_w"][l]
-    g = a2 @ wgu[:F].T
-    u = a2 @ wgu[F:].T
+    g = projection(a2, wgu[:F], cfg)
+    u = projection(a2, wgu[F:], cfg)
     hf = r(silu(g) * u)
-    ffn_out = hf @ W["down_w"][l].T
+    ffn_out = projection(hf, W["down_w"][l], cfg)
     x2 = r(x1 + gate2 * ffn_out)
     if taps is not None:
         taps.update(dict(a=a_all[rows], q=q, k=k_all, v=v_all, o=o, attn_out=attn_out, x1=x1,

@@ -684,6 +684,87 @@ def test_step_cache_reuse_composes_block0_and_the_cached_rest():
     np.testing.assert_array_equal(xs[0], xu[0])
 
 
+def _e4m3_table():
+    # every finite E4M3 value from the bit layout: S EEEE MMM, bias 7, E = 0 subnormal, S 1111 111 NaN
+    vals = []
+    for code in range(256):
+        s_, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        vals.append((-v if s_ else v, m))
+    return vals
+
+
+def test_e4m3_round_bruteforce_over_all_codes():
+    table = _e4m3_table()
+    assert max(v for v, _ in table) == golden()["fp8_e4m3"]["max_finite"] == O.E4M3_MAX
+    assert min(v for v, _ in table if v > 0) == golden()["fp8_e4m3"]["min_subnormal"]
+    rng = np.random.default_rng(60)
+    xs = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.uniform(-4, 3, 3000),
+                         [v + d for v, _ in table for d in (0.0,)],          # every code exactly
+                         [0.5 * (a + b) for (a, _), (b, _) in zip(sorted(table), sorted(table)[1:])]])  # every tie
+    got = O.e4m3_round(xs)
+    for x, g in zip(xs, got):
+        if abs(x) >= O.E4M3_MAX:
+            assert g == math.copysign(O.E4M3_MAX, x)
+            continue
+        best = min(table, key=lambda vm: (abs(vm[0] - x), vm[1] & 1))   # nearest, ties to even mantissa
+        assert g == best[0] or (g == 0 and best[0] == 0), (x, g, best)
+
+
+def test_mx_quantize_hand_blocks_and_bounds():
+    # amax 3 -> scale exponent floor(log2 3) - 8 = -7; codes 1*2^7 = 128, 3*2^7 = 384 (both exact)
+    x = np.zeros((1, 64))
+    x[0, 0], x[0, 1] = 1.0, 3.0
+    x[0, 32] = 500.0          # second block: exponent 8 - 8 = 0, 500 saturates to 448
+    q, ex = O.mx_quantize(x)
+    assert ex.tolist() == [[-7, 0]]
+    assert (q[0, 0], q[0, 1], q[0, 32]) == (128.0, 384.0, 448.0)
+    np.testing.assert_array_equal(O.mx_dequantize(np.zeros((2, 32))), 0.0)
+    assert O.mx_quantize(np.zeros((1, 32)))[1].tolist() == [[-127]]
+    # values of the form e4m3 * 2^k with a shared block exponent come back exactly
+    rng = np.random.default_rng(61)
+    codes = np.array([v for v, _ in _e4m3_table() if abs(v) >= 1.0])
+    blk = rng.choice(codes, (4, 32)) * 2.0 ** -5
+    blk[:, 0] = 256.0 * 2.0 ** -5                        # fixes each block's amax binade
+    np.testing.assert_array_equal(O.mx_dequantize(blk), blk)
+    # error bound: half a unit of the element's binade (3 mantissa bits), or of 2^(scale-9) below normals,
+    # except where the scaled value exceeds 448 (the scale exponent floor(log2 amax) - 8 lets a block's
+    # largest elements reach [448, 512)) and saturates
+    x = rng.standard_normal((8, 256)) * 10.0 ** rng.uniform(-3, 3, (8, 1))
+    d = O.mx_dequantize(x)
+    _, ex = O.mx_quantize(x)
+    scale = np.repeat(np.ldexp(1.0, ex), 32, axis=1)
+    _, E = np.frexp(np.abs(x))
+    unit = np.maximum(np.ldexp(1.0, E - 1 - 3), scale * 2.0 ** -9)
+    sat = np.abs(x) >= O.E4M3_MAX * scale
+    assert np.all(np.abs(d - x)[~sat] <= 0.5 * unit[~sat])
+    np.testing.assert_array_equal(np.abs(d[sat]), (O.E4M3_MAX * scale)[sat])
+    assert sat.any()
+
+
+def test_mxfp8_projection_is_the_product_of_quantized_operands():
+    # the FP8 tier's projection multiplies the MXFP8 values of both operands (quantized along the
+    # reduction axis): on operands that already are MXFP8 values it is the plain product, exactly; and
+    # a whole block stays within a few percent of the bf16 block's update
+    cfg = _tiny_cfg()
+    cfg8 = O.Config(**{**cfg.__dict__, "gemm_precision": "mxfp8"})
+    rng = np.random.default_rng(62)
+    a = O.mx_dequantize(rng.standard_normal((5, 64)))
+    w = O.mx_dequantize(rng.standard_normal((7, 64)) * 0.05)
+    np.testing.assert_array_equal(O.projection(a, w, cfg8), a @ w.T)
+    a2 = rng.standard_normal((5, 64))
+    np.testing.assert_array_equal(O.projection(a2, w, cfg8), O.mx_dequantize(a2) @ w.T)
+    W = _tiny_weights(cfg, rng)
+    x = rng.standard_normal((6, cfg.hidden))
+    m, _ = O.modulation(0.4, W, cfg)
+    b16 = O.block(x, m[0], W, 0, cfg, 2, 2)
+    b8 = O.block(x, m[0], W, 0, cfg8, 2, 2)
+    rel = np.linalg.norm(b8 - b16) / np.linalg.norm(b16 - x)
+    assert 1e-4 < rel < 0.2          # 3 mantissa bits: about 2-3 % per operand, compounded
+
+
 # ------------------------------------------------------------------------------------------------
 # dimension pins (the SwiGLU / shape readings against the pages' printed sizes)
 # ------------------------------------------------------------------------------------------------
