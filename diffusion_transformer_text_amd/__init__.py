@@ -41,7 +41,8 @@ class moss_dit_config(C.Structure):
                 ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_hidden", C.c_int32),
                 ("latent_channels", C.c_int32), ("patch", C.c_int32), ("temb_dim", C.c_int32),
                 ("qk_norm", C.c_int32), ("rope_theta", C.c_float), ("norm_eps", C.c_float),
-                ("flow_multiplier", C.c_float), ("text_dim", C.c_int32), ("refiner_layers", C.c_int32)]
+                ("flow_multiplier", C.c_float), ("text_dim", C.c_int32), ("refiner_layers", C.c_int32),
+                ("gemm_precision", C.c_int32)]
 
 
 class moss_dit_weights(C.Structure):
@@ -106,6 +107,8 @@ _sig("moss_step_cache_stats", C.c_int, _P, C.POINTER(C.c_int32), C.POINTER(C.c_i
 _sig("moss_text_refine", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, _P)
 _sig("moss_attention", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_gemm_bf16", C.c_int, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P)
+_sig("moss_mx_quantize", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, C.c_int64, _P)
+_sig("moss_gemm_mxfp8", C.c_int, _P, _P, C.c_int64, _P, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_dit_profile_enable", C.c_int, _P, C.c_int32)
 _sig("moss_dit_profile_read", C.c_int, _P, C.POINTER(C.c_double), C.POINTER(C.c_int64))
 
@@ -119,7 +122,7 @@ EXPORTED = ["moss_dit_abi_version", "moss_status_string", "moss_dit_last_error",
             "moss_sample_step", "moss_validate_step_args", "moss_cfg_euler", "moss_guidance_euler",
             "moss_text_refine", "moss_step_cache_stats", "moss_dit_modulation",
             "moss_block_taps_init", "moss_dit_block", "moss_attention", "moss_gemm_bf16",
-            "moss_dit_profile_enable", "moss_dit_profile_read"]
+            "moss_mx_quantize", "moss_gemm_mxfp8", "moss_dit_profile_enable", "moss_dit_profile_read"]
 
 
 # ---- host-only calls ----
@@ -244,6 +247,42 @@ def moss_gemm_bf16(A, W, out, stream=None):
     if W.shape[1] != K or tuple(out.shape) != (M, N):
         raise ValueError("shape mismatch")
     _check(_lib.moss_gemm_bf16(_ptr(A), _ptr(W), _ptr(out), M, N, K, _stream(stream)))
+
+
+def mx_scale_words(rows: int, K: int) -> int:
+    """Words of MXFP8 scale storage for `rows` rows (ld = rows) of reduction length K."""
+    return K // 128 * rows
+
+
+def moss_mx_quantize(x, codes, scales, ld_scale=None, stream=None):
+    """x bf16 [rows, K] -> codes uint8 [rows, K] and scale words int32 [K / 128 * ld_scale]."""
+    import torch
+    _check_dev(x, torch.bfloat16, "x")
+    _check_dev(codes, torch.uint8, "codes")
+    _check_dev(scales, torch.int32, "scales")
+    rows, K = x.shape
+    ld = rows if ld_scale is None else int(ld_scale)
+    if tuple(codes.shape) != (rows, K) or scales.numel() < K // 128 * ld:
+        raise ValueError("codes / scales sizes do not match x")
+    _check(_lib.moss_mx_quantize(_ptr(x), rows, K, _ptr(codes), _ptr(scales), ld, _stream(stream)))
+
+
+def moss_gemm_mxfp8(A, A_scales, lds_a, W, W_scales, lds_w, out, stream=None):
+    """out fp32 [M, N] = MXFP8(A) MXFP8(W)^T from codes (uint8 [M, K], [N, K]) and scale words (int32)."""
+    import torch
+    for t, name in ((A, "A"), (W, "W")):
+        _check_dev(t, torch.uint8, name)
+    for t, name in ((A_scales, "A_scales"), (W_scales, "W_scales")):
+        _check_dev(t, torch.int32, name)
+    _check_dev(out, torch.float32, "out")
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    if A_scales.numel() < K // 128 * lds_a or W_scales.numel() < K // 128 * lds_w:
+        raise ValueError("scale words too short for lds_a / lds_w")
+    _check(_lib.moss_gemm_mxfp8(_ptr(A), _ptr(A_scales), int(lds_a), _ptr(W), _ptr(W_scales), int(lds_w), _ptr(out),
+                                M, N, K, _stream(stream)))
 
 
 class MossDiT:

@@ -113,6 +113,16 @@ struct moss_dit {
   uint16_t* text_proj = nullptr;
   std::vector<uint16_t*> rqkv, rout, rgu, rdown;
   uint16_t* const_mod = nullptr;
+  // FP8 tier (gemm_precision 1): MXFP8 copies of the block projection weights (codes [N, K] and scale
+  // words with ld = N), in their own allocation
+  struct Mx8 {
+    const uint8_t* codes = nullptr;
+    const uint8_t* scales = nullptr;
+    long ld = 0;
+  };
+  std::vector<Mx8> qkv8, out8, gu8, down8, rqkv8, rout8, rgu8, rdown8;
+  void* w8buf = nullptr;
+  bool fp8() const { return cfg.gemm_precision == 1; }
   // step cache (First-Block Cache) of the current sampling run, in its own allocation
   struct StepCache {
     bool valid = false;                  // r_prev / rest hold the last full call of this row plan
@@ -213,6 +223,14 @@ int check_config(const moss_dit_config* c, std::string& msg) {
       c->refiner_layers > 8) {
     msg = fmt("unsupported text refiner configuration (need text_dim %% 64 == 0 in [64, 16384], 0..8 refiner layers; "
               "got %d, %d)", c->text_dim, c->refiner_layers);
+    return MOSS_ERR_NOT_SUPPORTED;
+  }
+  if (c->gemm_precision != 0 && c->gemm_precision != 1) {
+    msg = fmt("gemm_precision must be 0 (bf16) or 1 (MXFP8), got %d", c->gemm_precision);
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (c->gemm_precision == 1 && c->ffn_hidden % 256 != 0) {
+    msg = fmt("the MXFP8 tier needs ffn_hidden %% 256 == 0 (got %d)", c->ffn_hidden);
     return MOSS_ERR_NOT_SUPPORTED;
   }
   return MOSS_OK;
@@ -349,6 +367,8 @@ int validate_step(const moss_dit_config* c, const moss_step_args* a, std::string
 struct Carve {
   uint16_t *x, *a, *qkv, *o, *h, *tokens, *mod;
   float *u, *vel;
+  uint8_t *q8, *s8;   // FP8 tier: one quantized activation (codes, scale words with ld = M rounded to 256)
+  long lds8;
 };
 
 size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, Carve* c) {
@@ -371,6 +391,13 @@ size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, 
   t.mod = (uint16_t*)take((size_t)B * H->mod_rows() * 2);
   t.u = (float*)take((size_t)B * k.temb_dim * 4);
   t.vel = (float*)take((size_t)B * lat_elems * 4);   // one velocity per row of the step's batch
+  t.q8 = t.s8 = nullptr;
+  t.lds8 = (long)(M + 255) / 256 * 256;
+  if (H->fp8()) {
+    const size_t Kmax = D > F ? D : F;
+    t.q8 = (uint8_t*)take(M * Kmax);
+    t.s8 = (uint8_t*)take(Kmax / 128 * (size_t)t.lds8 * 4);
+  }
   if (c) *c = t;
   return off;
 }
@@ -435,9 +462,48 @@ LnModArgs ln_args(const uint16_t* x, uint16_t* out, int rows, int D, int rows_pe
 // The weights of one joint block (a DiT block or a text-refiner block).
 struct BlockW {
   const uint16_t *qkv, *out, *gu, *down;
+  moss_dit::Mx8 qkv8, out8, gu8, down8;   // FP8 tier only
 };
 
-BlockW dit_block(const moss_dit* H, int l) { return {H->qkv[l], H->out[l], H->gu[l], H->down[l]}; }
+BlockW dit_block(const moss_dit* H, int l) {
+  BlockW w{H->qkv[l], H->out[l], H->gu[l], H->down[l], {}, {}, {}, {}};
+  if (H->fp8()) {
+    w.qkv8 = H->qkv8[l];
+    w.out8 = H->out8[l];
+    w.gu8 = H->gu8[l];
+    w.down8 = H->down8[l];
+  }
+  return w;
+}
+
+BlockW refiner_block(const moss_dit* H, int l) {
+  BlockW w{H->rqkv[l], H->rout[l], H->rgu[l], H->rdown[l], {}, {}, {}, {}};
+  if (H->fp8()) {
+    w.qkv8 = H->rqkv8[l];
+    w.out8 = H->rout8[l];
+    w.gu8 = H->rgu8[l];
+    w.down8 = H->rdown8[l];
+  }
+  return w;
+}
+
+// A block projection: the bf16 GEMM, or in the FP8 tier the activation quantized to MXFP8 (into the
+// workspace) and the scaled FP8 GEMM against the weight's MXFP8 copy. g carries the bf16 operands and
+// the epilogue arguments; its M rows of A (row stride K) are the activation.
+hipError_t project(const moss_dit* H, const Carve& c, GemmArgs g, const moss_dit::Mx8& w8, int epi, hipStream_t st) {
+  if (!H->fp8()) return launch_gemm(g, epi, st);
+  const hipError_t e = launch_mx_quant(g.A, g.lda, g.M, g.K, c.q8, c.s8, c.lds8, st);
+  if (e != hipSuccess) return e;
+  g.A = reinterpret_cast<const uint16_t*>(c.q8);
+  g.lda = g.K;
+  g.W = reinterpret_cast<const uint16_t*>(w8.codes);
+  g.ldw = g.K;
+  g.A_scale = c.s8;
+  g.W_scale = w8.scales;
+  g.lds_a = c.lds8;
+  g.lds_w = w8.ld;
+  return launch_gemm_mxfp8(g, epi, st);
+}
 
 // One joint block on nb samples of S rows each (x [nb * S, D], in place). m: the block's six modulation
 // vectors of the first sample ([6 * D]); sample b's are at m + b * mod_stride (stride 0: all share).
@@ -465,7 +531,7 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   g.rope_cols = 2 * D;
   {
     ProfScope ps(H, PC_QKV, st);
-    HIP_TRY(H, launch_gemm(g, EPI_QKV_ROPE, st));
+    HIP_TRY(H, project(H, c, g, w.qkv8, EPI_QKV_ROPE, st));
   }
   HIP_TRY(H, tap_copy(taps ? taps->qkv : nullptr, c.qkv, (size_t)M * 3 * D * 2));
   // A6: attention
@@ -484,14 +550,14 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   }
   HIP_TRY(H, tap_copy(taps ? taps->o : nullptr, c.o, (size_t)M * D * 2));
   // A7: out projection + gated residual
-  if (taps && taps->attn) HIP_TRY(H, launch_gemm(gemm_args(c.o, w.out, M, D, D, taps->attn, D), EPI_F32, st));
+  if (taps && taps->attn) HIP_TRY(H, project(H, c, gemm_args(c.o, w.out, M, D, D, taps->attn, D), w.out8, EPI_F32, st));
   g = gemm_args(c.o, w.out, M, D, D, x, D);
   g.gate = m + 2 * D;
   g.rows_per_sample = S;
   g.gate_stride = mod_stride;
   {
     ProfScope ps(H, PC_OUT, st);
-    HIP_TRY(H, launch_gemm(g, EPI_GATED_RES, st));
+    HIP_TRY(H, project(H, c, g, w.out8, EPI_GATED_RES, st));
   }
   HIP_TRY(H, tap_copy(taps ? taps->x1 : nullptr, x, (size_t)M * D * 2));
   // A8: LN2 + modulation
@@ -503,18 +569,18 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   // A9: gate/up projection + SiLU * mul
   {
     ProfScope ps(H, PC_GATE_UP, st);
-    HIP_TRY(H, launch_gemm(gemm_args(c.a, w.gu, M, 2 * F, D, c.h, F), EPI_SWIGLU, st));
+    HIP_TRY(H, project(H, c, gemm_args(c.a, w.gu, M, 2 * F, D, c.h, F), w.gu8, EPI_SWIGLU, st));
   }
   HIP_TRY(H, tap_copy(taps ? taps->h : nullptr, c.h, (size_t)M * F * 2));
   // A10: down projection + gated residual
-  if (taps && taps->ffn) HIP_TRY(H, launch_gemm(gemm_args(c.h, w.down, M, D, F, taps->ffn, D), EPI_F32, st));
+  if (taps && taps->ffn) HIP_TRY(H, project(H, c, gemm_args(c.h, w.down, M, D, F, taps->ffn, D), w.down8, EPI_F32, st));
   g = gemm_args(c.h, w.down, M, D, F, x, D);
   g.gate = m + 5 * D;
   g.rows_per_sample = S;
   g.gate_stride = mod_stride;
   {
     ProfScope ps(H, PC_DOWN, st);
-    HIP_TRY(H, launch_gemm(g, EPI_GATED_RES, st));
+    HIP_TRY(H, project(H, c, g, w.down8, EPI_GATED_RES, st));
   }
   return MOSS_OK;
 }
@@ -733,6 +799,7 @@ void moss_dit_config_init(moss_dit_config* c, uint32_t size) {
   d.flow_multiplier = 1000.f;
   d.text_dim = 4096;
   d.refiner_layers = 2;
+  d.gemm_precision = 0;
   memcpy(c, &d, size < sizeof d ? size : sizeof d);
 }
 
@@ -847,6 +914,7 @@ int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int w
   uint16_t* stage = nullptr;   // staging for host gate/up weights (interleaved on the device)
   auto bail = [&](int status, const std::string& m) {
     if (stage) hipFree(stage);
+    if (H->w8buf) hipFree(H->w8buf);
     if (H->wbuf) hipFree(H->wbuf);
     delete H;
     return fail(nullptr, status, m);
@@ -947,6 +1015,48 @@ int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int w
     for (size_t i = 0; i < D; ++i) cmod[2 * D + i] = cmod[5 * D + i] = 0x3f80;
     CREATE_TRY(hipMemcpyAsync(H->const_mod, cmod.data(), n_cmod * 2, hipMemcpyHostToDevice, st));
   }
+  if (H->fp8()) {
+    // MXFP8 copies of the block projections: codes [N, K] then the scale words (ld = N), 256-byte aligned
+    struct Mat {
+      const uint16_t* src;
+      long N, K;
+      std::vector<moss_dit::Mx8>* dst;
+    };
+    std::vector<Mat> mats;
+    for (int l = 0; l < L; ++l) {
+      mats.push_back({H->qkv[l], 3 * (long)D, (long)D, &H->qkv8});
+      mats.push_back({H->out[l], (long)D, (long)D, &H->out8});
+      mats.push_back({H->gu[l], 2 * (long)F, (long)D, &H->gu8});
+      mats.push_back({H->down[l], (long)D, (long)F, &H->down8});
+    }
+    for (int l = 0; l < RL; ++l) {
+      mats.push_back({H->rqkv[l], 3 * (long)D, (long)D, &H->rqkv8});
+      mats.push_back({H->rout[l], (long)D, (long)D, &H->rout8});
+      mats.push_back({H->rgu[l], 2 * (long)F, (long)D, &H->rgu8});
+      mats.push_back({H->rdown[l], (long)D, (long)F, &H->rdown8});
+    }
+    size_t bytes8 = 0;
+    for (const Mat& m : mats) bytes8 += align_up((size_t)(m.N * m.K)) + align_up((size_t)(m.K / 128 * m.N * 4));
+    if (dev_alloc(&H->w8buf, bytes8) != hipSuccess) {
+      (void)hipGetLastError();
+      H->w8buf = nullptr;
+      if (stage) hipFree(stage);
+      stage = nullptr;
+      return bail(MOSS_ERR_OUT_OF_MEMORY, fmt("MXFP8 weight allocation of %zu bytes failed", bytes8));
+    }
+    uint8_t* c8 = (uint8_t*)H->w8buf;
+    for (const Mat& m : mats) {
+      moss_dit::Mx8 q;
+      q.codes = c8;
+      c8 += align_up((size_t)(m.N * m.K));
+      q.scales = c8;
+      c8 += align_up((size_t)(m.K / 128 * m.N * 4));
+      q.ld = m.N;
+      CREATE_TRY(launch_mx_quant(m.src, m.K, (int)m.N, (int)m.K, const_cast<uint8_t*>(q.codes),
+                                 const_cast<uint8_t*>(q.scales), m.N, st));
+      m.dst->push_back(q);
+    }
+  }
   CREATE_TRY(hipStreamSynchronize(st));
   if (stage) hipFree(stage);
   CREATE_TRY(rope_table(cfg->rope_theta, &H->rope));
@@ -964,6 +1074,7 @@ void moss_dit_destroy(moss_dit* h) {
   if (h->ws) (void)hipFree(h->ws);
   if (h->fbc.mem) (void)hipFree(h->fbc.mem);
   if (h->wbuf) (void)hipFree(h->wbuf);
+  if (h->w8buf) (void)hipFree(h->w8buf);
   for (auto& pool : h->prof_ev)
     for (auto& e : pool) {
       (void)hipEventDestroy(e.first);
@@ -1099,7 +1210,7 @@ int moss_text_refine(moss_dit* h, int32_t batch, int32_t text_len, const float* 
   }
   for (int l = 0; l < k.refiner_layers; ++l) {
     // text rows only (T = S: no RoPE), one shared unmodulated modulation vector (stride 0)
-    if ((s = run_block(h, {h->rqkv[l], h->rout[l], h->rgu[l], h->rdown[l]}, c.x, batch, T, 1, T, h->const_mod, 0, c,
+    if ((s = run_block(h, refiner_block(h, l), c.x, batch, T, 1, T, h->const_mod, 0, c,
                        nullptr, st)))
       return s;
   }
@@ -1231,6 +1342,44 @@ int moss_gemm_bf16(const void* A, const void* W, float* out, int32_t M, int32_t 
                                    (hipStream_t)stream);
   if (e != hipSuccess) {
     g_thread_error = fmt("moss_gemm_bf16 failed: %s", hipGetErrorString(e));
+    return MOSS_ERR_DEVICE;
+  }
+  return MOSS_OK;
+}
+
+int moss_mx_quantize(const void* x, int32_t rows, int32_t K, void* codes, void* scales, int64_t ld_scale,
+                     void* stream) {
+  if (!x || !codes || !scales || rows < 1 || K < 256 || K % 256 != 0 || ld_scale < rows ||
+      (reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(codes) & 15) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3)) {
+    g_thread_error = "moss_mx_quantize: need non-NULL 16-byte aligned x and codes, K % 256 == 0, ld_scale >= rows";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = launch_mx_quant((const uint16_t*)x, K, rows, K, (uint8_t*)codes, (uint8_t*)scales, ld_scale,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_thread_error = fmt("moss_mx_quantize failed: %s", hipGetErrorString(e));
+    return MOSS_ERR_DEVICE;
+  }
+  return MOSS_OK;
+}
+
+int moss_gemm_mxfp8(const void* A, const void* A_scales, int64_t lds_a, const void* W, const void* W_scales,
+                    int64_t lds_w, float* out, int32_t M, int32_t N, int32_t K, void* stream) {
+  if (!A || !A_scales || !W || !W_scales || !out || M < 1 || N < 1 || K < 1 || N % 256 != 0 || K % 256 != 0 ||
+      lds_a % 256 != 0 || lds_a < (M + 255) / 256 * 256 || lds_w % 256 != 0 || lds_w < N) {
+    g_thread_error = "moss_gemm_mxfp8: need non-NULL pointers, N % 256 == 0, K % 256 == 0, lds_a >= M rounded up "
+                     "to 256, lds_w >= N, both multiples of 256";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  GemmArgs g = gemm_args((const uint16_t*)A, (const uint16_t*)W, M, N, K, out, N);
+  g.A_scale = (const uint8_t*)A_scales;
+  g.W_scale = (const uint8_t*)W_scales;
+  g.lds_a = lds_a;
+  g.lds_w = lds_w;
+  const hipError_t e = launch_gemm_mxfp8(g, EPI_F32, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_thread_error = fmt("moss_gemm_mxfp8 failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;

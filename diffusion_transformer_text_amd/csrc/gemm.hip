@@ -397,6 +397,173 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_deep_kern
   store_tile<T, EPI>(p, acc, m0, n0, wm, wn, fr, fh);
 }
 
+// ---------------------------------------------------------------------------------------------
+// MXFP8 GEMM (the FP8 tier). One v_mfma_scale_f32_32x32x64_f8f6f4 consumes a k-tile of 64 E4M3 codes:
+// lane (row r = lane % 32, half h = lane / 32) supplies bytes 0..15 = K [16h, 16h + 16) and bytes
+// 16..31 = K [32 + 16h, 48 + 16h) of row r, i.e. 16-byte chunks h and 2 + h of the row's 64 bytes,
+// and the E8M0 scale of 32-element block h of row r (measured on the hardware with an in-bounds probe).
+//
+// A k-tile row is 64 bytes, so a 256 x 256 tile stages 32 KB per k-tile; four stages are in LDS. The
+// workgroup is four waves, one per SIMD, each computing 128 x 128 (16 accumulator blocks, 256
+// registers: the accumulators live in AGPRs). A wave double-buffers its fragments in VGPRs, so the
+// fragment reads of k-tile t + 1 are in flight while the 16 MFMAs of k-tile t run.
+//
+// Scales do not go through LDS: a lane loads its own scale words straight into VGPRs. Scales are
+// stored as 32-bit words, word (2g + h) * ld + r holding in byte q the scale of block 8g + 2q + h of
+// row r, so one word covers the four k-tiles 4g .. 4g + 3 and k-tile 4g + q picks byte q with the
+// MFMA's scale byte select. A lane's words for group g + 1 are loaded during group g.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int swzb(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// copy_barrier for vmcnt up to 63 (the count's high bits sit in bits 15:14 of the immediate)
+template <int N>
+__device__ __forceinline__ void copy_barrier64() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_mxfp8_kernel(GemmArgs p) {
+  constexpr int BM = 256, BN = 256;
+  using T = Tile<BM, BN, 2, 2>;                           // wave tile 128 x 128: TM = TN = 4
+  typedef int int8v __attribute__((ext_vector_type(8)));
+  typedef int int4v __attribute__((ext_vector_type(4)));
+  constexpr int SZ = (BM + BN) * 64;                      // bytes per stage: A rows, then W rows
+  __shared__ __attribute__((aligned(16))) uint8_t st0[SZ];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[SZ];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[SZ];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[SZ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nN = p.N / BN, nM = (p.M + BM - 1) / BM;
+  int tm, tn;
+  tile_coords(nM, nN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // copy windows: 16 rows x 64 bytes; lane i writes LDS bytes 16 i (row i / 4, physical chunk i % 4)
+  // and reads logical chunk (i % 4) ^ ((row >> 2) & 3) of its row (swzb's swizzle)
+  constexpr int PER_WAVE = BM / 16 / T::NW;               // windows per operand per wave (4)
+  constexpr int LOADS = 2 * PER_WAVE;                     // copies per wave per k-tile
+  constexpr int NSC = T::TM + T::TN;                      // scale words per lane per group
+  const int win_row = lane >> 2, win_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t a_off[PER_WAVE], w_off[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int ra = min(m0 + (wave + T::NW * j) * 16 + win_row, p.M - 1);
+    a_off[j] = (uint32_t)(ra * p.lda + win_chunk * 16);
+    const int rw = n0 + (wave + T::NW * j) * 16 + win_row;
+    w_off[j] = (uint32_t)(rw * p.ldw + win_chunk * 16);
+  }
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (int)((long)p.M * p.lda));
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, (int)((long)p.N * p.ldw));
+  const int KT = p.K / 64;
+  // k-tiles past the end (the last group's look-ahead) get an offset beyond every buffer: the range check
+  // turns such a copy into zeros written to a stage that is no longer read, without touching memory,
+  // and keeps the per-step copy count, and with it every barrier's vmcnt, the same in every step
+  auto issue = [&](int kt, uint8_t* st) {
+    const uint32_t k0 = kt < KT ? (uint32_t)(kt * 64) : 0x7fffffffu;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) buf_load_lds_16(rA, st + (wave + T::NW * j) * 1024, (int)(a_off[j] + k0));
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) buf_load_lds_16(rW, st + BM * 64 + (wave + T::NW * j) * 1024, (int)(w_off[j] + k0));
+  };
+
+
+  const int fr = lane & 31, fh = lane >> 5;
+  const int a_row0 = wm * T::WM + fr, w_row0 = wn * T::WN + fr;
+  const int G = p.K / 256;                                // k-tile groups (K % 256 == 0, checked at launch)
+  const __amdgpu_buffer_rsrc_t rSA = make_rsrc(p.A_scale, (int)(8L * G * p.lds_a));
+  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(p.W_scale, (int)(8L * G * p.lds_w));
+  const int sa_off = (fh * (int)p.lds_a + m0 + a_row0) * 4, sw_off = (fh * (int)p.lds_w + n0 + w_row0) * 4;
+  uint32_t sa[T::TM], sw[T::TN], sa_n[T::TM], sw_n[T::TN];
+  // the group offset goes into the per-lane offset, which the range check covers (group G reads zeros)
+  auto load_scales = [&](int g) {
+    const int ga = sa_off + g * 8 * (int)p.lds_a, gw = sw_off + g * 8 * (int)p.lds_w;
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) sa_n[i] = __builtin_amdgcn_raw_buffer_load_b32(rSA, ga + 128 * i, 0, 0);
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) sw_n[j] = __builtin_amdgcn_raw_buffer_load_b32(rSW, gw + 128 * j, 0, 0);
+  };
+
+  floatx16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  int8v fa[2][T::TM], fw[2][T::TN];
+  auto frag = [](const uint8_t* st, int r, int h) {
+    const int4v lo = *reinterpret_cast<const int4v*>(st + swzb(r, h));
+    const int4v hi = *reinterpret_cast<const int4v*>(st + swzb(r, 2 + h));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto load_frags = [&](const uint8_t* st, int buf) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) fa[buf][i] = frag(st, a_row0 + i * 32, fh);
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) fw[buf][j] = frag(st + BM * 64, w_row0 + j * 32, fh);
+  };
+
+  // Step t = 4g + Q: k-tile t's fragments are in buffer Q & 1 and the group's scale words in sa / sw.
+  // Wait until k-tile t + 1 has landed: issued after it are k-tiles t + 2 and t + 3 and, at Q = 1 and 2,
+  // the NSC scale loads of the next group (at Q = 3 the count holds for either issue order and only
+  // waits longer). Then copy k-tile t + 4 into k-tile t's stage (its reads finished before the barrier),
+  // read k-tile t + 1's fragments into the other buffer and run k-tile t's MFMAs. Every step has the
+  // same shape: the look-ahead past the last k-tile copies and reads nothing that is used.
+  auto step = [&](auto q_c, int t, const uint8_t* nxt, uint8_t* fill) {
+    constexpr int Q = decltype(q_c)::value;
+    copy_barrier64<2 * LOADS + ((Q == 1 || Q == 2) ? NSC : 0)>();
+    if constexpr (Q == 0) {
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i) sa[i] = sa_n[i];
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) sw[j] = sw_n[j];
+    }
+    issue(t + 4, fill);
+    if constexpr (Q == 0) load_scales(t / 4 + 1);           // group G's words are out of range: zeros
+    load_frags(nxt, (Q + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[Q & 1][j], fa[Q & 1][i], acc[i][j], 0, 0, Q,
+                                                                    (int)sw[j], Q, (int)sa[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+
+  load_scales(0);                                         // before the copies: complete at the first barrier
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  issue(3, st3);
+  copy_barrier64<3 * LOADS>();                            // k-tile 0 (and group 0's scales) have landed
+  load_frags(st0, 0);
+  for (int t = 0; t < KT; t += 4) {                       // straight-line steps, one k-tile group per trip
+    step(Q0{}, t, st1, st0);
+    step(Q1{}, t + 1, st2, st1);
+    step(Q2{}, t + 2, st3, st2);
+    step(Q3{}, t + 3, st0, st3);
+  }
+  // the look-ahead copies (zeros into unused stages) must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
+  // keep the last MFMAs here: left free, the compiler sinks them into the epilogue's row-bound branches
+  // and holds the last k-tiles' fragments live (and spilled) until then
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) asm volatile("" : "+a"(acc[i][j]));
+  store_tile<T, EPI>(p, acc, m0, n0, wm, wn, fr, fh);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t launch_tile(const GemmArgs& a, int epi, hipStream_t stream) {
   const int nM = (a.M + BM - 1) / BM, nN = a.N / BN;
@@ -466,6 +633,32 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream) {
   }
   if (a.N % 128 == 0) return launch_tile<128, 128, 2, 2>(a, epi, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_mxfp8(const GemmArgs& a, int epi, hipStream_t stream) {
+  if (a.M <= 0) return hipSuccess;
+  if ((reinterpret_cast<uintptr_t>(a.A) & 15) || (reinterpret_cast<uintptr_t>(a.W) & 15) ||
+      (reinterpret_cast<uintptr_t>(a.A_scale) & 3) || (reinterpret_cast<uintptr_t>(a.W_scale) & 3))
+    return hipErrorInvalidValue;
+  if (a.N % 256 != 0 || a.K % 256 != 0 || a.lda % 16 != 0 || a.ldw % 16 != 0 || !a.A_scale || !a.W_scale ||
+      a.lds_a % 256 != 0 || a.lds_a < (a.M + 255) / 256 * 256 || a.lds_w % 256 != 0 || a.lds_w < a.N)
+    return hipErrorInvalidValue;
+  if ((long)a.M * a.lda >= (1L << 31) || (long)a.N * a.ldw >= (1L << 31) ||
+      2L * a.K * a.lds_a / 64 >= (1L << 31) || 2L * a.K * a.lds_w / 64 >= (1L << 31))
+    return hipErrorInvalidValue;                          // buffer byte offsets must fit 31 bits
+  const int nM = (a.M + 255) / 256, nN = a.N / 256;
+  dim3 grid(nM * nN), block(256);
+#define MOSS_GEMM_LAUNCH(E) hipLaunchKernelGGL((gemm_mxfp8_kernel<E>), grid, block, 0, stream, a)
+  switch (epi) {
+    case EPI_BF16: MOSS_GEMM_LAUNCH(EPI_BF16); break;
+    case EPI_QKV_ROPE: MOSS_GEMM_LAUNCH(EPI_QKV_ROPE); break;
+    case EPI_GATED_RES: MOSS_GEMM_LAUNCH(EPI_GATED_RES); break;
+    case EPI_SWIGLU: MOSS_GEMM_LAUNCH(EPI_SWIGLU); break;
+    case EPI_F32: MOSS_GEMM_LAUNCH(EPI_F32); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOSS_GEMM_LAUNCH
+  return hipGetLastError();
 }
 
 hipError_t launch_interleave_gate_up(const uint16_t* src, uint16_t* dst, int F, int D, hipStream_t stream) {

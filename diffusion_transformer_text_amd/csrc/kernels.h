@@ -41,10 +41,18 @@ struct GemmArgs {
   int S, T, grid_w, rope_cols;
   // EPI_F32_UNPATCH
   int C, lat_h, lat_w, n_img;
+  // MXFP8 operands (launch_gemm_mxfp8): A and W hold E4M3 codes (bytes; lda / ldw in bytes); their E8M0
+  // scales are 32-bit words, word (2g + h) * ld + r holding in byte q the scale of 32-element block
+  // 8g + 2q + h of row r (ld = lds_a, lds_w in words; lds_a >= M rounded up to 256, lds_w >= N)
+  const uint8_t* A_scale;
+  const uint8_t* W_scale;
+  long lds_a, lds_w;
 };
 
 // Picks a tile shape for (M, N) and launches. Returns hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream);
+// The same product with MXFP8 operands (needs N % 256 == 0 and K % 256 == 0); same epilogues.
+hipError_t launch_gemm_mxfp8(const GemmArgs& a, int epi, hipStream_t stream);
 // Interleave W_gate_up [2F, D] = [gate rows | up rows] into 32-row groups [g0 | u0 | g1 | u1 | ...].
 hipError_t launch_interleave_gate_up(const uint16_t* src, uint16_t* dst, int F, int D, hipStream_t stream);
 
@@ -106,6 +114,14 @@ hipError_t launch_text_cast(PtrBatch text, int B, int T, int D, int S, uint16_t*
 // x = x + (sigma_next - sigma) * (v_u + cfg * (v_c - v_u)); v_u == nullptr means v = v_c.
 hipError_t launch_cfg_euler(const float* v_c, const float* v_u, float* x, long n, float cfg, float sigma,
                             float sigma_next, hipStream_t stream);
+// As above plus slg * (v_c - v_s) when v_s != nullptr (the skipped conditional prediction).
+hipError_t launch_guidance_euler(const float* v_c, const float* v_u, const float* v_s, float* x, long n, float cfg,
+                                 float slg, float sigma, float sigma_next, hipStream_t stream);
+// MXFP8 quantization (OCP MX: E4M3 codes, one E8M0 scale per 32 elements along K; K % 256 == 0):
+// x bf16 [rows, K] (row stride ldx) -> q [rows, K] bytes and the scale words of GemmArgs::A_scale with
+// ld = lds >= rows.
+hipError_t launch_mx_quant(const uint16_t* x, long ldx, int rows, int K, uint8_t* q, uint8_t* s, long lds,
+                           hipStream_t stream);
 // Step cache (First-Block Cache): r_cur = x1 - x0 (fp32); with r_prev also sums[0] = sum|r_cur - r_prev|
 // and sums[1] = sum|r_prev| (fixed-order reduction through `partial`, 2 * 1024 floats).
 hipError_t launch_fbc_change(const uint16_t* x1, const uint16_t* x0, const float* r_prev, float* r_cur, long n,
@@ -117,8 +133,5 @@ hipError_t launch_fbc_apply(uint16_t* x, const float* rest, long n, hipStream_t 
 constexpr int kFbcPartials = 1024;
 // dst = float(src) for n bf16 values (src 8-byte, dst 16-byte aligned).
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, long n, hipStream_t stream);
-// As above plus slg * (v_c - v_s) when v_s != nullptr (the skipped conditional prediction).
-hipError_t launch_guidance_euler(const float* v_c, const float* v_u, const float* v_s, float* x, long n, float cfg,
-                                 float slg, float sigma, float sigma_next, hipStream_t stream);
 
 }  // namespace moss

@@ -66,13 +66,21 @@ const char* moss_dit_last_error(const moss_dit* h);
  * Supported: head_dim == 128, hidden == num_heads * 128, hidden % 256 == 0, hidden <= 4096,
  * ffn_hidden % 64 == 0, temb_dim == 256, patch == 2, 1 <= num_layers <= 64, qk_norm == 0,
  * text_dim % 64 == 0 and 64 <= text_dim <= 16384, 0 <= refiner_layers <= 8;
- * anything else -> MOSS_ERR_NOT_SUPPORTED. */
+ * anything else -> MOSS_ERR_NOT_SUPPORTED.
+ * gemm_precision = 1 selects the FP8 tier (lossy: the pages' "high/turbo" tiers run FP8 GEMMs, MossInfer
+ * integration guide "Quality tier", Qwen-Image 2.1 cookbook "Online FP8"): the four projections of
+ * every joint block (DiT and text refiner) quantize both operands to OCP MXFP8 -- E4M3 with one
+ * power-of-two scale per 32 elements along the reduction axis, weights once at creation, activations
+ * on the fly -- and run on the scaled FP8 matrix cores with fp32 accumulation; everything else stays
+ * as in the bf16 tier. Needs ffn_hidden % 256 == 0. The pages' tiers use channel- or tensor-wise
+ * scales; the block format is the one gfx950's FP8 matrix instruction applies in hardware. */
 typedef struct {
   uint32_t struct_size;
   int32_t num_layers, hidden, num_heads, head_dim, ffn_hidden, latent_channels, patch, temb_dim, qk_norm;
   float rope_theta, norm_eps, flow_multiplier;
   int32_t text_dim;                /* width of the text encoder's states (input of the text refiner)   */
   int32_t refiner_layers;          /* text-only blocks after the text projection                       */
+  int32_t gemm_precision;          /* block projections: 0 = bf16 (default), 1 = MXFP8 (lossy FP8 tier) */
 } moss_dit_config;
 void moss_dit_config_init(moss_dit_config* c, uint32_t size);
 

@@ -63,6 +63,30 @@ int moss_gemm_bf16(const void* A, const void* W, float* out, int32_t M, int32_t 
  *   6 gate/up GEMM + SiLU*mul                    7 down GEMM + gated residual
  *   8 final layer (LN-mod + output GEMM)         9 CFG + Euler */
 #define MOSS_PROF_CLASSES 10
+/* FP8 tier ("MOSS-Image" SGLang cookbook, "3. Guidance and precision", and the MossInfer integration
+ * guide, "Quality tier": lossy FP8 GEMM tiers; the Qwen-Image 2.1 cookbook, "Online FP8", quantizes
+ * weights and activations on the fly). Format: OCP microscaling MXFP8 -- E4M3 codes and one E8M0
+ * (power-of-two) scale per 32 consecutive elements of the reduction axis, scale exponent
+ * floor(log2(block amax)) - 8, elements rounded to nearest even and saturated at +-448, an all-zero
+ * block taking exponent -127. The pages' FP8 tiers use channel- or tensor-wise scales on their
+ * hardware; the block format is what gfx950's scaled FP8 MFMA applies natively.
+ *
+ * Scale storage ("scale words"): uint32 words, word (2g + h) * ld + r holding in byte q (low byte
+ * first) the biased exponent (exponent + 127) of block 8g + 2q + h of row r, for g < K / 256, h < 2,
+ * q < 4: K / 128 * ld words in all.
+ *
+ * Quantize x (device bf16 [rows, K], 16-byte aligned) to codes (device uint8 [rows, K], E4M3 bytes,
+ * 16-byte aligned) and scale words (device, ld_scale >= rows). K % 256 == 0, rows >= 1. */
+int moss_mx_quantize(const void* x, int32_t rows, int32_t K, void* codes, void* scales, int64_t ld_scale,
+                     void* stream);
+
+/* MXFP8 GEMM with an fp32 output: out[m, n] = sum_k a(m, k) w(n, k), a and w the MXFP8 values of A
+ * (codes [M, K], scale words with ld = lds_a) and W (codes [N, K], scale words with ld = lds_w), fp32
+ * accumulation. N % 256 == 0, K % 256 == 0, lds_a >= M rounded up to 256 (the scale words of rows
+ * M .. that bound are read, their products discarded), lds_w >= N, both multiples of 256. */
+int moss_gemm_mxfp8(const void* A, const void* A_scales, int64_t lds_a, const void* W, const void* W_scales,
+                    int64_t lds_w, float* out, int32_t M, int32_t N, int32_t K, void* stream);
+
 int moss_dit_profile_enable(moss_dit* h, int32_t enable);
 /* Synchronises the device, writes the summed milliseconds and the launch count of each class since
  * the last read (host arrays of MOSS_PROF_CLASSES), and resets the counters. */

@@ -47,6 +47,8 @@ FULL = Shape()
 # Tiny single-stream DiT: 2 blocks, hidden 256, 2 heads x 128, FFN 704 (the 8/3 rule rounded up to a
 # multiple of 64), 32 latent channels, 2x2 patches.
 TINY = Shape(num_layers=2, hidden=256, num_heads=2, head_dim=128, ffn_hidden=704, text_dim=320)
+# the FP8 tier works on whole 256-element k-tile groups: its tiny shape widens the FFN to 768
+TINY_FP8 = Shape(num_layers=2, hidden=256, num_heads=2, head_dim=128, ffn_hidden=768, text_dim=320)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -130,11 +132,11 @@ def make_sampling_inputs(shape: Shape, latent_h: int, latent_w: int, text_len: i
     return SamplingInputs(latents, text_cond, np.zeros_like(text_cond))
 
 
-def tiny_workload(mod_scale: float = 1.0, seed: int = 0):
+def tiny_workload(mod_scale: float = 1.0, seed: int = 0, shape: Shape = TINY):
     """Tiny 2-block DiT, 16x16 latent (64 image tokens) + 32 text tokens, seed 0."""
     rng = np.random.default_rng(seed)
-    w = make_weights(TINY, rng=rng, mod_scale=mod_scale)
-    inp = make_sampling_inputs(TINY, 16, 16, 32, rng)
+    w = make_weights(shape, rng=rng, mod_scale=mod_scale)
+    inp = make_sampling_inputs(shape, 16, 16, 32, rng)
     return w, inp
 
 

@@ -1,0 +1,238 @@
+"""The FP8 tier (gemm_precision = 1: the four projections of every joint block on MXFP8 operands) on
+the GPU, against the oracle run with gemm_precision "mxfp8".
+
+* Tiny: 2 blocks, hidden 256, 2 heads x 128, FFN 768 (the tier needs FFN % 256 == 0), 16x16 latent
+  (64 image tokens) + 32 text tokens, seed 0, modulation weights x1 and x50. One block stage by stage
+  (each stage from the GPU's previous one) and whole; the forward of a CFG pair (the unconditional row
+  skipping block 1); the text refiner (320-wide states, two text-only blocks); and the drift of the
+  FP8 forward from the bf16 forward of the same weights, which is the tier's loss.
+* Full size: one joint block (hidden 3072, 24 heads, FFN 8192, batch 2, 256 text + 4096 image tokens)
+  on sampled rows against the oracle's MXFP8 block from the same input.
+
+The projections' own error bound: the scaled FP8 MFMA's result on identical MXFP8 operands deviates
+from the exact product by a relative L2 of about 1.4e-5 (it does not sum a 64-product k-tile in
+fp32), so a branch output computed from the GPU's own input is held to 5e-5.
+
+Quantities the oracle computes through its own chain of quantized activations (a branch output, a
+block's update, the difference of two passes) carry rounding noise amplified by the E4M3 grid: an
+activation that differs from the oracle's by delta crosses an E4M3 rounding boundary with probability
+about delta / u (u = 1/16, the E4M3 unit) and then moves by u, an rms change of sqrt(delta * u). With
+delta one bf16 unit (1/256) that is 4 x the bf16 tier's rounding noise, so those comparisons take
+4 x the bf16 tier's bound.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_util import REL_L2_BF16, dev_bf16, dev_weights, host_bf16, log, oracle_cfg, rel_l2
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+dt = pytest.importorskip("diffusion_transformer_text_amd")
+
+MODES = [1.0, 50.0]
+REL_L2_MX_GEMM = 5e-5
+REL_L2_FP8_CHAIN = 4 * REL_L2_BF16
+
+
+def mx(a):
+    return O.mx_dequantize(a)
+
+
+def _cfg(shape, precision):
+    return dt.moss_dit_config_init(num_layers=shape.num_layers, hidden=shape.hidden, num_heads=shape.num_heads,
+                                   ffn_hidden=shape.ffn_hidden, text_dim=shape.text_dim,
+                                   refiner_layers=shape.refiner_layers, gemm_precision=precision)
+
+
+_cache = {}
+
+
+def tiny(mod_scale, precision=1):
+    key = (mod_scale, precision)
+    if key not in _cache:
+        log(f"create tiny FP8-shape model mod_scale={mod_scale} precision={precision}")
+        s = synth.TINY_FP8
+        w, inp = synth.tiny_workload(mod_scale=mod_scale, shape=s)
+        rw = synth.refiner_weights(s, seed=100)
+        d = dev_weights(w, torch)
+        d["text_proj_w"] = dev_bf16(rw["text_proj_w"], torch)
+        for k in ("refiner_qkv_w", "refiner_out_w", "refiner_gate_up_w", "refiner_down_w"):
+            d[k] = [dev_bf16(a, torch) for a in rw[k]]
+        cfg = _cfg(s, precision)
+        W = O.weights_to_f64(w)
+        W["text_proj_w"] = O.from_bf16_bits(rw["text_proj_w"])
+        for k in ("refiner_qkv_w", "refiner_out_w", "refiner_gate_up_w", "refiner_down_w"):
+            W[k] = [O.from_bf16_bits(a) for a in rw[k]]
+        _cache[key] = (dt.MossDiT(cfg, d), inp, W, oracle_cfg(cfg))
+    return _cache[key]
+
+
+def test_oracle_cfg_carries_the_tier():
+    assert oracle_cfg(_cfg(synth.TINY_FP8, 1)).gemm_precision == "mxfp8"
+    assert oracle_cfg(_cfg(synth.TINY_FP8, 0)).gemm_precision == "bf16"
+
+
+@pytest.mark.parametrize("mod_scale", MODES)
+def test_fp8_block_stages_vs_oracle(mod_scale):
+    m, inp, W, ocfg = tiny(mod_scale)
+    D, F, T, gh, gw = ocfg.hidden, ocfg.ffn_hidden, 32, 8, 8
+    S, B = T + gh * gw, 2
+    rng = np.random.default_rng(5)
+    xbits = synth.bf16_normal_bits(rng, (B, S, D))
+    x = dev_bf16(xbits, torch)
+    mod = torch.empty((B, m.mod_stride), dtype=torch.bfloat16, device="cuda")
+    m.moss_dit_modulation([0.8, 0.3], mod)
+    M = B * S
+    taps = {k: torch.empty((M, n), dtype=t, device="cuda") for k, n, t in
+            [("a", D, torch.bfloat16), ("qkv", 3 * D, torch.bfloat16), ("o", D, torch.bfloat16),
+             ("attn", D, torch.float32), ("x1", D, torch.bfloat16), ("a2", D, torch.bfloat16),
+             ("h", F, torch.bfloat16), ("ffn", D, torch.float32)]}
+    layer = 1
+    log(f"fp8 block taps layer={layer} mod_scale={mod_scale}")
+    m.moss_dit_block(layer, x, T, gh, gw, mod, taps=taps)
+    torch.cuda.synchronize()
+    g = {k: (host_bf16(v) if v.dtype == torch.bfloat16 else v.cpu().numpy().astype(np.float64)) for k, v in taps.items()}
+    x0 = O.from_bf16_bits(xbits).reshape(M, D)
+    modv = host_bf16(mod)
+    wq, wo = mx(W["qkv_w"][layer]), mx(W["out_w"][layer])
+    wgu, wd = mx(W["gate_up_w"][layer]), mx(W["down_w"][layer])
+    errs = {}
+    for b in range(B):
+        rs = slice(b * S, (b + 1) * S)
+        mb = modv[b, layer * 6 * D:(layer + 1) * 6 * D].reshape(6, D)
+        errs.setdefault("a", []).append(rel_l2(g["a"][rs], O.bf16_round(O.ln_modulate(x0[rs], mb[0], mb[1], 1e-6))))
+        qkv = O.bf16_round(mx(g["a"][rs]) @ wq.T)
+        q = O.bf16_round(O.rope_rows(qkv[:, :D], T, gw, 128, 1e4))
+        k = O.bf16_round(O.rope_rows(qkv[:, D:2 * D], T, gw, 128, 1e4))
+        errs.setdefault("qkv", []).append(rel_l2(g["qkv"][rs], np.concatenate([q, k, qkv[:, 2 * D:]], 1)))
+        gq = g["qkv"][rs]
+        errs.setdefault("o", []).append(rel_l2(g["o"][rs], O.attention(gq[:, :D], gq[:, D:2 * D], gq[:, 2 * D:], 2, 128)))
+        errs.setdefault("attn", []).append(rel_l2(g["attn"][rs], mx(g["o"][rs]) @ wo.T))
+        errs.setdefault("x1", []).append(rel_l2(g["x1"][rs], O.bf16_round(x0[rs] + mb[2] * g["attn"][rs])))
+        errs.setdefault("a2", []).append(rel_l2(g["a2"][rs], O.bf16_round(O.ln_modulate(g["x1"][rs], mb[3], mb[4], 1e-6))))
+        gu = mx(g["a2"][rs]) @ wgu.T
+        errs.setdefault("h", []).append(rel_l2(g["h"][rs], O.bf16_round(O.silu(gu[:, :F]) * gu[:, F:])))
+        errs.setdefault("ffn", []).append(rel_l2(g["ffn"][rs], mx(g["h"][rs]) @ wd.T))
+        taps_o = {}
+        ref = O.block(x0[rs], mb, W, layer, ocfg, T, gw, mirror=True, taps=taps_o)
+        errs.setdefault("block", []).append(rel_l2(host_bf16(x).reshape(M, D)[rs], ref))
+        errs.setdefault("attn_branch", []).append(rel_l2(g["attn"][rs], taps_o["attn_out"]))
+        errs.setdefault("ffn_branch", []).append(rel_l2(g["ffn"][rs], taps_o["ffn_out"]))
+    log({k: f"{max(v):.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        tol = REL_L2_MX_GEMM if k in ("attn", "ffn") else REL_L2_BF16
+        assert max(v) <= tol, (k, v)
+
+
+def _forward(m, inp, sigma, skip):
+    lat = torch.from_numpy(np.concatenate([inp.latents, inp.latents])).cuda()
+    txt = torch.from_numpy(np.concatenate([inp.text_cond, inp.text_uncond])).cuda()
+    vel = torch.empty_like(lat)
+    m.moss_dit_forward(lat, txt, sigma, vel, skip_mask=skip)
+    torch.cuda.synchronize()
+    return vel.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("mod_scale", MODES)
+def test_fp8_forward_vs_oracle(mod_scale):
+    m, inp, W, ocfg = tiny(mod_scale)
+    log(f"fp8 tiny forward mod_scale={mod_scale}")
+    v = _forward(m, inp, [0.6, 0.6], [0, 1 << 1])
+    lat = np.concatenate([inp.latents, inp.latents]).astype(np.float64)
+    txt = np.concatenate([inp.text_cond, inp.text_uncond]).astype(np.float64)
+    ref = O.forward(lat, txt, [0.6, 0.6], W, ocfg, skip=[set(), {1}], mirror=True)
+    e_v = rel_l2(v, ref)
+    e_d = rel_l2(v[0] - v[1], ref[0] - ref[1])
+    log(f"rel-L2 v {e_v:.3e}  (v_c - v_u) {e_d:.3e}")
+    assert e_v <= REL_L2_BF16
+    # v_c - v_u is the small effect of one skipped block: its error is the two passes' rounding noise
+    assert e_d <= REL_L2_FP8_CHAIN * (5 if mod_scale == 1.0 else 1)
+
+
+@pytest.mark.parametrize("mod_scale", MODES)
+def test_fp8_drift_from_bf16(mod_scale):
+    """The tier's loss: FP8 against bf16 forward of the same weights (a report with a loose bound)."""
+    m8, inp, _, _ = tiny(mod_scale, 1)
+    m16, _, _, _ = tiny(mod_scale, 0)
+    v8 = _forward(m8, inp, [0.6, 0.6], [0, 1 << 1])
+    v16 = _forward(m16, inp, [0.6, 0.6], [0, 1 << 1])
+    e_v = rel_l2(v8, v16)
+    e_d = rel_l2(v8[0] - v8[1], v16[0] - v16[1])
+    log(f"fp8 vs bf16 forward mod_scale={mod_scale}: rel-L2 v {e_v:.3e}  (v_c - v_u) {e_d:.3e}")
+    assert 0 < e_v < 0.1
+
+
+def test_fp8_text_refiner_vs_oracle():
+    m, _, W, ocfg = tiny(1.0)
+    rng = np.random.default_rng(41)
+    B, T = 2, 32
+    enc = rng.standard_normal((B, T, ocfg.text_dim)).astype(np.float32)
+    log(f"fp8 refiner B={B} T={T}")
+    out = torch.empty((B, T, ocfg.hidden), dtype=torch.float32, device="cuda")
+    m.moss_text_refine(torch.from_numpy(enc).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        ref = O.text_refine(enc[b].astype(np.float64), W, ocfg, mirror=True)
+        assert rel_l2(got[b], ref) <= REL_L2_BF16
+
+
+# ------------------------------------------------------------------------------------------------
+# full size
+# ------------------------------------------------------------------------------------------------
+
+FT, FGH, FGW = 256, 64, 64
+FS = FT + FGH * FGW
+
+
+@pytest.mark.timeout(600)
+def test_fp8_full_block_sampled_rows():
+    log(f"fp8 full block: D=3072 F=8192 H=24, B=2, S={FS}")
+    shape = synth.Shape(num_layers=1)
+    w = synth.torch_weights(shape, seed=3, device="cuda", mod_scale=50.0)
+    cfg = dt.moss_dit_config_init(num_layers=1, gemm_precision=1)
+    model = dt.MossDiT(cfg, w)
+    ocfg = oracle_cfg(cfg)
+    D, F = ocfg.hidden, ocfg.ffn_hidden
+    rng = np.random.default_rng(12)
+    B = 2
+    xbits = synth.bf16_normal_bits(rng, (B, FS, D))
+    sig = synth.uniform_f32(rng, (B,))
+    x = dev_bf16(xbits, torch)
+    mod = torch.empty((B, model.mod_stride), dtype=torch.bfloat16, device="cuda")
+    model.moss_dit_modulation([float(s) for s in sig], mod)
+    M = B * FS
+    taps = {k: torch.empty((M, n), dtype=t, device="cuda") for k, n, t in
+            [("o", D, torch.bfloat16), ("attn", D, torch.float32),
+             ("h", F, torch.bfloat16), ("ffn", D, torch.float32)]}
+    model.moss_dit_block(0, x, FT, FGH, FGW, mod, taps=taps)
+    torch.cuda.synchronize()
+    W = {"qkv_w": [host_bf16(w["qkv_w"][0])], "out_w": [host_bf16(w["out_w"][0])],
+         "gate_up_w": [host_bf16(w["gate_up_w"][0])], "down_w": [host_bf16(w["down_w"][0])]}
+    wo, wd = mx(W["out_w"][0]), mx(W["down_w"][0])
+    modv = host_bf16(mod)
+    x_out = host_bf16(x).reshape(B, FS, D)
+    g = {k: (host_bf16(v) if v.dtype == torch.bfloat16 else v.cpu().numpy().astype(np.float64)).reshape(B, FS, -1)
+         for k, v in taps.items()}
+    x0 = O.from_bf16_bits(xbits)
+    errs = {}
+    for b in range(B):
+        mb = modv[b, :6 * D].reshape(6, D)
+        rows = np.unique(np.concatenate([rng.integers(0, FS, 16), [0, FT - 1, FT, FS - 1]]))
+        errs.setdefault("out_proj", []).append(rel_l2(g["attn"][b][rows], mx(g["o"][b][rows]) @ wo.T))
+        errs.setdefault("down_proj", []).append(rel_l2(g["ffn"][b][rows], mx(g["h"][b][rows]) @ wd.T))
+        taps_o = {}
+        ref = O.block(x0[b], mb, W, 0, ocfg, FT, FGW, mirror=True, rows=rows, taps=taps_o)
+        errs.setdefault("block", []).append(rel_l2(x_out[b][rows], ref))
+        errs.setdefault("block_update", []).append(rel_l2(x_out[b][rows] - x0[b][rows], ref - x0[b][rows]))
+        errs.setdefault("attn_branch", []).append(rel_l2(g["attn"][b][rows], taps_o["attn_out"]))
+        errs.setdefault("ffn_branch", []).append(rel_l2(g["ffn"][b][rows], taps_o["ffn_out"]))
+    log({k: f"{max(v):.2e}" for k, v in errs.items()})
+    model.close()
+    for k, v in errs.items():
+        tol = {"out_proj": REL_L2_MX_GEMM, "down_proj": REL_L2_MX_GEMM, "block": REL_L2_BF16}.get(k, REL_L2_FP8_CHAIN)
+        assert max(v) <= tol, (k, v)
