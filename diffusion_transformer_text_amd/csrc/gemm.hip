@@ -523,17 +523,40 @@ __global__ __launch_bounds__(256, 1) void gemm_mxfp8_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < T::TN; ++j) sw[j] = sw_n[j];
     }
-    issue(t + 4, fill);
-    if constexpr (Q == 0) load_scales(t / 4 + 1);           // group G's words are out of range: zeros
-    load_frags(nxt, (Q + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
+    // The 16 MFMAs are interleaved with the step's memory instructions, one MFMA then the next copy
+    // (8), scale load (group start only) and fragment half (16), so the single wave of this SIMD keeps
+    // its MFMA pipe fed while it issues them.
+    const uint32_t k0 = t + 4 < KT ? (uint32_t)((t + 4) * 64) : 0x7fffffffu;
+    constexpr int NB = (Q + 1) & 1;
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < T::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[Q & 1][j], fa[Q & 1][i], acc[i][j], 0, 0, Q,
-                                                                    (int)sw[j], Q, (int)sa[i]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int n = 0; n < 16; ++n) {
+      const int i = n >> 2, j = n & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[Q & 1][j], fa[Q & 1][i], acc[i][j], 0, 0, Q,
+                                                                  (int)sw[j], Q, (int)sa[i]);
+      if (n < PER_WAVE) {
+        buf_load_lds_16(rA, fill + (wave + T::NW * n) * 1024, (int)(a_off[n] + k0));
+      } else if (n < 2 * PER_WAVE) {
+        const int jj = n - PER_WAVE;
+        buf_load_lds_16(rW, fill + BM * 64 + (wave + T::NW * jj) * 1024, (int)(w_off[jj] + k0));
+      } else if (Q == 0) {
+        const int m = n - 2 * PER_WAVE;                     // group G's words are out of range: zeros
+        if (m < T::TM)
+          sa_n[m] = __builtin_amdgcn_raw_buffer_load_b32(rSA, sa_off + (t / 4 + 1) * 8 * (int)p.lds_a + 128 * m, 0, 0);
+        else
+          sw_n[m - T::TM] = __builtin_amdgcn_raw_buffer_load_b32(rSW, sw_off + (t / 4 + 1) * 8 * (int)p.lds_w +
+                                                                     128 * (m - T::TM), 0, 0);
+      }
+      const int o = n >> 1, h = n & 1;                      // fragment o (A 0..3, W 4..7), half h
+      if (o < T::TM) {
+        const int4v v = *reinterpret_cast<const int4v*>(nxt + swzb(a_row0 + o * 32, 2 * h + fh));
+        if (h == 0) fa[NB][o].lo = v; else fa[NB][o].hi = v;
+      } else {
+        const int4v v = *reinterpret_cast<const int4v*>(nxt + BM * 64 + swzb(w_row0 + (o - T::TM) * 32, 2 * h + fh));
+        if (h == 0) fw[NB][o - T::TM].lo = v; else fw[NB][o - T::TM].hi = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   using Q0 = std::integral_constant<int, 0>;
   using Q1 = std::integral_constant<int, 1>;
