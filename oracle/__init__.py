@@ -39,6 +39,14 @@ Parity status of each function (pins in tests/test_oracle_pins.py):
   truncation)                 blocks' gate rows zeroed (bitwise); slg 0 / empty skip list / outside
                               the window give the two-pass step bitwise; a truncated step equals the
                               CFG-1 step bitwise
+  int8_codes, q8_quantize_q,  pinned: hand codes (half-even ties, the amax row at +-127, zero rows),
+  q8_quantize_k,              per-block amax of K blocks of different magnitude, E4M3 codes of V
+  fp8_quantize_v              channels (amax channel at +-448)
+  attention_q8                pinned: with exact probabilities it equals the exact softmax of the
+                              dequantized operands (the pinned attention above), ragged last block;
+                              V constant over keys and a single key give V exactly (convex weights);
+                              a dominant key selects its V row; within a few percent of the exact
+                              attention on random inputs
 """
 from .moss_oracle import *  # noqa: F401,F403
 from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, embed, euler_step,  # noqa
@@ -46,5 +54,7 @@ from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, emb
                           modulation, negative_pass_runs, text_refine, StepCache,
                           first_block_change, forward_cached, sample_step_cached,
                           e4m3_round, mx_quantize, mx_dequantize, E4M3_MAX, projection,
+                          attention_q8, q8_quantize_q, q8_quantize_k, fp8_quantize_v, int8_codes,
+                          Q8_KEY_BLOCK,
                           patchify, rope_angles, apply_rope, rope_rows, sample_step, sigmas, silu,
                           slg_active, time_features, unpatchify, weights_to_f64)

@@ -305,6 +305,94 @@ def mx_dequantize(x: np.ndarray, block: int = 32) -> np.ndarray:
     return (q.reshape(q.shape[:-1] + (K // block, block)) * np.ldexp(1.0, ex)[..., None]).reshape(q.shape)
 
 
+# ----------------------------------------------------------------------------------------------
+# FP8 tier: 8-bit attention (Q K^T on INT8 codes, P V on FP8 E4M3 codes)
+# ----------------------------------------------------------------------------------------------
+# The pages name 8-bit attention modes (q8_fp8: 8-bit Q and K, FP8 P V; fp32-accumulating variants;
+# MossInfer integration guide, "Quality tier" and the feature table's attention modes) and give no
+# formula. Reading, step by step below: Q symmetric INT8 per token and head, K symmetric INT8 per
+# block of 64 consecutive keys and head, V FP8 E4M3 per channel (head dimension) with scale amax/448;
+# the integer dot products are exact, the softmax runs online over the 64-key blocks in order with
+# the exact running max, each block's probabilities are rounded to E4M3 on the scale 448 (p <= 1 maps
+# to <= 448), and the normaliser sums the same rounded probabilities, so the output is a convex
+# combination of the dequantized V rows. Codes are decided in float32 (x * 127 and x * 448 are exact
+# for bf16 inputs; one correctly rounded division), as the GPU decides them.
+
+Q8_KEY_BLOCK = 64
+
+
+def int8_codes(x32: np.ndarray, amax32) -> np.ndarray:
+    """rint(x * 127 / amax) with float32 operations (round half to even); all-zero input gives zeros."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    amax32 = np.asarray(amax32, dtype=np.float32)
+    safe = np.where(amax32 > 0, amax32, np.float32(1.0))
+    return np.rint((x32 * np.float32(127.0)) / safe).astype(np.float64)
+
+
+def q8_quantize_q(q: np.ndarray):
+    """Per-row INT8 of q [S, d]: codes [S, d] and the row amax [S] (dequantized q = code * amax / 127)."""
+    q32 = np.asarray(q, dtype=np.float32)
+    amax = np.abs(q32).max(axis=1)
+    return int8_codes(q32, amax[:, None]), amax.astype(np.float64)
+
+
+def q8_quantize_k(k: np.ndarray, block: int = Q8_KEY_BLOCK):
+    """INT8 of k [S, d] per block of `block` consecutive rows: codes [S, d], block amax [ceil(S/block)]."""
+    k32 = np.asarray(k, dtype=np.float32)
+    S = k32.shape[0]
+    nb = (S + block - 1) // block
+    codes = np.zeros(k32.shape, dtype=np.float64)
+    amax = np.zeros(nb, dtype=np.float64)
+    for t in range(nb):
+        blk = k32[t * block:(t + 1) * block]
+        a = np.abs(blk).max()
+        amax[t] = a
+        codes[t * block:(t + 1) * block] = int8_codes(blk, a)
+    return codes, amax
+
+
+def fp8_quantize_v(v: np.ndarray):
+    """Per-channel E4M3 of v [S, d]: codes e4m3_round(v * 448 / amax_channel) (float32 ops), amax [d]."""
+    v32 = np.asarray(v, dtype=np.float32)
+    amax = np.abs(v32).max(axis=0)
+    safe = np.where(amax > 0, amax, np.float32(1.0))
+    codes = e4m3_round(((v32 * np.float32(E4M3_MAX)) / safe[None, :]).astype(np.float64))
+    return codes, amax.astype(np.float64)
+
+
+def attention_q8(q: np.ndarray, k: np.ndarray, v: np.ndarray, num_heads: int, head_dim: int,
+                 quantize_p: bool = True) -> np.ndarray:
+    """8-bit attention per head (reading above). q [Sq, H*d], k/v [Sk, H*d] -> [Sq, H*d].
+    quantize_p=False keeps the probabilities exact (the same online algorithm, for the pins)."""
+    out = np.zeros((q.shape[0], num_heads * head_dim), dtype=np.float64)
+    scale = 1.0 / math.sqrt(head_dim)
+    Sk = k.shape[0]
+    nb = (Sk + Q8_KEY_BLOCK - 1) // Q8_KEY_BLOCK
+    for h in range(num_heads):
+        sl = slice(h * head_dim, (h + 1) * head_dim)
+        qc, qa = q8_quantize_q(q[:, sl])
+        kc, ka = q8_quantize_k(k[:, sl])
+        vc, va = fp8_quantize_v(v[:, sl])
+        v_hat = vc * (va / E4M3_MAX)[None, :]
+        Sq = q.shape[0]
+        m = np.full(Sq, -np.inf)
+        o = np.zeros((Sq, head_dim))
+        l = np.zeros(Sq)
+        for t in range(nb):
+            ks = slice(t * Q8_KEY_BLOCK, min((t + 1) * Q8_KEY_BLOCK, Sk))
+            s = (qc @ kc[ks].T) * (qa / 127.0)[:, None] * (ka[t] / 127.0) * scale
+            m_new = np.maximum(m, s.max(axis=1))
+            alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
+            p = np.exp(s - m_new[:, None])
+            if quantize_p:
+                p = e4m3_round(p * E4M3_MAX) / E4M3_MAX
+            o = o * alpha[:, None] + p @ v_hat[ks]
+            l = l * alpha + p.sum(axis=1)
+            m = m_new
+        out[:, sl] = o / l[:, None]
+    return out
+
+
 def projection(a: np.ndarray, w: np.ndarray, cfg: "Config") -> np.ndarray:
     """a w^T of a block projection: bf16 operands as they are, or both operands MXFP8-quantized along
     the reduction axis (the FP8 tier)."""

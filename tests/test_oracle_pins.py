@@ -788,3 +788,82 @@ def test_page_dimensions():
     assert round(params * 2 / 1e9) == a["dit_bf16_gb_about"]
     # a two-matrix GELU FFN of 8192 would give ~3.9B: the SwiGLU reading is the one that reaches 5B
     assert round(cfg.num_layers * (4 * D * D + 2 * D * F) / 1e9) != a["dit_params_billion"]
+
+
+# ------------------------------------------------------------------------------------------------
+# FP8 tier: 8-bit attention (INT8 Q K^T, FP8 P V)
+# ------------------------------------------------------------------------------------------------
+
+def test_int8_codes_by_hand():
+    # amax 1: 0.5 * 127 = 63.5 -> 64 (tie to even), 0.25 * 127 = 31.75 -> 32, the amax element -> -127
+    q = np.array([[0.5, -1.0, 0.25, 0.0], [0.0, 0.0, 0.0, 0.0], [3.0, 1.5, -0.75, 0.1015625]])
+    codes, amax = O.q8_quantize_q(q)
+    assert codes[0].tolist() == [64.0, -127.0, 32.0, 0.0]
+    assert codes[1].tolist() == [0.0, 0.0, 0.0, 0.0] and amax[1] == 0.0
+    # amax 3: 1.5 * 127 / 3 = 63.5 -> 64; -0.75 * 127 / 3 = -31.75 -> -32; 0.1015625 * 127 / 3 = 4.2995.. -> 4
+    assert codes[2].tolist() == [127.0, 64.0, -32.0, 4.0] and amax[2] == 3.0
+    assert np.abs(codes).max() <= 127
+
+
+def test_q8_key_blocks_and_v_channels():
+    rng = np.random.default_rng(70)
+    k = rng.standard_normal((100, 8))
+    k[64:] *= 100.0                                    # the second block is 100x larger
+    codes, amax = O.q8_quantize_k(k)
+    assert amax.shape == (2,)
+    assert amax[0] == np.abs(k[:64].astype(np.float32)).max() and amax[1] == np.abs(k[64:].astype(np.float32)).max()
+    assert np.abs(codes[:64]).max() == 127 and np.abs(codes[64:]).max() == 127   # each block uses the full range
+    err = np.abs(codes * np.repeat(amax, [64, 36])[:, None] / 127 - k)
+    assert np.all(err[:64] <= 0.5 * amax[0] / 127 * (1 + 1e-6)) and np.all(err[64:] <= 0.5 * amax[1] / 127 * (1 + 1e-6))
+    v = rng.standard_normal((50, 4))
+    vc, va = O.fp8_quantize_v(v)
+    assert np.all(np.abs(vc).max(axis=0) == O.E4M3_MAX)                            # each channel's amax -> 448
+    np.testing.assert_array_equal(vc, O.e4m3_round(vc))                            # valid E4M3 values
+    rel = np.abs(vc * va / O.E4M3_MAX - v) / np.abs(v)
+    assert np.all(rel[np.abs(v) > va / 64] <= 2.0 ** -4 * (1 + 1e-6))             # half an E4M3 unit (3 bits)
+
+
+def test_q8_attention_exact_probabilities_is_softmax_of_dequantized_operands():
+    # with the probability rounding switched off, the online block algorithm must reproduce the exact
+    # softmax attention (the pinned oracle above) of the dequantized q, k, v; Sk = 150 leaves a ragged block
+    rng = np.random.default_rng(71)
+    H, d, Sq, Sk = 2, 16, 7, 150
+    q = rng.standard_normal((Sq, H * d)) * 2.0
+    k = rng.standard_normal((Sk, H * d)) * 2.0
+    v = rng.standard_normal((Sk, H * d))
+    got = O.attention_q8(q, k, v, H, d, quantize_p=False)
+    deq = lambda c, a: c * a / 127.0
+    qd, kd, vd = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(H):
+        sl = slice(h * d, (h + 1) * d)
+        c, a = O.q8_quantize_q(q[:, sl]); qd[:, sl] = deq(c, a[:, None])
+        c, a = O.q8_quantize_k(k[:, sl]); kd[:, sl] = deq(c, np.repeat(a, [64, 64, 22])[:, None])
+        c, a = O.fp8_quantize_v(v[:, sl]); vd[:, sl] = c * a[None, :] / O.E4M3_MAX
+    np.testing.assert_allclose(got, O.attention(qd, kd, vd, H, d), rtol=1e-12, atol=1e-12)
+
+
+def test_q8_attention_convex_weights_and_selection():
+    rng = np.random.default_rng(72)
+    H, d = 1, 16
+    q = rng.standard_normal((5, d))
+    k = rng.standard_normal((130, d))
+    vrow = O.bf16_round(rng.standard_normal(d))        # bf16 inputs, as the GPU gets them
+    v = np.tile(vrow, (130, 1))                        # V constant over keys: amax = |v| -> codes +-448, exact
+    np.testing.assert_allclose(O.attention_q8(q, k, v, H, d), np.tile(vrow, (5, 1)), rtol=1e-12)
+    np.testing.assert_allclose(O.attention_q8(q, k[:1], v[:1], H, d), np.tile(vrow, (5, 1)), rtol=1e-12)
+    # one key far above the rest: its probability is 1, the others round to 0 in E4M3 -> its V row
+    k2 = rng.standard_normal((70, d)) * 0.01
+    k2[37] = q[0] * 40.0
+    v2 = rng.standard_normal((70, d))
+    vc, va = O.fp8_quantize_v(v2)
+    np.testing.assert_allclose(O.attention_q8(q[:1], k2, v2, H, d)[0], vc[37] * va / O.E4M3_MAX, rtol=1e-12)
+
+
+def test_q8_attention_is_close_to_exact():
+    rng = np.random.default_rng(73)
+    H, d, S = 2, 128, 200
+    q, k, v = (rng.standard_normal((S, H * d)) for _ in range(3))
+    exact = O.attention(q, k, v, H, d)
+    got = O.attention_q8(q, k, v, H, d)
+    rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
+    assert 1e-4 < rel < 0.05, rel
