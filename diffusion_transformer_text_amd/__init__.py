@@ -42,7 +42,7 @@ class moss_dit_config(C.Structure):
                 ("latent_channels", C.c_int32), ("patch", C.c_int32), ("temb_dim", C.c_int32),
                 ("qk_norm", C.c_int32), ("rope_theta", C.c_float), ("norm_eps", C.c_float),
                 ("flow_multiplier", C.c_float), ("text_dim", C.c_int32), ("refiner_layers", C.c_int32),
-                ("gemm_precision", C.c_int32)]
+                ("gemm_precision", C.c_int32), ("attention_mode", C.c_int32)]
 
 
 class moss_dit_weights(C.Structure):
@@ -108,6 +108,8 @@ _sig("moss_text_refine", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, _P)
 _sig("moss_attention", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_gemm_bf16", C.c_int, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_mx_quantize", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, C.c_int64, _P)
+_sig("moss_attention_q8_workspace", C.c_int64, C.c_int32, C.c_int32, C.c_int32)
+_sig("moss_attention_q8", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64, _P)
 _sig("moss_gemm_mxfp8", C.c_int, _P, _P, C.c_int64, _P, _P, C.c_int64, _P, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_dit_profile_enable", C.c_int, _P, C.c_int32)
 _sig("moss_dit_profile_read", C.c_int, _P, C.POINTER(C.c_double), C.POINTER(C.c_int64))
@@ -122,7 +124,8 @@ EXPORTED = ["moss_dit_abi_version", "moss_status_string", "moss_dit_last_error",
             "moss_sample_step", "moss_validate_step_args", "moss_cfg_euler", "moss_guidance_euler",
             "moss_text_refine", "moss_step_cache_stats", "moss_dit_modulation",
             "moss_block_taps_init", "moss_dit_block", "moss_attention", "moss_gemm_bf16",
-            "moss_mx_quantize", "moss_gemm_mxfp8", "moss_dit_profile_enable", "moss_dit_profile_read"]
+            "moss_mx_quantize", "moss_gemm_mxfp8", "moss_attention_q8_workspace", "moss_attention_q8",
+            "moss_dit_profile_enable", "moss_dit_profile_read"]
 
 
 # ---- host-only calls ----
@@ -247,6 +250,30 @@ def moss_gemm_bf16(A, W, out, stream=None):
     if W.shape[1] != K or tuple(out.shape) != (M, N):
         raise ValueError("shape mismatch")
     _check(_lib.moss_gemm_bf16(_ptr(A), _ptr(W), _ptr(out), M, N, K, _stream(stream)))
+
+
+def moss_attention_q8_workspace(batch: int, seq: int, heads: int) -> int:
+    return int(_lib.moss_attention_q8_workspace(batch, seq, heads))
+
+
+def moss_attention_q8(qkv, out, batch: int, seq: int, heads: int, ws=None, stream=None):
+    """8-bit attention of qkv bf16 [B, S, 3 H 128] into out bf16 [B, S, H 128]; ws: uint8 device tensor of
+    at least moss_attention_q8_workspace bytes (allocated here when None). Returns the workspace."""
+    import torch
+    _check_dev(qkv, torch.bfloat16, "qkv")
+    _check_dev(out, torch.bfloat16, "out")
+    if qkv.numel() != batch * seq * 3 * heads * 128 or out.numel() != batch * seq * heads * 128:
+        raise ValueError("qkv / out sizes do not match batch, seq, heads")
+    need = moss_attention_q8_workspace(batch, seq, heads)
+    if ws is None:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=qkv.device)
+    _check_dev(ws, torch.uint8, "ws")
+    off = (-ws.data_ptr()) % 256
+    if ws.numel() - off < need:
+        raise ValueError("workspace too small")
+    _check(_lib.moss_attention_q8(_ptr(qkv), _ptr(out), batch, seq, heads, C.c_void_p(ws.data_ptr() + off),
+                                  ws.numel() - off, _stream(stream)))
+    return ws
 
 
 def mx_scale_words(rows: int, K: int) -> int:

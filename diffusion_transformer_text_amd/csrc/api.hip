@@ -123,6 +123,7 @@ struct moss_dit {
   std::vector<Mx8> qkv8, out8, gu8, down8, rqkv8, rout8, rgu8, rdown8;
   void* w8buf = nullptr;
   bool fp8() const { return cfg.gemm_precision == 1; }
+  bool q8attn() const { return cfg.attention_mode == 1; }
   // step cache (First-Block Cache) of the current sampling run, in its own allocation
   struct StepCache {
     bool valid = false;                  // r_prev / rest hold the last full call of this row plan
@@ -227,6 +228,10 @@ int check_config(const moss_dit_config* c, std::string& msg) {
   }
   if (c->gemm_precision != 0 && c->gemm_precision != 1) {
     msg = fmt("gemm_precision must be 0 (bf16) or 1 (MXFP8), got %d", c->gemm_precision);
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (c->attention_mode != 0 && c->attention_mode != 1) {
+    msg = fmt("attention_mode must be 0 (exact) or 1 (8-bit), got %d", c->attention_mode);
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   if (c->gemm_precision == 1 && c->ffn_hidden % 256 != 0) {
@@ -369,6 +374,8 @@ struct Carve {
   float *u, *vel;
   uint8_t *q8, *s8;   // FP8 tier: one quantized activation (codes, scale words with ld = M rounded to 256)
   long lds8;
+  void* attn8;        // 8-bit attention: codes and scales of one layer's q, k, v
+  size_t attn8_bytes;
 };
 
 size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, Carve* c) {
@@ -397,6 +404,12 @@ size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, 
     const size_t Kmax = D > F ? D : F;
     t.q8 = (uint8_t*)take(M * Kmax);
     t.s8 = (uint8_t*)take(Kmax / 128 * (size_t)t.lds8 * 4);
+  }
+  t.attn8 = nullptr;
+  t.attn8_bytes = 0;
+  if (H->q8attn()) {
+    t.attn8_bytes = attention_q8_workspace(B, S, k.num_heads);
+    t.attn8 = take(t.attn8_bytes);
   }
   if (c) *c = t;
   return off;
@@ -546,7 +559,10 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
   {
     ProfScope ps(H, PC_ATTN, st);
-    HIP_TRY(H, launch_attention(at, st));
+    if (H->q8attn())
+      HIP_TRY(H, launch_attention_q8(at, c.attn8, c.attn8_bytes, st));
+    else
+      HIP_TRY(H, launch_attention(at, st));
   }
   HIP_TRY(H, tap_copy(taps ? taps->o : nullptr, c.o, (size_t)M * D * 2));
   // A7: out projection + gated residual
@@ -800,6 +816,7 @@ void moss_dit_config_init(moss_dit_config* c, uint32_t size) {
   d.text_dim = 4096;
   d.refiner_layers = 2;
   d.gemm_precision = 0;
+  d.attention_mode = 0;
   memcpy(c, &d, size < sizeof d ? size : sizeof d);
 }
 
@@ -1328,6 +1345,44 @@ int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t hea
   }
   if (e != hipSuccess) {
     g_thread_error = fmt("moss_attention failed: %s", hipGetErrorString(e));
+    return MOSS_ERR_DEVICE;
+  }
+  return MOSS_OK;
+}
+
+int64_t moss_attention_q8_workspace(int32_t batch, int32_t seq, int32_t heads) {
+  if (batch < 1 || seq < 1 || heads < 1) return 0;
+  return (int64_t)attention_q8_workspace(batch, seq, heads);
+}
+
+int moss_attention_q8(const void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, void* ws,
+                      int64_t ws_bytes, void* stream) {
+  if (!qkv || !out || !ws || batch < 1 || seq < 1 || heads < 1 || batch > 65535 || heads > 65535) {
+    g_thread_error = "moss_attention_q8: bad arguments";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  if (ws_bytes < (int64_t)attention_q8_workspace(batch, seq, heads) || (reinterpret_cast<uintptr_t>(ws) & 255)) {
+    g_thread_error = "moss_attention_q8: the workspace must be 256-byte aligned and hold moss_attention_q8_workspace bytes";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  const long D = (long)heads * kHeadDim;
+  const long nblk = (seq + 63) / 64;
+  if (2L * seq * 3 * D > 0x7fffffffL || (long)seq * D > 0x7fffffffL || (long)batch * heads * kHeadDim * nblk * 64 > 0x7fffffffL) {
+    g_thread_error = "moss_attention_q8: one sample's qkv rows and the whole V^T copy must stay below 2 GiB";
+    return MOSS_ERR_INVALID_ARGUMENT;
+  }
+  AttnArgs at;
+  at.qkv = (const uint16_t*)qkv;
+  at.out = (uint16_t*)out;
+  at.B = batch;
+  at.S = seq;
+  at.H = heads;
+  at.ld_qkv = 3 * D;
+  at.ld_out = D;
+  at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+  const hipError_t e = launch_attention_q8(at, ws, (size_t)ws_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_thread_error = fmt("moss_attention_q8 failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;

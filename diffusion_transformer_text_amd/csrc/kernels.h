@@ -84,6 +84,27 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
 
+// 8-bit attention (the FP8 tier's attention): qkv as above (q and k already rotated). The workspace
+// (attention_q8_workspace bytes, 256-byte aligned) receives the INT8 Q and K, the FP8 V^T and their
+// scales. Two quantization passes, then the attention.
+struct AttnQ8Args {
+  const uint16_t* qkv;
+  uint16_t* out;
+  int B, S, H;
+  long ld_qkv, ld_out;
+  float scale_log2;
+  int nblk;                 // 64-key blocks per sequence
+  int8_t* q8;               // [B*S][H*128] INT8
+  int8_t* k8;               // [B*S][H*128] INT8
+  uint8_t* vt8;             // [B][H][128][nblk*64] E4M3, keys permuted within each block
+  float* qa;                // [B*S][H] per-token amax of q
+  float* ka;                // [B][H][nblk] per-block amax of k
+  float* va;                // [B][H][128] per-channel amax of v
+  float* vpart;             // [B][H][nblk][128] per-block channel maxima of v
+};
+size_t attention_q8_workspace(int B, int S, int H);
+hipError_t launch_attention_q8(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+
 // In-place axial rotary turn of the q and k columns of the image rows of qkv (standalone attention).
 hipError_t launch_rope_inplace(uint16_t* qkv, int B, int S, int T, int grid_w, int H, long ld,
                                const float* cos_t, const float* sin_t, hipStream_t stream);

@@ -73,7 +73,10 @@ const char* moss_dit_last_error(const moss_dit* h);
  * power-of-two scale per 32 elements along the reduction axis, weights once at creation, activations
  * on the fly -- and run on the scaled FP8 matrix cores with fp32 accumulation; everything else stays
  * as in the bf16 tier. Needs ffn_hidden % 256 == 0. The pages' tiers use channel- or tensor-wise
- * scales; the block format is the one gfx950's FP8 matrix instruction applies in hardware. */
+ * scales; the block format is the one gfx950's FP8 matrix instruction applies in hardware.
+ * attention_mode = 1 runs every joint block's attention in 8 bits, the pages' q8_fp8 mode (MossInfer
+ * integration guide, "Quality tier": the faster tiers pair their GEMMs with 8-bit attention); the
+ * arithmetic is the one moss_attention_q8 (moss_dit_ops.h) states. Independent of gemm_precision. */
 typedef struct {
   uint32_t struct_size;
   int32_t num_layers, hidden, num_heads, head_dim, ffn_hidden, latent_channels, patch, temb_dim, qk_norm;
@@ -81,6 +84,7 @@ typedef struct {
   int32_t text_dim;                /* width of the text encoder's states (input of the text refiner)   */
   int32_t refiner_layers;          /* text-only blocks after the text projection                       */
   int32_t gemm_precision;          /* block projections: 0 = bf16 (default), 1 = MXFP8 (lossy FP8 tier) */
+  int32_t attention_mode;          /* 0 = exact (default), 1 = 8-bit (q8_fp8: INT8 Q K^T, FP8 P V; lossy) */
 } moss_dit_config;
 void moss_dit_config_init(moss_dit_config* c, uint32_t size);
 

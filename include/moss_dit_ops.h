@@ -50,6 +50,20 @@ int moss_dit_block(moss_dit* h, int32_t layer, void* x, int32_t batch, int32_t t
 int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, int32_t text_len,
                    int32_t grid_w, int32_t rope, void* stream);
 
+/* 8-bit attention (the FP8 tier's attention: the pages' q8_fp8 mode -- 8-bit Q and K, FP8 P V; MossInfer
+ * integration guide, "Quality tier" and its attention modes). Reading (the pages give no formula): Q
+ * symmetric INT8 per token and head (scale amax/127), K symmetric INT8 per block of 64 consecutive keys
+ * and head, V FP8 E4M3 per channel (scale amax/448); exact integer Q K^T, fp32 online softmax over
+ * the 64-key blocks with the exact running max, each block's probabilities rounded to E4M3 on the
+ * scale 448, the normaliser summing the same rounded probabilities; fp32 accumulation.
+ *   qkv: device bf16 [B, S, 3*H*128] (q | k | v, q and k already rotated where wanted), 16-byte
+ *   aligned; out: device bf16 [B, S, H*128]. ws: device scratch of moss_attention_q8_workspace(B, S, H)
+ *   bytes, 256-byte aligned, owned by the caller; it receives the codes and scales (contents undefined
+ *   afterwards). One sample's qkv and the V^T copy must stay below 2 GiB. */
+int64_t moss_attention_q8_workspace(int32_t batch, int32_t seq, int32_t heads);
+int moss_attention_q8(const void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, void* ws,
+                      int64_t ws_bytes, void* stream);
+
 /* bf16 GEMM out = A W^T with an fp32 output (device A bf16 [M, K], W bf16 [N, K], out fp32 [M, N]);
  * K % 64 == 0, N % 128 == 0. */
 int moss_gemm_bf16(const void* A, const void* W, float* out, int32_t M, int32_t N, int32_t K, void* stream);

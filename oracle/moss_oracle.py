@@ -88,6 +88,7 @@ class Config:
     text_dim: int = 4096
     refiner_layers: int = 2
     gemm_precision: str = "bf16"        # "bf16", or "mxfp8" for the FP8 tier of the block projections
+    attention_mode: str = "exact"       # "exact", or "q8" for the 8-bit attention of the FP8 tier
 
     @property
     def patch_dim(self) -> int:
@@ -433,7 +434,8 @@ def block(x: np.ndarray, m: np.ndarray, W: Dict, l: int, cfg: Config, text_len: 
     v_all = kv[:, D:]
     q = r(projection(a_all[rows], wqkv[:D], cfg))
     q = r(rope_rows(q, text_len, grid_w, d, theta, rows=rows))
-    o = r(attention(q, k_all, v_all, H, d))
+    attn = attention_q8 if cfg.attention_mode == "q8" else attention
+    o = r(attn(q, k_all, v_all, H, d))
     attn_out = projection(o, W["out_w"][l], cfg)
     x1 = r(x[rows] + gate1 * attn_out)
     a2 = r(ln_modulate(x1, shift2, scale2, eps))

@@ -61,4 +61,5 @@ def oracle_cfg(cfg) -> O.Config:
     return O.Config(num_layers=cfg.num_layers, hidden=cfg.hidden, num_heads=cfg.num_heads, head_dim=cfg.head_dim,
                     ffn_hidden=cfg.ffn_hidden, latent_channels=cfg.latent_channels, patch=cfg.patch,
                     temb_dim=cfg.temb_dim, text_dim=cfg.text_dim, refiner_layers=cfg.refiner_layers,
-                    gemm_precision="mxfp8" if cfg.gemm_precision == 1 else "bf16")
+                    gemm_precision="mxfp8" if cfg.gemm_precision == 1 else "bf16",
+                    attention_mode="q8" if cfg.attention_mode == 1 else "exact")

@@ -71,6 +71,7 @@ def test_config_defaults_are_the_pages():
     # the refiner: two text-only blocks ("Architecture and specs"); the state width is a reading
     assert c.refiner_layers == a["refiner_blocks"] == o.refiner_layers and c.text_dim == o.text_dim
     assert c.gemm_precision == 0 and o.gemm_precision == "bf16"    # the reference tier is bf16
+    assert c.attention_mode == 0 and o.attention_mode == "exact"  # and runs exact attention
 
 
 def test_step_defaults_are_the_pages():
@@ -185,6 +186,14 @@ def test_validate_fp8_tier_config():
     """gemm_precision: 0 or 1; the MXFP8 tier needs ffn_hidden % 256 == 0 (a whole k-tile group)."""
     for kw, want in (({"gemm_precision": 1}, 0), ({"gemm_precision": 2}, 1), ({"gemm_precision": -1}, 1),
                      ({"gemm_precision": 1, "ffn_hidden": 8192 + 64}, 2), ({"gemm_precision": 0, "ffn_hidden": 8192 + 64}, 0)):
+        cfg = dt.moss_dit_config_init(**kw)
+        a, keep = _valid_step(cfg)
+        assert dt.moss_validate_step_args(cfg, a)[0] == want, kw
+
+
+def test_validate_attention_mode():
+    for kw, want in (({"attention_mode": 1}, 0), ({"attention_mode": 2}, 1), ({"attention_mode": -1}, 1),
+                     ({"attention_mode": 1, "gemm_precision": 1}, 0)):
         cfg = dt.moss_dit_config_init(**kw)
         a, keep = _valid_step(cfg)
         assert dt.moss_validate_step_args(cfg, a)[0] == want, kw

@@ -6,8 +6,12 @@ the GPU, against the oracle run with gemm_precision "mxfp8".
   (each stage from the GPU's previous one) and whole; the forward of a CFG pair (the unconditional row
   skipping block 1); the text refiner (320-wide states, two text-only blocks); and the drift of the
   FP8 forward from the bf16 forward of the same weights, which is the tier's loss.
+* 8-bit attention (attention_mode = 1, alone and with the MXFP8 GEMMs): the block's attention tap
+  against the oracle's attention_q8 of the GPU's own q, k, v; the forward against the oracle in the
+  same mode.
 * Full size: one joint block (hidden 3072, 24 heads, FFN 8192, batch 2, 256 text + 4096 image tokens)
-  on sampled rows against the oracle's MXFP8 block from the same input.
+  on sampled rows against the oracle's MXFP8 block from the same input, with exact and with 8-bit
+  attention.
 
 The projections' own error bound: the scaled FP8 MFMA's result on identical MXFP8 operands deviates
 from the exact product by a relative L2 of about 1.4e-5 (it does not sum a 64-product k-tile in
@@ -42,19 +46,20 @@ def mx(a):
     return O.mx_dequantize(a)
 
 
-def _cfg(shape, precision):
+def _cfg(shape, precision, attention_mode=0):
     return dt.moss_dit_config_init(num_layers=shape.num_layers, hidden=shape.hidden, num_heads=shape.num_heads,
                                    ffn_hidden=shape.ffn_hidden, text_dim=shape.text_dim,
-                                   refiner_layers=shape.refiner_layers, gemm_precision=precision)
+                                   refiner_layers=shape.refiner_layers, gemm_precision=precision,
+                                   attention_mode=attention_mode)
 
 
 _cache = {}
 
 
-def tiny(mod_scale, precision=1):
-    key = (mod_scale, precision)
+def tiny(mod_scale, precision=1, attention_mode=0):
+    key = (mod_scale, precision, attention_mode)
     if key not in _cache:
-        log(f"create tiny FP8-shape model mod_scale={mod_scale} precision={precision}")
+        log(f"create tiny FP8-shape model mod_scale={mod_scale} precision={precision} attention={attention_mode}")
         s = synth.TINY_FP8
         w, inp = synth.tiny_workload(mod_scale=mod_scale, shape=s)
         rw = synth.refiner_weights(s, seed=100)
@@ -62,7 +67,7 @@ def tiny(mod_scale, precision=1):
         d["text_proj_w"] = dev_bf16(rw["text_proj_w"], torch)
         for k in ("refiner_qkv_w", "refiner_out_w", "refiner_gate_up_w", "refiner_down_w"):
             d[k] = [dev_bf16(a, torch) for a in rw[k]]
-        cfg = _cfg(s, precision)
+        cfg = _cfg(s, precision, attention_mode)
         W = O.weights_to_f64(w)
         W["text_proj_w"] = O.from_bf16_bits(rw["text_proj_w"])
         for k in ("refiner_qkv_w", "refiner_out_w", "refiner_gate_up_w", "refiner_down_w"):
@@ -236,3 +241,93 @@ def test_fp8_full_block_sampled_rows():
     for k, v in errs.items():
         tol = {"out_proj": REL_L2_MX_GEMM, "down_proj": REL_L2_MX_GEMM, "block": REL_L2_BF16}.get(k, REL_L2_FP8_CHAIN)
         assert max(v) <= tol, (k, v)
+
+
+# ------------------------------------------------------------------------------------------------
+# 8-bit attention in the model
+# ------------------------------------------------------------------------------------------------
+
+REL_L2_Q8_ATTN = 4e-3      # the attention kernel's own bound on identical inputs (bf16 output rounding)
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_q8_attention_block_tap_and_forward_vs_oracle(precision):
+    mod_scale = 50.0
+    m, inp, W, ocfg = tiny(mod_scale, precision, 1)
+    assert ocfg.attention_mode == "q8"
+    D, T, gh, gw = ocfg.hidden, 32, 8, 8
+    S, B = T + gh * gw, 2
+    rng = np.random.default_rng(6)
+    x = dev_bf16(synth.bf16_normal_bits(rng, (B, S, D)), torch)
+    mod = torch.empty((B, m.mod_stride), dtype=torch.bfloat16, device="cuda")
+    m.moss_dit_modulation([0.8, 0.3], mod)
+    M = B * S
+    taps = {"qkv": torch.empty((M, 3 * D), dtype=torch.bfloat16, device="cuda"),
+            "o": torch.empty((M, D), dtype=torch.bfloat16, device="cuda")}
+    log(f"q8 attention block tap precision={precision}")
+    m.moss_dit_block(1, x, T, gh, gw, mod, taps=taps)
+    torch.cuda.synchronize()
+    qkv, o = host_bf16(taps["qkv"]), host_bf16(taps["o"])
+    errs = []
+    for b in range(B):
+        rs = slice(b * S, (b + 1) * S)
+        ref = O.bf16_round(O.attention_q8(qkv[rs, :D], qkv[rs, D:2 * D], qkv[rs, 2 * D:], 2, 128))
+        errs.append(rel_l2(o[rs], ref))
+    log(f"  attention tap rel_l2 {max(errs):.2e}")
+    assert max(errs) <= REL_L2_Q8_ATTN
+    v = _forward(m, inp, [0.6, 0.6], [0, 1 << 1])
+    lat = np.concatenate([inp.latents, inp.latents]).astype(np.float64)
+    txt = np.concatenate([inp.text_cond, inp.text_uncond]).astype(np.float64)
+    ref = O.forward(lat, txt, [0.6, 0.6], W, ocfg, skip=[set(), {1}], mirror=True)
+    e_v = rel_l2(v, ref)
+    e_d = rel_l2(v[0] - v[1], ref[0] - ref[1])
+    log(f"  forward rel-L2 v {e_v:.3e}  (v_c - v_u) {e_d:.3e}")
+    assert e_v <= REL_L2_BF16
+    assert e_d <= REL_L2_FP8_CHAIN
+
+
+@pytest.mark.timeout(600)
+def test_q8_attention_full_block_sampled_rows():
+    log(f"fp8 + q8 attention full block: D=3072 F=8192 H=24, B=2, S={FS}")
+    shape = synth.Shape(num_layers=1)
+    w = synth.torch_weights(shape, seed=3, device="cuda", mod_scale=50.0)
+    cfg = dt.moss_dit_config_init(num_layers=1, gemm_precision=1, attention_mode=1)
+    model = dt.MossDiT(cfg, w)
+    ocfg = oracle_cfg(cfg)
+    D = ocfg.hidden
+    rng = np.random.default_rng(13)
+    B = 2
+    xbits = synth.bf16_normal_bits(rng, (B, FS, D))
+    sig = synth.uniform_f32(rng, (B,))
+    x = dev_bf16(xbits, torch)
+    mod = torch.empty((B, model.mod_stride), dtype=torch.bfloat16, device="cuda")
+    model.moss_dit_modulation([float(s_) for s_ in sig], mod)
+    M = B * FS
+    taps = {"qkv": torch.empty((M, 3 * D), dtype=torch.bfloat16, device="cuda"),
+            "o": torch.empty((M, D), dtype=torch.bfloat16, device="cuda")}
+    model.moss_dit_block(0, x, FT, FGH, FGW, mod, taps=taps)
+    torch.cuda.synchronize()
+    W = {"qkv_w": [host_bf16(w["qkv_w"][0])], "out_w": [host_bf16(w["out_w"][0])],
+         "gate_up_w": [host_bf16(w["gate_up_w"][0])], "down_w": [host_bf16(w["down_w"][0])]}
+    modv = host_bf16(mod)
+    x_out = host_bf16(x).reshape(B, FS, D)
+    qkv = host_bf16(taps["qkv"]).reshape(B, FS, 3 * D)
+    o = host_bf16(taps["o"]).reshape(B, FS, D)
+    x0 = O.from_bf16_bits(xbits)
+    errs = {}
+    for b in range(B):
+        rows = np.unique(np.concatenate([rng.integers(0, FS, 12), [0, FT - 1, FT, FS - 1]]))
+        for h in (0, 13, 23):
+            sl = slice(h * 128, (h + 1) * 128)
+            ref = O.bf16_round(O.attention_q8(qkv[b][rows, sl], qkv[b][:, D + h * 128:D + (h + 1) * 128],
+                                              qkv[b][:, 2 * D + h * 128:2 * D + (h + 1) * 128], 1, 128))
+            errs.setdefault("attention", []).append(rel_l2(o[b][rows, sl], ref))
+        mb = modv[b, :6 * D].reshape(6, D)
+        ref = O.block(x0[b], mb, W, 0, ocfg, FT, FGW, mirror=True, rows=rows)
+        errs.setdefault("block", []).append(rel_l2(x_out[b][rows], ref))
+        errs.setdefault("block_update", []).append(rel_l2(x_out[b][rows] - x0[b][rows], ref - x0[b][rows]))
+    log({k: f"{max(v):.2e}" for k, v in errs.items()})
+    model.close()
+    assert max(errs["attention"]) <= REL_L2_Q8_ATTN
+    assert max(errs["block"]) <= REL_L2_BF16
+    assert max(errs["block_update"]) <= REL_L2_FP8_CHAIN

@@ -867,3 +867,19 @@ def test_q8_attention_is_close_to_exact():
     got = O.attention_q8(q, k, v, H, d)
     rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
     assert 1e-4 < rel < 0.05, rel
+
+
+def test_block_with_q8_attention_uses_attention_q8():
+    # the block's attention tap under attention_mode "q8" is attention_q8 of the block's own q, k, v
+    cfg = _tiny_cfg()
+    cfgq = O.Config(**{**cfg.__dict__, "attention_mode": "q8"})
+    rng = np.random.default_rng(74)
+    W = _tiny_weights(cfg, rng)
+    x = rng.standard_normal((6, cfg.hidden))
+    m, _ = O.modulation(0.4, W, cfg)
+    taps = {}
+    bq = O.block(x, m[0], W, 0, cfgq, 2, 2, taps=taps)
+    np.testing.assert_array_equal(taps["o"], O.attention_q8(taps["q"], taps["k"], taps["v"], cfg.num_heads, cfg.head_dim))
+    b16 = O.block(x, m[0], W, 0, cfg, 2, 2)
+    rel = np.linalg.norm(bq - b16) / np.linalg.norm(b16 - x)
+    assert 0 < rel < 0.1
