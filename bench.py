@@ -366,47 +366,52 @@ def main():
             del enc, outr
         log(f"[bench] text refiner: {json.dumps(refiner)}")
 
-    # ---- the FP8 tier (lossy, opt-in): a second handle on the same weights with MXFP8 block projections;
-    # the same window steps, the per-class split, and one step's drift from the bf16 tier ----
+    # ---- the FP8 tier (lossy, opt-in): second handles on the same weights, with the MXFP8 block
+    # projections, then also with 8-bit attention; the same window steps, the per-class split, and one
+    # step's drift from the bf16 tier ----
     fp8 = None
     if args.fp8_steps > 0:
-        t0 = time.time()
-        model8 = dt.MossDiT(dt.moss_dit_config_init(gemm_precision=1), weights)
-        log(f"[bench] FP8 handle created (weights quantized) in {time.time() - t0:.1f} s")
+        fp8 = {}
+        for name, kw in (("mxfp8_gemm", {"gemm_precision": 1}),
+                         ("mxfp8_gemm_q8_attention", {"gemm_precision": 1, "attention_mode": 1})):
+            t0 = time.time()
+            model8 = dt.MossDiT(dt.moss_dit_config_init(**kw), weights)
+            log(f"[bench] {name} handle created (weights quantized) in {time.time() - t0:.1f} s")
 
-        def step8(k):
-            model8.moss_sample_step(x, text_cond, text_uncond, sig, 1 + (k % 49), cfg_scale=3.0,
-                                    uncond_skip_layers=[22], slg_start=0.01, slg_stop=1.0)
+            def step8(k):
+                model8.moss_sample_step(x, text_cond, text_uncond, sig, 1 + (k % 49), cfg_scale=3.0,
+                                        uncond_skip_layers=[22], slg_start=0.01, slg_stop=1.0)
 
-        x.copy_(x0)
-        ms8 = timed(step8, args.fp8_steps)
-        model8.moss_dit_profile_enable(True)
-        for k in range(args.profile_steps):
-            step8(k)
-        prof8 = model8.moss_dit_profile_read()
-        model8.moss_dit_profile_enable(False)
-        k8 = {}
-        for cls, (ms, n) in prof8.items():
-            if n == 0 or not cls.startswith("gemm"):
-                continue
-            fl, _ = class_work(cls, L, D, F, S, N, T, 2, [22], lat_elems, mod_rows, P)
-            ms_s = ms / args.profile_steps
-            k8[cls] = {"ms_per_step": round(ms_s, 4), "tflops": round(fl / (ms_s * 1e-3) / 1e12, 1),
-                       "frac_fp8_peak": round(fl / (ms_s * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
-        # one step from the same state with each tier: the tier's drift on this (random-weight) model
-        xa, xb = x0.clone(), x0.clone()
-        model.moss_sample_step(xa, text_cond, text_uncond, sig, 1, cfg_scale=3.0, uncond_skip_layers=[22])
-        model8.moss_sample_step(xb, text_cond, text_uncond, sig, 1, cfg_scale=3.0, uncond_skip_layers=[22])
-        torch.cuda.synchronize()
-        dv = ((xb - x0) - (xa - x0)).double().norm() / (xa - x0).double().norm()
-        fp8 = {"ms_per_step": round(ms8, 3), "forwards_per_s": round(2000.0 / ms8, 3),
-               "speedup_vs_bf16": round(ms_step / ms8, 3), "gemm_classes": k8,
-               "step_update_rel_l2_vs_bf16": round(float(dv), 5),
-               "format": "OCP MXFP8 (E4M3, E8M0 scale per 32 along K), weights quantized at creation, "
-                         "activations before each block projection"}
-        log(f"[bench] FP8 tier: {json.dumps(fp8)}")
-        model8.close()
-        del model8
+            x.copy_(x0)
+            ms8 = timed(step8, args.fp8_steps)
+            model8.moss_dit_profile_enable(True)
+            for k in range(args.profile_steps):
+                step8(k)
+            prof8 = model8.moss_dit_profile_read()
+            model8.moss_dit_profile_enable(False)
+            k8 = {}
+            for cls, (ms, n) in prof8.items():
+                if n == 0 or not (cls.startswith("gemm") or cls == "attention"):
+                    continue
+                fl, _ = class_work(cls, L, D, F, S, N, T, 2, [22], lat_elems, mod_rows, P)
+                ms_s = ms / args.profile_steps
+                k8[cls] = {"ms_per_step": round(ms_s, 4), "tflops": round(fl / (ms_s * 1e-3) / 1e12, 1),
+                           "frac_fp8_peak": round(fl / (ms_s * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+            # one step from the same state with each tier: the tier's drift on this (random-weight) model
+            xa, xb = x0.clone(), x0.clone()
+            model.moss_sample_step(xa, text_cond, text_uncond, sig, 1, cfg_scale=3.0, uncond_skip_layers=[22])
+            model8.moss_sample_step(xb, text_cond, text_uncond, sig, 1, cfg_scale=3.0, uncond_skip_layers=[22])
+            torch.cuda.synchronize()
+            dv = ((xb - x0) - (xa - x0)).double().norm() / (xa - x0).double().norm()
+            fp8[name] = {"ms_per_step": round(ms8, 3), "forwards_per_s": round(2000.0 / ms8, 3),
+                         "speedup_vs_bf16": round(ms_step / ms8, 3), "classes": k8,
+                         "step_update_rel_l2_vs_bf16": round(float(dv), 5)}
+            log(f"[bench] FP8 tier {name}: {json.dumps(fp8[name])}")
+            model8.close()
+            del model8
+        fp8["format"] = ("OCP MXFP8 GEMMs (E4M3, E8M0 scale per 32 along K; weights quantized at creation, "
+                         "activations before each block projection); 8-bit attention: INT8 Q (per token) and "
+                         "K (per 64-key block), E4M3 P and V (per channel)")
 
     cpu = None
     if args.cpu_baseline_blocks > 0:
