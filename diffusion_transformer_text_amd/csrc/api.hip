@@ -376,6 +376,8 @@ struct Carve {
   long lds8;
   void* attn8;        // 8-bit attention: codes and scales of one layer's q, k, v
   size_t attn8_bytes;
+  void* attn_split;   // exact attention: partial results of the key-split tail tiles
+  size_t attn_split_bytes;
 };
 
 size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, Carve* c) {
@@ -407,6 +409,8 @@ size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, 
   }
   t.attn8 = nullptr;
   t.attn8_bytes = 0;
+  t.attn_split_bytes = attention_split_workspace(B, S, k.num_heads);
+  t.attn_split = t.attn_split_bytes ? take(t.attn_split_bytes) : nullptr;
   if (H->q8attn()) {
     t.attn8_bytes = attention_q8_workspace(B, S, k.num_heads);
     t.attn8 = take(t.attn8_bytes);
@@ -562,7 +566,7 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
     if (H->q8attn())
       HIP_TRY(H, launch_attention_q8(at, c.attn8, c.attn8_bytes, st));
     else
-      HIP_TRY(H, launch_attention(at, st));
+      HIP_TRY(H, launch_attention(at, st, c.attn_split, c.attn_split_bytes));
   }
   HIP_TRY(H, tap_copy(taps ? taps->o : nullptr, c.o, (size_t)M * D * 2));
   // A7: out projection + gated residual
@@ -1341,7 +1345,19 @@ int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t hea
     at.ld_qkv = 3 * D;
     at.ld_out = D;
     at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
-    e = launch_attention(at, st);
+    // the key-split tail needs scratch for its partial results: a temporary allocation here (this entry
+    // point is for tests and measurement; the model path carves it from the handle's workspace)
+    const size_t split_bytes = attention_split_workspace(batch, seq, heads);
+    void* split_ws = nullptr;
+    if (split_bytes && hipMalloc(&split_ws, split_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      split_ws = nullptr;                  // runs unsplit
+    }
+    e = launch_attention(at, st, split_ws, split_ws ? split_bytes : 0);
+    if (split_ws) {
+      if (e == hipSuccess) e = hipStreamSynchronize(st);
+      (void)hipFree(split_ws);
+    }
   }
   if (e != hipSuccess) {
     g_thread_error = fmt("moss_attention failed: %s", hipGetErrorString(e));

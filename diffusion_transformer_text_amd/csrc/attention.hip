@@ -13,6 +13,8 @@
 // exchange with lane l ^ 32. The output is also computed transposed, O^T = V^T P^T, which leaves the
 // lane's own query in its accumulator columns: the online-softmax rescale is a per-lane multiply and
 // P feeds the second MFMA straight from the score registers (no LDS round trip for P).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -42,7 +44,16 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
 }
 
-__global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
+// Work split of one launch: workgroups [0, n_full) each take a whole query tile (all keys); each of the
+// n_split leftover tiles (tile index n_full + j) is split along its key tiles into `parts` workgroups
+// that write unnormalised partial results (o, running max, sum) for merge_kernel.
+struct AttnSplit {
+  int n_full, n_split, parts;
+  float* part_o;     // [n_split * parts][BQ queries][128]
+  float* part_ml;    // [n_split * parts][BQ queries][2]: running max, sum
+};
+
+__global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit sp) {
   // Two LDS stages each for K and V, as four separate arrays: every access below names a fixed array
   // (the tile loop is unrolled by two), so the compiler can tell a read of one stage from the
   // direct loads still landing in another and waits for those loads only at the next barrier.
@@ -57,12 +68,21 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   // id so that XCD x runs a contiguous range of (sample, head) pairs with all their query tiles:
   // the ~2 heads resident on an XCD at a time share their K/V in that XCD's L2.
   const int nq = (p.S + BQ - 1) / BQ;
-  const int total = nq * p.H * p.B;
+  const int S = p.S;
+  const int ntiles = (S + BKV - 1) / BKV;
   int lin = blockIdx.x;
-  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  int t_begin = 0, t_end = ntiles, part_slot = -1;
+  if (lin < sp.n_full) {
+    if ((sp.n_full & 7) == 0) lin = (lin & 7) * (sp.n_full >> 3) + (lin >> 3);
+  } else {
+    const int j = lin - sp.n_full, part = j % sp.parts;
+    part_slot = j;
+    lin = sp.n_full + j / sp.parts;
+    t_begin = part * ntiles / sp.parts;
+    t_end = (part + 1) * ntiles / sp.parts;
+  }
   const int bh = lin / nq;
   const int q0 = (lin - bh * nq) * BQ, h = bh % p.H, b = bh / p.H;
-  const int S = p.S;
   const int DM = p.H * D;
   const uint16_t* base = p.qkv + (long)b * S * p.ld_qkv;
   const uint16_t* Qg = base + h * D;
@@ -209,10 +229,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   // interleaved with the softmax VALU work of tile t, and the MFMAs of P(t) V(t) with the row max of
   // S(t+1). Stages: K(t) lives in sK[t & 1], V(t) in sV[t & 1]. Iteration t reads K(t+1) and V(t)
   // and refills the two stages read one iteration earlier: K(t+2) -> sK[t & 1], V(t+1) -> sV[(t+1) & 1]. ----
-  const int ntiles = (S + BKV - 1) / BKV;
-  issue_k(0, sK0);
-  issue_v(0, sV0);
-  if (ntiles > 1) issue_k(1, sK1);
+  // key tiles [t_begin, t_end) of this workgroup (all of them unless it holds one part of a split tile)
+  issue_k(t_begin, sK0);
+  issue_v(t_begin, sV0);
+  if (t_begin + 1 < t_end) issue_k(t_begin + 1, sK1);
   lds_copy_barrier();
   floatx16 s_cur[2];
   scores(sK0, s_cur);
@@ -221,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
   auto iteration = [&](int t, uint16_t* kFree, const uint16_t* kNext, uint16_t* vFree, const uint16_t* vCur,
                        floatx16 (&s_cur)[2], floatx16 (&s_next)[2]) {
     lds_copy_barrier();              // K(t+1) and V(t) have landed; kFree and vFree are no longer read
-    if (t + 2 < ntiles) issue_k(t + 2, kFree);
+    if (t + 2 < t_end) issue_k(t + 2, kFree);
     issue_v(t + 1, vFree);
     maybe_rescale(mx_cur);
     // region A: S(t+1) on the matrix core while the VALU turns S(t) into probabilities. Step i issues
@@ -289,19 +309,19 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
     mx_cur = mx_next;
   };
   floatx16 s_alt[2];
-  int t = 0;
-  for (; t + 2 < ntiles; t += 2) {
+  int t = t_begin;
+  for (; t + 2 < t_end; t += 2) {
     iteration(t, sK0, sK1, sV1, sV0, s_cur, s_alt);
     iteration(t + 1, sK1, sK0, sV0, sV1, s_alt, s_cur);
   }
-  if (t + 1 < ntiles) {
+  if (t + 1 < t_end) {
     iteration(t, sK0, sK1, sV1, sV0, s_cur, s_alt);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_alt[kb];
   }
   // ---- last tile: mask keys past the sequence, then the same softmax and P V ----
   {
-    const int t = ntiles - 1;
+    const int t = t_end - 1;
     const int k0 = t * BKV;
     lds_copy_barrier();              // V(t) has landed
     if (k0 + BKV > S) {
@@ -317,11 +337,24 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
     maybe_rescale(mx_cur);
     bf16x8 pf[2][2];
     probs(s_cur, pf);
-    pv_update((t & 1) ? sV1 : sV0, pf);
+    pv_update(((t - t_begin) & 1) ? sV1 : sV0, pf);
   }
 
-  // ---- normalise and store: lane holds query my_q, d = 32 db + 8 g + 4 fh + [0, 4) ----
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (part_slot >= 0) {
+    // one part of a split tile: the unnormalised output and the (max, sum) pair it is relative to
+    const long qrow = (long)part_slot * BQ + wave * 32 + fr;
+    float* po = sp.part_o + qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * gg + 4 * fh) =
+            make_float4(o[db][4 * gg], o[db][4 * gg + 1], o[db][4 * gg + 2], o[db][4 * gg + 3]);
+    if (fh == 0) *reinterpret_cast<float2*>(sp.part_ml + 2 * qrow) = make_float2(m_run, l_tot);
+    return;
+  }
+  // ---- normalise and store: lane holds query my_q, d = 32 db + 8 g + 4 fh + [0, 4) ----
   const float inv = 1.0f / l_tot;
   if (my_q < S) {
     uint16_t* orow = p.out + ((long)b * S + my_q) * p.ld_out + h * D;
@@ -336,6 +369,84 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p) {
         *reinterpret_cast<uint2*>(orow + d) = w;
       }
   }
+}
+
+// Combines the parts of split tile j (grid x = j): thread (query qi = tid / 2, half) of 64 dims.
+// out = sum_p o_p 2^((m_p - m) c) / sum_p l_p 2^((m_p - m) c), m = max_p m_p.
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
+  const int j = blockIdx.x, qi = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int nq = (p.S + BQ - 1) / BQ;
+  const int idx = sp.n_full + j;
+  const int bh = idx / nq;
+  const int q0 = (idx - bh * nq) * BQ, h = bh % p.H, b = bh / p.H;
+  const int q = q0 + qi;
+  if (q >= p.S) return;
+  const float c = p.scale_log2;
+  float m = -INFINITY;
+  for (int pt = 0; pt < sp.parts; ++pt) m = fmaxf(m, sp.part_ml[2 * ((long)(j * sp.parts + pt) * BQ + qi)]);
+  float acc[64];
+#pragma unroll
+  for (int d = 0; d < 64; ++d) acc[d] = 0.f;
+  float l = 0.f;
+  for (int pt = 0; pt < sp.parts; ++pt) {
+    const long row = (long)(j * sp.parts + pt) * BQ + qi;
+    const float2 ml = *reinterpret_cast<const float2*>(sp.part_ml + 2 * row);
+    const float f = __builtin_amdgcn_exp2f((ml.x - m) * c);
+    l += ml.y * f;
+    const float4* po = reinterpret_cast<const float4*>(sp.part_o + row * D + 64 * half);
+#pragma unroll
+    for (int d4 = 0; d4 < 16; ++d4) {
+      const float4 v = po[d4];
+      acc[4 * d4] += v.x * f;
+      acc[4 * d4 + 1] += v.y * f;
+      acc[4 * d4 + 2] += v.z * f;
+      acc[4 * d4 + 3] += v.w * f;
+    }
+  }
+  const float inv = 1.0f / l;
+  uint16_t* orow = p.out + ((long)b * p.S + q) * p.ld_out + h * D + 64 * half;
+#pragma unroll
+  for (int d4 = 0; d4 < 16; ++d4) {
+    uint2 w;
+    w.x = pack2_bf16(acc[4 * d4] * inv, acc[4 * d4 + 1] * inv);
+    w.y = pack2_bf16(acc[4 * d4 + 2] * inv, acc[4 * d4 + 3] * inv);
+    *reinterpret_cast<uint2*>(orow + 4 * d4) = w;
+  }
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// The split plan: `slots` workgroups fit on the chip at once (two per CU); whole rounds stay unsplit,
+// and a last round holding at most half the slots is split into parts filling it.
+AttnSplit split_plan(int B, int S, int H) {
+  AttnSplit sp{};
+  const long total = (long)((S + BQ - 1) / BQ) * H * B;
+  const int ntiles = (S + BKV - 1) / BKV;
+  const long slots = 2L * cu_count();
+  sp.n_full = (int)total;
+  sp.n_split = 0;
+  sp.parts = 1;
+  if (total > slots) {
+    const long rem = total % slots;
+    const int parts = rem > 0 ? (int)std::min<long>(std::min<long>(slots / rem, ntiles / 2), 8) : 1;
+    if (rem > 0 && rem * 2 <= slots && parts >= 2) {
+      sp.n_full = (int)(total - rem);
+      sp.n_split = (int)rem;
+      sp.parts = parts;
+    }
+  }
+  return sp;
 }
 
 __global__ void rope_inplace_kernel(uint16_t* qkv, int B, int S, int T, int grid_w, int H, long ld,
@@ -361,13 +472,33 @@ __global__ void rope_inplace_kernel(uint16_t* qkv, int B, int S, int T, int grid
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
+size_t attention_split_workspace(int B, int S, int H) {
+  const AttnSplit sp = split_plan(B, S, H);
+  const size_t rows = (size_t)sp.n_split * sp.parts * BQ;
+  return rows == 0 ? 0 : rows * D * 4 + rows * 2 * 4 + 256;
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, void* ws, size_t ws_bytes) {
   if (a.S <= 0 || a.B <= 0) return hipSuccess;
   if (a.ld_qkv % 8 != 0 || a.ld_out % 4 != 0) return hipErrorInvalidValue;
   const long wgs = (long)((a.S + BQ - 1) / BQ) * a.H * a.B;
   if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
   if (2L * a.S * a.ld_qkv > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit buffer offsets per sample
-  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
+  AttnSplit sp = split_plan(a.B, a.S, a.H);
+  const size_t rows = (size_t)sp.n_split * sp.parts * BQ;
+  if (rows == 0 || !ws || ws_bytes < attention_split_workspace(a.B, a.S, a.H)) {
+    sp.n_full = (int)wgs;                    // no workspace (or nothing to split): whole tiles only
+    sp.n_split = 0;
+    sp.parts = 1;
+  } else {
+    char* base = static_cast<char*>(ws);
+    base += (256 - (reinterpret_cast<uintptr_t>(base) & 255)) & 255;
+    sp.part_o = reinterpret_cast<float*>(base);
+    sp.part_ml = reinterpret_cast<float*>(base + rows * D * 4);
+  }
+  const long grid = (long)sp.n_full + (long)sp.n_split * sp.parts;
+  hipLaunchKernelGGL(attention_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, sp);
+  if (sp.n_split > 0) hipLaunchKernelGGL(merge_kernel, dim3((unsigned)sp.n_split), dim3(256), 0, stream, a, sp);
   return hipGetLastError();
 }
 

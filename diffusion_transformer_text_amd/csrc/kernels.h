@@ -82,7 +82,11 @@ struct AttnArgs {
   long ld_qkv, ld_out;
   float scale_log2;   // log2(e) / sqrt(d)
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);
+// ws (optional, attention_split_workspace bytes): when the query tiles leave the last round of
+// workgroups on the chip partly empty, those leftover tiles are split along the keys into parts that
+// run side by side, and a merge kernel combines the parts (no ws: no split).
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, void* ws = nullptr, size_t ws_bytes = 0);
+size_t attention_split_workspace(int B, int S, int H);
 
 // 8-bit attention (the FP8 tier's attention): qkv as above (q and k already rotated). The workspace
 // (attention_q8_workspace bytes, 256-byte aligned) receives the INT8 Q and K, the FP8 V^T and their
