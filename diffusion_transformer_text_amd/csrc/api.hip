@@ -373,6 +373,7 @@ struct Carve {
   uint16_t *x, *a, *qkv, *o, *h, *tokens, *mod;
   float *u, *vel;
   uint8_t *q8, *s8;   // FP8 tier: one quantized activation (codes, scale words with ld = M rounded to 256)
+  uint8_t *q8h, *s8h; // FP8 tier: the quantized SwiGLU output h (written by the gate/up GEMM's epilogue)
   long lds8;
   void* attn8;        // 8-bit attention: codes and scales of one layer's q, k, v
   size_t attn8_bytes;
@@ -400,12 +401,14 @@ size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, 
   t.mod = (uint16_t*)take((size_t)B * H->mod_rows() * 2);
   t.u = (float*)take((size_t)B * k.temb_dim * 4);
   t.vel = (float*)take((size_t)B * lat_elems * 4);   // one velocity per row of the step's batch
-  t.q8 = t.s8 = nullptr;
+  t.q8 = t.s8 = t.q8h = t.s8h = nullptr;
   t.lds8 = (long)(M + 255) / 256 * 256;
   if (H->fp8()) {
     const size_t Kmax = D > F ? D : F;
     t.q8 = (uint8_t*)take(M * Kmax);
     t.s8 = (uint8_t*)take(Kmax / 128 * (size_t)t.lds8 * 4);
+    t.q8h = (uint8_t*)take(M * F);
+    t.s8h = (uint8_t*)take(F / 128 * (size_t)t.lds8 * 4);
   }
   t.attn8 = nullptr;
   t.attn8_bytes = 0;
@@ -472,6 +475,9 @@ LnModArgs ln_args(const uint16_t* x, uint16_t* out, int rows, int D, int rows_pe
   l.scale = scale;
   l.mod_stride = mod_stride;
   l.eps = eps;
+  l.q8 = nullptr;
+  l.s8 = nullptr;
+  l.lds8 = 0;
   return l;
 }
 
@@ -506,16 +512,22 @@ BlockW refiner_block(const moss_dit* H, int l) {
 
 // A block projection: the bf16 GEMM, or in the FP8 tier the activation quantized to MXFP8 (into the
 // workspace) and the scaled FP8 GEMM against the weight's MXFP8 copy. g carries the bf16 operands and
-// the epilogue arguments; its M rows of A (row stride K) are the activation.
-hipError_t project(const moss_dit* H, const Carve& c, GemmArgs g, const moss_dit::Mx8& w8, int epi, hipStream_t st) {
+// the epilogue arguments; its M rows of A (row stride K) are the activation. pre_q / pre_s: the
+// activation's MXFP8 codes and scale words (ld = c.lds8) already written by its producer.
+hipError_t project(const moss_dit* H, const Carve& c, GemmArgs g, const moss_dit::Mx8& w8, int epi, hipStream_t st,
+                   const uint8_t* pre_q = nullptr, const uint8_t* pre_s = nullptr) {
   if (!H->fp8()) return launch_gemm(g, epi, st);
-  const hipError_t e = launch_mx_quant(g.A, g.lda, g.M, g.K, c.q8, c.s8, c.lds8, st);
-  if (e != hipSuccess) return e;
-  g.A = reinterpret_cast<const uint16_t*>(c.q8);
+  if (!pre_q) {
+    const hipError_t e = launch_mx_quant(g.A, g.lda, g.M, g.K, c.q8, c.s8, c.lds8, st);
+    if (e != hipSuccess) return e;
+    pre_q = c.q8;
+    pre_s = c.s8;
+  }
+  g.A = reinterpret_cast<const uint16_t*>(pre_q);
   g.lda = g.K;
   g.W = reinterpret_cast<const uint16_t*>(w8.codes);
   g.ldw = g.K;
-  g.A_scale = c.s8;
+  g.A_scale = pre_s;
   g.W_scale = w8.scales;
   g.lds_a = c.lds8;
   g.lds_w = w8.ld;
@@ -532,10 +544,22 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
     if (!taps || !dst) return hipSuccess;
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
   };
+  // FP8 tier without taps: the LN outputs and h go straight to MXFP8 codes (written by their
+  // producers), the bf16 copies are not written
+  const bool fuse = H->fp8() && !taps;
+  auto ln = [&](const uint16_t* shift, const uint16_t* scale) {
+    LnModArgs l = ln_args(x, fuse ? nullptr : c.a, M, D, S, shift, scale, mod_stride, k.norm_eps);
+    if (fuse) {
+      l.q8 = c.q8;
+      l.s8 = c.s8;
+      l.lds8 = c.lds8;
+    }
+    return l;
+  };
   // A4: LN1 + modulation
   {
     ProfScope ps(H, PC_LN, st);
-    HIP_TRY(H, launch_ln_mod(ln_args(x, c.a, M, D, S, m, m + D, mod_stride, k.norm_eps), st));
+    HIP_TRY(H, launch_ln_mod(ln(m, m + D), st));
   }
   HIP_TRY(H, tap_copy(taps ? taps->a : nullptr, c.a, (size_t)M * D * 2));
   // A5: QKV projection, RoPE on image rows of q and k
@@ -548,7 +572,7 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   g.rope_cols = 2 * D;
   {
     ProfScope ps(H, PC_QKV, st);
-    HIP_TRY(H, project(H, c, g, w.qkv8, EPI_QKV_ROPE, st));
+    HIP_TRY(H, project(H, c, g, w.qkv8, EPI_QKV_ROPE, st, fuse ? c.q8 : nullptr, fuse ? c.s8 : nullptr));
   }
   HIP_TRY(H, tap_copy(taps ? taps->qkv : nullptr, c.qkv, (size_t)M * 3 * D * 2));
   // A6: attention
@@ -583,13 +607,20 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   // A8: LN2 + modulation
   {
     ProfScope ps(H, PC_LN, st);
-    HIP_TRY(H, launch_ln_mod(ln_args(x, c.a, M, D, S, m + 3 * D, m + 4 * D, mod_stride, k.norm_eps), st));
+    HIP_TRY(H, launch_ln_mod(ln(m + 3 * D, m + 4 * D), st));
   }
   HIP_TRY(H, tap_copy(taps ? taps->a2 : nullptr, c.a, (size_t)M * D * 2));
   // A9: gate/up projection + SiLU * mul
   {
     ProfScope ps(H, PC_GATE_UP, st);
-    HIP_TRY(H, project(H, c, gemm_args(c.a, w.gu, M, 2 * F, D, c.h, F), w.gu8, EPI_SWIGLU, st));
+    if (fuse) {
+      GemmArgs gu = gemm_args(c.a, w.gu, M, 2 * F, D, c.q8h, F);
+      gu.out_scale = c.s8h;
+      gu.lds_out = c.lds8;
+      HIP_TRY(H, project(H, c, gu, w.gu8, EPI_SWIGLU_MX, st, c.q8, c.s8));
+    } else {
+      HIP_TRY(H, project(H, c, gemm_args(c.a, w.gu, M, 2 * F, D, c.h, F), w.gu8, EPI_SWIGLU, st));
+    }
   }
   HIP_TRY(H, tap_copy(taps ? taps->h : nullptr, c.h, (size_t)M * F * 2));
   // A10: down projection + gated residual
@@ -600,7 +631,7 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   g.gate_stride = mod_stride;
   {
     ProfScope ps(H, PC_DOWN, st);
-    HIP_TRY(H, project(H, c, g, w.down8, EPI_GATED_RES, st));
+    HIP_TRY(H, project(H, c, g, w.down8, EPI_GATED_RES, st, fuse ? c.q8h : nullptr, fuse ? c.s8h : nullptr));
   }
   return MOSS_OK;
 }

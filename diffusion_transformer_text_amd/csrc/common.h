@@ -63,6 +63,35 @@ __device__ __forceinline__ void lds_copy_barrier() {
   __syncthreads();
 }
 
+// ---- OCP MX FP8 (E4M3 elements, one E8M0 scale per 32 elements along the reduction axis) ----
+// Scale exponent floor(log2(amax)) - 8 (8 = E4M3's largest exponent), read from the fp32 exponent
+// field (exact for bf16 values), clamped to [-127, 127]; an all-zero block takes -127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  int ex = -127;
+  if (amax > 0.f) {
+    const int biased = (int)((__float_as_uint(amax) >> 23) & 0xff);
+    ex = (biased == 0 ? -127 : biased - 127) - 8;
+    ex = max(-127, min(127, ex));
+  }
+  return ex;
+}
+// 2^-ex, exact (ex <= 119 for finite bf16 amax)
+__device__ __forceinline__ float mx_inv_scale(int ex) { return __uint_as_float((uint32_t)(127 - ex) << 23); }
+// Four values -> four E4M3 codes, byte i = value i: x * inv clamped to the largest finite E4M3 value
+// first (the hardware conversion rounds to nearest even but turns values past the range into NaN).
+__device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d, float inv) {
+  const float a0 = fminf(fmaxf(a * inv, -448.f), 448.f), a1 = fminf(fmaxf(b * inv, -448.f), 448.f);
+  const float a2 = fminf(fmaxf(c * inv, -448.f), 448.f), a3 = fminf(fmaxf(d * inv, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, w, true);
+  return (uint32_t)w;
+}
+// Byte offset of the scale of 32-element block kb of row r in the scale-word layout (word
+// (2g + h) * ld + r holds in byte q the scale of block 8g + 2q + h).
+__device__ __forceinline__ long mx_scale_byte(int kb, long r, long ld) {
+  return ((long)(2 * (kb >> 3) + (kb & 1)) * ld + r) * 4 + ((kb >> 1) & 3);
+}
+
 // Wave-wide (64 lanes) sum.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

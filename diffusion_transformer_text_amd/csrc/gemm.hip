@@ -85,6 +85,31 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, floatx16 (&acc)[T:
           *reinterpret_cast<uint2*>(out + (long)m * p.ldo + hc) = v;
         }
       }
+    } else if constexpr (EPI == EPI_SWIGLU_MX) {
+      // the same 32 h-columns per q are one MX block: 16 values here, 16 in lane ^ 32 (same token);
+      // codes of the bf16-rounded h, as the separate quantizer would write them
+      uint8_t* out = static_cast<uint8_t*>(p.out);
+#pragma unroll
+      for (int q = 0; q < T::TN / 2; ++q) {
+        float h[4][4];
+        float amax = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[g][e] = round_bf16(silu_f32(acc[i][2 * q][4 * g + e]) * acc[i][2 * q + 1][4 * g + e]);
+            amax = fmaxf(amax, fabsf(h[g][e]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int ex = mx_exponent(amax);
+        const float inv = mx_inv_scale(ex);
+        const int hb = (n0 + wn * T::WN) / 2 + q * 32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint32_t*>(out + (long)m * p.ldo + hb + 8 * g + 4 * fh) =
+              mx_pack4(h[g][0], h[g][1], h[g][2], h[g][3], inv);
+        if (fh == 0) p.out_scale[mx_scale_byte(hb / 32, m, p.lds_out)] = (uint8_t)(ex + 127);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < T::TN; ++j) {
@@ -677,6 +702,10 @@ hipError_t launch_gemm_mxfp8(const GemmArgs& a, int epi, hipStream_t stream) {
     case EPI_QKV_ROPE: MOSS_GEMM_LAUNCH(EPI_QKV_ROPE); break;
     case EPI_GATED_RES: MOSS_GEMM_LAUNCH(EPI_GATED_RES); break;
     case EPI_SWIGLU: MOSS_GEMM_LAUNCH(EPI_SWIGLU); break;
+    case EPI_SWIGLU_MX:
+      if (!a.out_scale || a.lds_out < a.M || a.ldo % 4 != 0) return hipErrorInvalidValue;
+      MOSS_GEMM_LAUNCH(EPI_SWIGLU_MX);
+      break;
     case EPI_F32: MOSS_GEMM_LAUNCH(EPI_F32); break;
     default: return hipErrorInvalidValue;
   }

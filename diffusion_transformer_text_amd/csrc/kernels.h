@@ -20,6 +20,7 @@ enum Epilogue {
   EPI_SWIGLU = 3,       // W holds [gate | up] interleaved in 32-row groups; out h = bf16(SiLU(g) * u)
   EPI_F32 = 4,          // out fp32 [m, n]
   EPI_F32_UNPATCH = 5,  // out fp32 velocity [B, C, lat_h, lat_w]: m = image token, n = c*4 + dy*2 + dx
+  EPI_SWIGLU_MX = 6,    // as EPI_SWIGLU, h written as MXFP8: codes to out (bytes, ldo), scale words to out_scale
 };
 
 struct GemmArgs {
@@ -47,6 +48,9 @@ struct GemmArgs {
   const uint8_t* A_scale;
   const uint8_t* W_scale;
   long lds_a, lds_w;
+  // EPI_SWIGLU_MX: scale words of h (ld = lds_out >= M)
+  uint8_t* out_scale;
+  long lds_out;
 };
 
 // Picks a tile shape for (M, N) and launches. Returns hipSuccess or the launch error.
@@ -69,6 +73,11 @@ struct LnModArgs {
   const uint16_t* scale;
   long mod_stride;
   float eps;
+  // optional MXFP8 copy of the output (the FP8 tier's GEMM operand): codes q8 [rows, D] and scale words
+  // (GemmArgs::A_scale layout, ld = lds8) of the bf16-rounded output; out may then be nullptr
+  uint8_t* q8;
+  uint8_t* s8;
+  long lds8;
 };
 hipError_t launch_ln_mod(const LnModArgs& a, hipStream_t stream);
 

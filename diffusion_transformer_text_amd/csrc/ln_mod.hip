@@ -62,7 +62,6 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(LnModArgs p) {
   const float var = wave_sum(q) * inv_d;
   const float rstd = 1.0f / sqrtf(var + p.eps);
 
-  uint16_t* o = p.out + (long)r * D;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     words w;
@@ -72,7 +71,26 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(LnModArgs p) {
       const float y1 = (hi(xw[c][h]) - mean) * rstd * (1.0f + hi(cw[c][h])) + hi(sw[c][h]);
       w[h] = pack2_bf16(y0, y1);
     }
-    *reinterpret_cast<words*>(o + (c * 64 + lane) * E) = w;
+    const int i0 = (c * 64 + lane) * E;
+    if (p.out) *reinterpret_cast<words*>(p.out + (long)r * D + i0) = w;
+    if (p.q8) {
+      // MXFP8 of the bf16 output: a 32-element block spans 32 / E neighbouring lanes
+      float amax = 0.f;
+#pragma unroll
+      for (int h = 0; h < E / 2; ++h) amax = fmaxf(amax, fmaxf(fabsf(lo(w[h])), fabsf(hi(w[h]))));
+#pragma unroll
+      for (int o = 1; o < 32 / E; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      const int ex = mx_exponent(amax);
+      const float inv = mx_inv_scale(ex);
+      uint32_t codes[E / 4];
+#pragma unroll
+      for (int u = 0; u < E / 4; ++u)
+        codes[u] = mx_pack4(lo(w[2 * u]), hi(w[2 * u]), lo(w[2 * u + 1]), hi(w[2 * u + 1]), inv);
+      uint8_t* qd = p.q8 + (long)r * D + i0;
+      if constexpr (E == 8) *reinterpret_cast<uint2*>(qd) = make_uint2(codes[0], codes[1]);
+      else *reinterpret_cast<uint32_t*>(qd) = codes[0];
+      if ((lane & (32 / E - 1)) == 0) p.s8[mx_scale_byte(i0 / 32, r, p.lds8)] = (uint8_t)(ex + 127);
+    }
   }
 }
 
@@ -94,6 +112,7 @@ bool launch_ln_any(const LnModArgs& a, hipStream_t stream, std::integer_sequence
 hipError_t launch_ln_mod(const LnModArgs& a, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   if (a.D % 256 != 0 || a.D > kMaxElems * 64 || a.seg <= 0 || a.rows_per_sample <= 0) return hipErrorInvalidValue;
+  if ((!a.out && !a.q8) || (a.q8 && (!a.s8 || a.lds8 < a.rows))) return hipErrorInvalidValue;
   const bool ok = (a.D % 512 == 0) ? launch_ln_any<8>(a, stream, std::make_integer_sequence<int, kMaxElems / 8>{})
                                    : launch_ln_any<4>(a, stream, std::make_integer_sequence<int, kMaxElems / 4>{});
   if (!ok) return hipErrorInvalidValue;

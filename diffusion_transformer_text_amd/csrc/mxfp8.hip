@@ -42,31 +42,15 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  // scale exponent floor(log2(amax)) - 8 from the fp32 exponent field (amax is a bf16 value: exact);
-  // an all-zero block takes the smallest scale, 2^-127
-  int ex = -127;
-  if (amax > 0.f) {
-    const int biased = (int)((__float_as_uint(amax) >> 23) & 0xff);
-    ex = (biased == 0 ? -127 : biased - 127) - 8;
-    ex = max(-127, min(127, ex));
-  }
-  const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);   // 2^-ex, exact: ex <= 119 for finite bf16
+  const int ex = mx_exponent(amax);
+  const float inv = mx_inv_scale(ex);
   uint32_t packed[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    // clamp to the largest finite E4M3 value first: the hardware conversion rounds to nearest even but
-    // turns values past the format's range into NaN
-    const float a0 = fminf(fmaxf(v[4 * e] * inv, -448.f), 448.f), a1 = fminf(fmaxf(v[4 * e + 1] * inv, -448.f), 448.f);
-    const float a2 = fminf(fmaxf(v[4 * e + 2] * inv, -448.f), 448.f), a3 = fminf(fmaxf(v[4 * e + 3] * inv, -448.f), 448.f);
-    int word = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, word, true);
-    packed[e] = (uint32_t)word;
-  }
+  for (int e = 0; e < 8; ++e) packed[e] = mx_pack4(v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3], inv);
   uint4* dst = reinterpret_cast<uint4*>(q + (long)r * K + kb * 32);
   dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-  const int g = kb >> 3, qb = (kb >> 1) & 3, h = kb & 1;
-  s[((long)(2 * g + h) * lds + r) * 4 + qb] = (uint8_t)(ex + 127);
+  s[mx_scale_byte(kb, r, lds)] = (uint8_t)(ex + 127);
 }
 
 }  // namespace
