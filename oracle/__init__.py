@@ -55,6 +55,6 @@ from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, emb
                           first_block_change, forward_cached, sample_step_cached,
                           e4m3_round, mx_quantize, mx_dequantize, E4M3_MAX, projection,
                           attention_q8, q8_quantize_q, q8_quantize_k, fp8_quantize_v, int8_codes,
-                          Q8_KEY_BLOCK,
+                          Q8_KEY_BLOCK, Q8_P_SCALE,
                           patchify, rope_angles, apply_rope, rope_rows, sample_step, sigmas, silu,
                           slg_active, time_features, unpatchify, weights_to_f64)

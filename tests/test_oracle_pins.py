@@ -883,3 +883,34 @@ def test_block_with_q8_attention_uses_attention_q8():
     b16 = O.block(x, m[0], W, 0, cfg, 2, 2)
     rel = np.linalg.norm(bq - b16) / np.linalg.norm(b16 - x)
     assert 0 < rel < 0.1
+
+
+def test_q8_attention_reference_max_moves_only_by_more_than_a_factor_two():
+    # one query, keys in three blocks whose maxima rise by 0.5, then 1.5 units of log2: the reference
+    # max stays at block 0's through block 1 (so block 1's top probability is 2^0.5, coded on the 224
+    # scale) and moves at block 2; the result must equal a hand computation of that schedule
+    d = 128
+    q = np.zeros((1, d)); q[0, 0] = 1.0
+    k = np.zeros((192, d))
+    ln2 = math.log(2.0)
+    tops = [0.0, 0.5, 2.0]                               # block maxima in log2 units (of the scaled score)
+    for t, top in enumerate(tops):
+        k[64 * t, 0] = top * ln2 * math.sqrt(d)          # score = q.k / sqrt(d) = top * ln 2
+    v = np.zeros((192, d)); v[:, 1] = np.arange(192) + 1.0
+    got = O.attention_q8(q, k, v, 1, d)
+    # rebuild with the same quantizers and the expected schedule of reference maxima
+    qc, qa = O.q8_quantize_q(q)
+    kc, ka = O.q8_quantize_k(k)
+    vc, va = O.fp8_quantize_v(v)
+    vh = vc * va / O.E4M3_MAX
+    s_all = [(qc @ kc[64 * t:64 * t + 64].T)[0] * qa[0] / 127 * ka[t] / 127 / math.sqrt(d) for t in range(3)]
+    m_sched = [s_all[0].max(), s_all[0].max(), s_all[2].max()]   # no move at block 1 (0.5 < 1), a move at block 2
+    o = np.zeros(d); l = 0.0; m_prev = None
+    for t in range(3):
+        a = 1.0 if m_prev is None or m_prev == m_sched[t] else math.exp(m_prev - m_sched[t])
+        p = O.e4m3_round(np.exp(s_all[t] - m_sched[t]) * O.Q8_P_SCALE) / O.Q8_P_SCALE
+        o = o * a + p @ vh[64 * t:64 * t + 64]
+        l = l * a + p.sum()
+        m_prev = m_sched[t]
+    np.testing.assert_allclose(got[0], o / l, rtol=1e-12)
+    assert np.exp(s_all[1] - m_sched[1]).max() > 1.0         # block 1 really had a probability above 1
