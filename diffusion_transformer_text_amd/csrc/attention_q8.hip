@@ -6,9 +6,10 @@
 // modes of its feature table) without printing their arithmetic. Reading: Q symmetric INT8 per token
 // and head (scale amax / 127), K symmetric INT8 per block of 64 consecutive keys and head, V FP8 E4M3
 // per channel (scale amax / 448); integer dot products are exact, the softmax runs online over the
-// 64-key blocks with the exact running max, each block's probabilities p <= 1 are rounded to E4M3 on
-// the scale 448, and the normaliser sums the same rounded probabilities, so the output is a convex
-// combination of the dequantized V rows. Codes are decided in fp32: x * 127 and x * 448 are exact for
+// 64-key blocks, each query's reference max moving to a block's max only when that is more than one
+// log2 unit above it (so the rare moves are the only rescales and every probability stays <= 2), the
+// probabilities are rounded to E4M3 on the scale 224, and the normaliser sums the same rounded
+// probabilities, so the output is a convex combination of the dequantized V rows. Codes are decided in fp32: x * 127 and x * 448 are exact for
 // bf16 inputs, followed by one correctly rounded division.
 //
 // Two passes quantize the (roped) bf16 qkv of a layer: q8k8_quant_kernel writes the INT8 Q and K and
@@ -18,6 +19,7 @@
 //
 // The attention kernel keeps the bf16 kernel's transposed form (S^T = K Q^T, O^T = V^T P^T: lane l
 // holds the scores and the output of query l % 32) with 8 KB K and V^T tiles, half of the bf16 ones.
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -29,6 +31,7 @@ namespace {
 constexpr int D = kHeadDim;   // 128
 constexpr int KB = 64;        // keys per block / tile
 constexpr float kE4M3Max = 448.f;
+constexpr float kLog2PScale = 7.807354922057604f;   // log2 224: probabilities <= 2 code to <= 448
 constexpr int kMaxKeyBlocks = 512;   // 32768 keys
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -290,44 +293,48 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
         si[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[ds], si[kb], 0, 0, 0);
       }
     }
-    // scores in the exp2 domain; keys past the sequence masked
+    // scores in the exp2 domain are si * f (f >= 0, so the largest code gives the largest score); keys
+    // past the sequence are masked
     const float f = qscale * s_ka[min(t, ntiles - 1)] * (1.0f / 127.f);
     const int k0 = t * KB;
-    float sc[2][16];
-    float mx = -INFINITY;
+    int mi = INT_MIN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float s = (float)si[kb][e] * f;
-        if (MASK && k0 + 32 * kb + 8 * (e >> 2) + 4 * fh + (e & 3) >= S) s = -INFINITY;
-        sc[kb][e] = s;
-        mx = fmaxf(mx, s);
+        const bool dead = MASK && k0 + 32 * kb + 8 * (e >> 2) + 4 * fh + (e & 3) >= S;
+        mi = max(mi, dead ? INT_MIN : si[kb][e]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // exact running max: rescale whenever it moves
-    if (__any(mx > m_run)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    mi = max(mi, __shfl_xor(mi, 32, 64));
+    const float mx = (float)mi * f;   // a wholly masked tile never moves the reference (tile 0 has a key)
+    // lazy reference max: a query's reference moves to the tile's max only when that is more than one
+    // log2 unit above it, so every probability stays <= 2; a move rescales that query's sums
+    const bool move = mx - m_run > 1.0f;
+    if (__any(move)) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;   // exp2(-inf) = 0 at the start
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         o_l[e] *= alpha;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) o[i][e] *= alpha;
       }
-      m_run = m_new;
+      m_run = move ? mx : m_run;
     }
-    // P <= 1 as E4M3 codes of 448 p: byte b of the operand = key 32 (b >> 4) + 8 ((b & 15) >> 2) + 4 fh + (b & 3)
+    // P <= 2 as E4M3 codes of 224 p = exp2(s - m_run + log2 224) <= 448: byte b of the operand = key
+    // 32 (b >> 4) + 8 ((b & 15) >> 2) + 4 fh + (b & 3)
+    const float m_b = m_run - kLog2PScale;
     v8i pf;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int kb = u >> 2, e0 = 4 * (u & 3);
-      const float p0 = __builtin_amdgcn_exp2f(sc[kb][e0] - m_run) * kE4M3Max;
-      const float p1 = __builtin_amdgcn_exp2f(sc[kb][e0 + 1] - m_run) * kE4M3Max;
-      const float p2 = __builtin_amdgcn_exp2f(sc[kb][e0 + 2] - m_run) * kE4M3Max;
-      const float p3 = __builtin_amdgcn_exp2f(sc[kb][e0 + 3] - m_run) * kE4M3Max;
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+      float a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = __builtin_fmaf((float)si[kb][e0 + i], f, -m_b);
+        if (MASK && k0 + 32 * kb + 8 * (e0 >> 2) + 4 * fh + i >= S) a[i] = -INFINITY;
+      }
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(a[0]), __builtin_amdgcn_exp2f(a[1]), 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(a[2]), __builtin_amdgcn_exp2f(a[3]), w, true);
       pf[u] = w;
     }
     // O^T += V^T P^T on E4M3 codes (scale bytes 127 = 2^0): V^T fragment = 32 contiguous bytes of
