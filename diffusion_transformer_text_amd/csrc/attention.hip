@@ -371,10 +371,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
   }
 }
 
-// Combines the parts of split tile j (grid x = j): thread (query qi = tid / 2, half) of 64 dims.
-// out = sum_p o_p 2^((m_p - m) c) / sum_p l_p 2^((m_p - m) c), m = max_p m_p.
+// Combines the parts of the split tiles: workgroup x covers 16 queries of split tile x / 8; thread
+// (query qi = tid / 16, dims [8 (tid % 16), +8)), so the 16 threads of a query read its 512-byte
+// partial rows contiguously. out = sum_p o_p 2^((m_p - m) c) / sum_p l_p 2^((m_p - m) c), m = max_p m_p.
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
-  const int j = blockIdx.x, qi = threadIdx.x >> 1, half = threadIdx.x & 1;
+  constexpr int QPW = 16;                                // queries per workgroup
+  const int j = blockIdx.x / (BQ / QPW);
+  const int qi = (blockIdx.x % (BQ / QPW)) * QPW + (threadIdx.x >> 4), d0 = (threadIdx.x & 15) * 8;
   const int nq = (p.S + BQ - 1) / BQ;
   const int idx = sp.n_full + j;
   const int bh = idx / nq;
@@ -384,34 +387,30 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
   const float c = p.scale_log2;
   float m = -INFINITY;
   for (int pt = 0; pt < sp.parts; ++pt) m = fmaxf(m, sp.part_ml[2 * ((long)(j * sp.parts + pt) * BQ + qi)]);
-  float acc[64];
+  float acc[8];
 #pragma unroll
-  for (int d = 0; d < 64; ++d) acc[d] = 0.f;
+  for (int d = 0; d < 8; ++d) acc[d] = 0.f;
   float l = 0.f;
   for (int pt = 0; pt < sp.parts; ++pt) {
     const long row = (long)(j * sp.parts + pt) * BQ + qi;
     const float2 ml = *reinterpret_cast<const float2*>(sp.part_ml + 2 * row);
     const float f = __builtin_amdgcn_exp2f((ml.x - m) * c);
     l += ml.y * f;
-    const float4* po = reinterpret_cast<const float4*>(sp.part_o + row * D + 64 * half);
-#pragma unroll
-    for (int d4 = 0; d4 < 16; ++d4) {
-      const float4 v = po[d4];
-      acc[4 * d4] += v.x * f;
-      acc[4 * d4 + 1] += v.y * f;
-      acc[4 * d4 + 2] += v.z * f;
-      acc[4 * d4 + 3] += v.w * f;
-    }
+    const float4* po = reinterpret_cast<const float4*>(sp.part_o + row * D + d0);
+    const float4 v0 = po[0], v1 = po[1];
+    acc[0] += v0.x * f;
+    acc[1] += v0.y * f;
+    acc[2] += v0.z * f;
+    acc[3] += v0.w * f;
+    acc[4] += v1.x * f;
+    acc[5] += v1.y * f;
+    acc[6] += v1.z * f;
+    acc[7] += v1.w * f;
   }
   const float inv = 1.0f / l;
-  uint16_t* orow = p.out + ((long)b * p.S + q) * p.ld_out + h * D + 64 * half;
-#pragma unroll
-  for (int d4 = 0; d4 < 16; ++d4) {
-    uint2 w;
-    w.x = pack2_bf16(acc[4 * d4] * inv, acc[4 * d4 + 1] * inv);
-    w.y = pack2_bf16(acc[4 * d4 + 2] * inv, acc[4 * d4 + 3] * inv);
-    *reinterpret_cast<uint2*>(orow + 4 * d4) = w;
-  }
+  uint2* orow = reinterpret_cast<uint2*>(p.out + ((long)b * p.S + q) * p.ld_out + h * D + d0);   // 8-byte aligned
+  orow[0] = make_uint2(pack2_bf16(acc[0] * inv, acc[1] * inv), pack2_bf16(acc[2] * inv, acc[3] * inv));
+  orow[1] = make_uint2(pack2_bf16(acc[4] * inv, acc[5] * inv), pack2_bf16(acc[6] * inv, acc[7] * inv));
 }
 
 // Compute units of the current device (cached per device).
@@ -498,7 +497,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, void* ws, siz
   }
   const long grid = (long)sp.n_full + (long)sp.n_split * sp.parts;
   hipLaunchKernelGGL(attention_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, sp);
-  if (sp.n_split > 0) hipLaunchKernelGGL(merge_kernel, dim3((unsigned)sp.n_split), dim3(256), 0, stream, a, sp);
+  if (sp.n_split > 0)
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)sp.n_split * (BQ / 16)), dim3(256), 0, stream, a, sp);
   return hipGetLastError();
 }
 

@@ -134,13 +134,24 @@ __global__ __launch_bounds__(256) void q8k8_quant_kernel(AttnQ8Args p) {
   }
 }
 
-// grid (H, B), 128 threads: V's channel maxima over all key blocks.
-__global__ __launch_bounds__(128) void va_reduce_kernel(AttnQ8Args p) {
+// grid (H, B), 1024 threads: V's channel maxima over all key blocks. Thread (group g = tid / 128,
+// dim d = tid % 128) reduces key blocks g, g + 8, ... (independent loads, several in flight), then
+// the 8 groups combine through LDS.
+__global__ __launch_bounds__(1024) void va_reduce_kernel(AttnQ8Args p) {
+  __shared__ float s_m[8][D];
   const long bh = (long)blockIdx.y * p.H + blockIdx.x;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x & (D - 1), g = threadIdx.x >> 7;
+  const float* src = p.vpart + bh * p.nblk * D + d;
   float m = 0.f;
-  for (int t = 0; t < p.nblk; ++t) m = fmaxf(m, p.vpart[(bh * p.nblk + t) * D + d]);
-  p.va[bh * D + d] = m;
+#pragma unroll 4
+  for (int t = g; t < p.nblk; t += 8) m = fmaxf(m, src[(long)t * D]);
+  s_m[g][d] = m;
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int j = 1; j < 8; ++j) m = fmaxf(m, s_m[j][d]);
+    p.va[bh * D + d] = m;
+  }
 }
 
 // grid (key blocks, H, B), 256 threads: this block's 64 keys of V as E4M3 codes, transposed and
@@ -448,7 +459,7 @@ hipError_t launch_attention_q8(const AttnArgs& a, void* ws, size_t ws_bytes, hip
   p.vpart = (float*)c;
   const dim3 qgrid((unsigned)nblk, (unsigned)a.H, (unsigned)a.B);
   hipLaunchKernelGGL(q8k8_quant_kernel, qgrid, dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(va_reduce_kernel, dim3((unsigned)a.H, (unsigned)a.B), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(va_reduce_kernel, dim3((unsigned)a.H, (unsigned)a.B), dim3(1024), 0, stream, p);
   hipLaunchKernelGGL(vt8_quant_kernel, qgrid, dim3(256), 0, stream, p);
   const long wgs = (long)((a.S + 127) / 128) * a.H * a.B;
   hipLaunchKernelGGL(attention_q8_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, p);
