@@ -413,26 +413,13 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
   orow[1] = make_uint2(pack2_bf16(acc[4] * inv, acc[5] * inv), pack2_bf16(acc[6] * inv, acc[7] * inv));
 }
 
-// Compute units of the current device (cached per device).
-int cu_count() {
-  static int cache[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 // The split plan: `slots` workgroups fit on the chip at once (two per CU); whole rounds stay unsplit,
 // and a last round holding at most half the slots is split into parts filling it.
 AttnSplit split_plan(int B, int S, int H) {
   AttnSplit sp{};
   const long total = (long)((S + BQ - 1) / BQ) * H * B;
   const int ntiles = (S + BKV - 1) / BKV;
-  const long slots = 2L * cu_count();
+  const long slots = 2L * device_cu_count();
   sp.n_full = (int)total;
   sp.n_split = 0;
   sp.parts = 1;
@@ -470,6 +457,19 @@ __global__ void rope_inplace_kernel(uint16_t* qkv, int B, int S, int T, int grid
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 size_t attention_split_workspace(int B, int S, int H) {
   const AttnSplit sp = split_plan(B, S, H);

@@ -55,6 +55,8 @@ struct GemmArgs {
 
 // Picks a tile shape for (M, N) and launches. Returns hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream);
+// Compute units of the current device (cached per device).
+int device_cu_count();
 // The same product with MXFP8 operands (needs N % 256 == 0 and K % 256 == 0); same epilogues.
 hipError_t launch_gemm_mxfp8(const GemmArgs& a, int epi, hipStream_t stream);
 // Interleave W_gate_up [2F, D] = [gate rows | up rows] into 32-row groups [g0 | u0 | g1 | u1 | ...].

@@ -54,8 +54,9 @@ int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t hea
  * integration guide, "Quality tier" and its attention modes). Reading (the pages give no formula): Q
  * symmetric INT8 per token and head (scale amax/127), K symmetric INT8 per block of 64 consecutive keys
  * and head, V FP8 E4M3 per channel (scale amax/448); exact integer Q K^T, fp32 online softmax over
- * the 64-key blocks with the exact running max, each block's probabilities rounded to E4M3 on the
- * scale 448, the normaliser summing the same rounded probabilities; fp32 accumulation.
+ * the 64-key blocks whose reference max per query moves to a block's max only when that exceeds it by
+ * more than a factor 2 in probability, each probability (<= 2) rounded to E4M3 on the scale 224, the
+ * normaliser summing the same rounded probabilities; fp32 accumulation.
  *   qkv: device bf16 [B, S, 3*H*128] (q | k | v, q and k already rotated where wanted), 16-byte
  *   aligned; out: device bf16 [B, S, H*128]. ws: device scratch of moss_attention_q8_workspace(B, S, H)
  *   bytes, 256-byte aligned, owned by the caller; it receives the codes and scales (contents undefined

@@ -37,6 +37,23 @@ def test_gemm_small_integers_bitwise(M, N, K):
     np.testing.assert_array_equal(got[rows], ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(8704, 3072, 8192), (8700, 9216, 3072), (4352, 16384, 3072), (2816, 6144, 3072)])
+def test_gemm_tile_tail_shapes_bitwise_full_output(M, N, K):
+    """Shapes whose 256 x 256 tiles leave a partial last round on a 256-CU device (152, 200, 64 and 8
+    leftover tiles; a ragged last tile row at M = 8700), checked over the WHOLE output: small integers
+    make every fp32 sum exact in any order, so every element must match bit for bit. The reference is
+    torch's CPU fp32 product of the same integers (exact: every partial sum is an integer below 2^24)."""
+    log(f"gemm full-output int M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 3 * N + K)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    W = rng.integers(-4, 5, (N, K)).astype(np.float32)
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    dt.moss_gemm_bf16(dev_bf16(f32_to_bf16_bits(A), torch), dev_bf16(f32_to_bf16_bits(W), torch), out)
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(A) @ torch.from_numpy(W).T
+    assert torch.equal(out.cpu(), ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(8704, 9216, 3072), (257, 384, 128)])
 def test_gemm_random_vs_fp64(M, N, K):
     log(f"gemm random M={M} N={N} K={K}")
