@@ -202,6 +202,15 @@ def test_attention_2048_sequence_sampled_rows():
     assert err <= REL_L2_BF16, err
 
 
+def test_attention_split_tail_ragged_sampled_rows():
+    """24 heads x 22 query tiles = 528 workgroups on a 256-CU device (512 slots): the last 16 tiles
+    (head 23, query tiles 6-21, the last one ragged: S = 2781 = 21 x 128 + 93) are split along their
+    key tiles into 8 parts merged afterwards: head 23's sampled rows from 768 on (the last row among
+    them) come from those parts, head 0's from whole tiles."""
+    err = _attn_case(1, 77, 52, 52, 24, seed=4, rows_per_head=40, heads=[0, 23])
+    assert err <= REL_L2_BF16, err
+
+
 def test_attention_special_cases():
     log("attention special cases")
     # identical keys -> mean of V; one dominant key -> that key's value
