@@ -675,7 +675,9 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream) {
   const bool big_n = (a.N % 256 == 0);
   const long tiles256 = (long)((a.M + 255) / 256) * (a.N / 256);
   const bool fits32 = 2L * a.M * a.lda < (1L << 31) && 2L * a.N * a.ldw < (1L << 31);   // buffer byte offsets
-  if (big_n && epi != EPI_F32_UNPATCH && a.M > 1024 && tiles256 >= 256) {
+  // 256 x 256 tiles from half a round of the chip on: one batch-1 out / down projection (204 tiles)
+  // runs 25-30 % faster on them than as 816 tiles of 128 x 128 (measured)
+  if (big_n && epi != EPI_F32_UNPATCH && a.M > 1024 && tiles256 >= 128) {
     if (fits32 && a.K % (4 * BK2) == 0) return launch_tile_deep<256, 256, 2, 4>(a, epi, stream);
     return launch_tile<256, 256, 2, 4>(a, epi, stream);
   }

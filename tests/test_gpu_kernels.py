@@ -37,10 +37,12 @@ def test_gemm_small_integers_bitwise(M, N, K):
     np.testing.assert_array_equal(got[rows], ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(8704, 3072, 8192), (8700, 9216, 3072), (4352, 16384, 3072), (2816, 6144, 3072)])
+@pytest.mark.parametrize("M,N,K", [(8704, 3072, 8192), (8700, 9216, 3072), (4352, 16384, 3072), (2816, 6144, 3072),
+                                   (4352, 3072, 3072), (3000, 3072, 1024)])
 def test_gemm_tile_tail_shapes_bitwise_full_output(M, N, K):
     """Shapes whose 256 x 256 tiles leave a partial last round on a 256-CU device (152, 200, 64 and 8
-    leftover tiles; a ragged last tile row at M = 8700), checked over the WHOLE output: small integers
+    leftover tiles; a ragged last tile row at M = 8700 and M = 3000) or fill less than one round (204
+    and 144 tiles: a batch-1 out projection), checked over the WHOLE output: small integers
     make every fp32 sum exact in any order, so every element must match bit for bit. The reference is
     torch's CPU fp32 product of the same integers (exact: every partial sum is an integer below 2^24)."""
     log(f"gemm full-output int M={M} N={N} K={K}")
