@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = (kb == 0 ? 2 : 0); e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
-    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+    return max_xor32(mx);
   };
   // The running max only moves when a score exceeds it by more than 2^8 in the exp2 domain: with a
   // stale max the probabilities stay below 256 (exact in fp32, same relative precision in bf16), the
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
         mx = fmaxf(mx, fmaxf(s_next[i >> 3][(2 * i) & 15], s_next[i >> 3][(2 * i + 1) & 15]));
         __builtin_amdgcn_sched_barrier(0);
       }
-      mx_next = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx_next = fmaxf(mx, __shfl_xor(mx, 32, 64));   // (the VALU exchange here costs a spill)
     }
     mx_cur = mx_next;
   };
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
     pv_update(((t - t_begin) & 1) ? sV1 : sV0, pf);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = sum_xor32(l_run);
   if (part_slot >= 0) {
     // one part of a split tile: the unnormalised output and the (max, sum) pair it is relative to
     const long qrow = (long)part_slot * BQ + wave * 32 + fr;

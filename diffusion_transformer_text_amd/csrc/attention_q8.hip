@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
         const bool dead = MASK && k0 + 32 * kb + 8 * (e >> 2) + 4 * fh + (e & 3) >= S;
         mi = max(mi, dead ? INT_MIN : si[kb][e]);
       }
-    mi = max(mi, __shfl_xor(mi, 32, 64));
+    mi = max_xor32(mi);
     const float mx = (float)mi * f;   // a wholly masked tile never moves the reference (tile 0 has a key)
     // lazy reference max: a query's reference moves to the tile's max only when that is more than one
     // log2 unit above it, so every probability stays <= 2; a move rescales that query's sums

@@ -92,6 +92,23 @@ __device__ __forceinline__ long mx_scale_byte(int kb, long r, long ld) {
   return ((long)(2 * (kb >> 3) + (kb & 1)) * ld + r) * 4 + ((kb >> 1) & 3);
 }
 
+// Combination with lane l ^ 32 in one VALU instruction: gfx950's v_permlane32_swap, given the same
+// register twice, returns x of lane (l & 31) and x of lane (l & 31) + 32 (checked on the hardware with
+// an in-bounds probe). Unlike __shfl_xor (ds_bpermute) it does not go through LDS, so waiting for it
+// does not also wait for the wave's outstanding LDS reads.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int max_xor32(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wave-wide (64 lanes) sum.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -100,7 +100,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, floatx16 (&acc)[T:
             h[g][e] = round_bf16(silu_f32(acc[i][2 * q][4 * g + e]) * acc[i][2 * q + 1][4 * g + e]);
             amax = fmaxf(amax, fabsf(h[g][e]));
           }
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        amax = max_xor32(amax);
         const int ex = mx_exponent(amax);
         const float inv = mx_inv_scale(ex);
         const int hb = (n0 + wn * T::WN) / 2 + q * 32;
