@@ -331,3 +331,55 @@ def test_q8_attention_full_block_sampled_rows():
     assert max(errs["attention"]) <= REL_L2_Q8_ATTN
     assert max(errs["block"]) <= REL_L2_BF16
     assert max(errs["block_update"]) <= REL_L2_FP8_CHAIN
+
+
+def _block_twice(model, layer, xbits, T, gh, gw, mod, taps_spec):
+    """The block on two copies of x: once with taps (every MXFP8 activation written by the separate
+    quantizer from its bf16 value) and once without (the producers write the codes themselves)."""
+    x_fused = dev_bf16(xbits, torch)
+    x_sep = dev_bf16(xbits, torch)
+    M = xbits.shape[0] * xbits.shape[1]
+    taps = {k: torch.empty((M, n), dtype=t, device="cuda") for k, n, t in taps_spec}
+    model.moss_dit_block(layer, x_fused, T, gh, gw, mod)
+    model.moss_dit_block(layer, x_sep, T, gh, gw, mod, taps=taps)
+    torch.cuda.synchronize()
+    return x_fused, x_sep
+
+
+@pytest.mark.parametrize("attention_mode", [0, 1])
+def test_fp8_fused_quantization_equals_separate_quantizer_bitwise(attention_mode):
+    """Without taps the LayerNorm-modulation kernel, the SwiGLU epilogue and the attention kernels write
+    the MXFP8 codes and scales of their bf16-rounded outputs themselves; with taps every activation
+    goes through the separate quantizer. Both quantize the same bf16 values, so the block's output
+    must be the same bits."""
+    m, inp, W, ocfg = tiny(1.0, precision=1, attention_mode=attention_mode)
+    D, T, gh, gw, B = ocfg.hidden, 32, 8, 8, 2
+    S = T + gh * gw
+    rng = np.random.default_rng(21)
+    xbits = synth.bf16_normal_bits(rng, (B, S, D))
+    mod = torch.empty((B, m.mod_stride), dtype=torch.bfloat16, device="cuda")
+    m.moss_dit_modulation([0.7, 0.2], mod)
+    log(f"fp8 fused vs separate quantizers, tiny, attention_mode={attention_mode}")
+    a, b = _block_twice(m, 1, xbits, T, gh, gw, mod, [("o", D, torch.bfloat16)])
+    assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("attention_mode", [0, 1])
+def test_fp8_fused_quantization_equals_separate_quantizer_full_size(attention_mode):
+    """The same at the full size (batch 2, 256 text + 4096 image tokens: the exact attention's
+    key-split tail and merge are in play)."""
+    log(f"fp8 fused vs separate quantizers, full size, attention_mode={attention_mode}")
+    shape = synth.Shape(num_layers=1)
+    w = synth.torch_weights(shape, seed=4, device="cuda", mod_scale=50.0)
+    cfg = dt.moss_dit_config_init(num_layers=1, gemm_precision=1, attention_mode=attention_mode)
+    model = dt.MossDiT(cfg, w)
+    D = cfg.hidden
+    rng = np.random.default_rng(22)
+    B = 2
+    xbits = synth.bf16_normal_bits(rng, (B, FS, D))
+    mod = torch.empty((B, model.mod_stride), dtype=torch.bfloat16, device="cuda")
+    model.moss_dit_modulation([0.9, 0.4], mod)
+    a, b = _block_twice(model, 0, xbits, FT, FGH, FGW, mod, [("o", D, torch.bfloat16)])
+    model.close()
+    assert torch.equal(a, b)
