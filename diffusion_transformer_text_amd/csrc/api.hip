@@ -585,6 +585,11 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   at.ld_qkv = 3L * D;
   at.ld_out = D;
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+  if (fuse) {   // the attention writes the out projection's MXFP8 input itself
+    at.q8 = c.q8;
+    at.s8 = c.s8;
+    at.lds8 = c.lds8;
+  }
   {
     ProfScope ps(H, PC_ATTN, st);
     if (H->q8attn())
@@ -601,7 +606,7 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
   g.gate_stride = mod_stride;
   {
     ProfScope ps(H, PC_OUT, st);
-    HIP_TRY(H, project(H, c, g, w.out8, EPI_GATED_RES, st));
+    HIP_TRY(H, project(H, c, g, w.out8, EPI_GATED_RES, st, fuse ? c.q8 : nullptr, fuse ? c.s8 : nullptr));
   }
   HIP_TRY(H, tap_copy(taps ? taps->x1 : nullptr, x, (size_t)M * D * 2));
   // A8: LN2 + modulation

@@ -356,7 +356,19 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
   }
   // ---- normalise and store: lane holds query my_q, d = 32 db + 8 g + 4 fh + [0, 4) ----
   const float inv = 1.0f / l_tot;
-  if (my_q < S) {
+  if (my_q < S && p.q8) {                 // MXFP8 codes (both lanes of a query take this branch)
+    const long row = (long)b * S + my_q;
+    uint8_t* crow = p.q8 + row * DM + h * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      float v[4][4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[gg][e] = o[db][4 * gg + e] * inv;
+      mx_store_pair_block(v, fh, crow + 32 * db, p.s8 + mx_scale_byte((h * D + 32 * db) / 32, row, p.lds8));
+    }
+  } else if (my_q < S) {
     uint16_t* orow = p.out + ((long)b * S + my_q) * p.ld_out + h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -408,7 +420,26 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
     acc[7] += v1.w * f;
   }
   const float inv = 1.0f / l;
-  uint2* orow = reinterpret_cast<uint2*>(p.out + ((long)b * p.S + q) * p.ld_out + h * D + d0);   // 8-byte aligned
+  const long row = (long)b * p.S + q;
+  if (p.q8) {
+    // MXFP8 codes: a 32-column block is 4 threads (consecutive lanes, the same query)
+    float r[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      r[d] = round_bf16(acc[d] * inv);
+      amax = fmaxf(amax, fabsf(r[d]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int ex = mx_exponent(amax);
+    const float sc = mx_inv_scale(ex);
+    *reinterpret_cast<uint2*>(p.q8 + row * (p.H * D) + h * D + d0) =
+        make_uint2(mx_pack4(r[0], r[1], r[2], r[3], sc), mx_pack4(r[4], r[5], r[6], r[7], sc));
+    if ((threadIdx.x & 3) == 0) p.s8[mx_scale_byte((h * D + d0) / 32, row, p.lds8)] = (uint8_t)(ex + 127);
+    return;
+  }
+  uint2* orow = reinterpret_cast<uint2*>(p.out + row * p.ld_out + h * D + d0);   // 8-byte aligned
   orow[0] = make_uint2(pack2_bf16(acc[0] * inv, acc[1] * inv), pack2_bf16(acc[2] * inv, acc[3] * inv));
   orow[1] = make_uint2(pack2_bf16(acc[4] * inv, acc[5] * inv), pack2_bf16(acc[6] * inv, acc[7] * inv));
 }
@@ -480,6 +511,7 @@ size_t attention_split_workspace(int B, int S, int H) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, void* ws, size_t ws_bytes) {
   if (a.S <= 0 || a.B <= 0) return hipSuccess;
   if (a.ld_qkv % 8 != 0 || a.ld_out % 4 != 0) return hipErrorInvalidValue;
+  if (a.q8 && (!a.s8 || (a.H * D) % 256 != 0 || a.lds8 < (long)a.B * a.S)) return hipErrorInvalidValue;
   const long wgs = (long)((a.S + BQ - 1) / BQ) * a.H * a.B;
   if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
   if (2L * a.S * a.ld_qkv > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit buffer offsets per sample

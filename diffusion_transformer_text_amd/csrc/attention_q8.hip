@@ -394,7 +394,25 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);       // the look-ahead copies land before the LDS is released
 
   // out = O / l, with V's channel scale: lane holds query my_q, d = 32 db + 8 g + 4 fh + [0, 4)
-  if (my_q < S) {
+  if (my_q < S && p.out8) {               // MXFP8 codes (both lanes of a query take this branch)
+    const float inv = 1.0f / (kE4M3Max * o_l[0]);
+    const long row = (long)b * S + my_q;
+    uint8_t* crow = p.out8 + row * DM + h * D;
+    const float* va = p.va + bh * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      float v[4][4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float4 sv = *reinterpret_cast<const float4*>(va + 32 * db + 8 * gg + 4 * fh);
+        v[gg][0] = o[db][4 * gg] * sv.x * inv;
+        v[gg][1] = o[db][4 * gg + 1] * sv.y * inv;
+        v[gg][2] = o[db][4 * gg + 2] * sv.z * inv;
+        v[gg][3] = o[db][4 * gg + 3] * sv.w * inv;
+      }
+      mx_store_pair_block(v, fh, crow + 32 * db, p.out8_scale + mx_scale_byte((h * D + 32 * db) / 32, row, p.lds8));
+    }
+  } else if (my_q < S) {
     const float inv = 1.0f / (kE4M3Max * o_l[0]);
     uint16_t* orow = p.out + ((long)b * S + my_q) * p.ld_out + h * D;
     const float* va = p.va + bh * D;
@@ -429,6 +447,7 @@ hipError_t launch_attention_q8(const AttnArgs& a, void* ws, size_t ws_bytes, hip
   const long nblk = (a.S + KB - 1) / KB;
   const long DM = (long)a.H * D;
   if (nblk > kMaxKeyBlocks) return hipErrorInvalidValue;
+  if (a.q8 && (!a.s8 || DM % 256 != 0 || a.lds8 < (long)a.B * a.S)) return hipErrorInvalidValue;
   // 32-bit buffer offsets: K codes per sample and all of V^T
   if ((long)a.S * DM > 0x7fffffffL || (long)a.B * a.H * D * nblk * KB > 0x7fffffffL) return hipErrorInvalidValue;
   AttnQ8Args p;
@@ -441,6 +460,9 @@ hipError_t launch_attention_q8(const AttnArgs& a, void* ws, size_t ws_bytes, hip
   p.ld_out = a.ld_out;
   p.scale_log2 = a.scale_log2;
   p.nblk = (int)nblk;
+  p.out8 = a.q8;
+  p.out8_scale = a.s8;
+  p.lds8 = a.lds8;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* c = static_cast<char*>(ws);
   const size_t M = (size_t)a.B * a.S;

@@ -109,6 +109,30 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One 32-element MX block held by the lane pair (l, l ^ 32) in the MFMA output layout: this lane's
+// 16 values v[g][e] sit at block positions 8 g + 4 h + e (h = lane / 32), the partner's at the other
+// 16. Rounds them to bf16, writes this lane's four code words at codes + 8 g + 4 h and, from the h == 0
+// lane, the scale byte (biased exponent) at *scale -- the bytes the separate MXFP8 quantizer writes
+// for the same bf16 values. Both lanes of the pair must execute it.
+__device__ __forceinline__ void mx_store_pair_block(const float (&v)[4][4], int h, uint8_t* codes, uint8_t* scale) {
+  float r[4][4];
+  float amax = 0.f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[g][e] = round_bf16(v[g][e]);
+      amax = fmaxf(amax, fabsf(r[g][e]));
+    }
+  amax = max_xor32(amax);
+  const int ex = mx_exponent(amax);
+  const float inv = mx_inv_scale(ex);
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<uint32_t*>(codes + 8 * g + 4 * h) = mx_pack4(r[g][0], r[g][1], r[g][2], r[g][3], inv);
+  if (h == 0) *scale = (uint8_t)(ex + 127);
+}
+
 // Wave-wide (64 lanes) sum.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -92,6 +92,13 @@ struct AttnArgs {
   int B, S, H;
   long ld_qkv, ld_out;
   float scale_log2;   // log2(e) / sqrt(d)
+  // Optional MXFP8 output (the FP8 tier's out-projection input): when q8 is set, row r = b S + token is
+  // written as the E4M3 codes of its bf16-rounded values, q8[r * H * 128 + col], with one E8M0 scale
+  // byte per 32 columns in the scale words s8 (ld = lds8 >= B S) -- what the separate quantizer would
+  // write; out is then not written. Needs H * 128 % 256 == 0.
+  uint8_t* q8 = nullptr;
+  uint8_t* s8 = nullptr;
+  long lds8 = 0;
 };
 // ws (optional, attention_split_workspace bytes): when the query tiles leave the last round of
 // workgroups on the chip partly empty, those leftover tiles are split along the keys into parts that
@@ -116,6 +123,9 @@ struct AttnQ8Args {
   float* ka;                // [B][H][nblk] per-block amax of k
   float* va;                // [B][H][128] per-channel amax of v
   float* vpart;             // [B][H][nblk][128] per-block channel maxima of v
+  uint8_t* out8;            // optional MXFP8 output (AttnArgs::q8 / s8 / lds8)
+  uint8_t* out8_scale;
+  long lds8;
 };
 size_t attention_q8_workspace(int B, int S, int H);
 hipError_t launch_attention_q8(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
