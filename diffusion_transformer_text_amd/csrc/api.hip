@@ -544,8 +544,8 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
     if (!taps || !dst) return hipSuccess;
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
   };
-  // FP8 tier without taps: the LN outputs and h go straight to MXFP8 codes (written by their
-  // producers), the bf16 copies are not written
+  // FP8 tier without taps: the LN outputs, the attention output and h go straight to MXFP8 codes
+  // (written by their producers), their bf16 copies are not written
   const bool fuse = H->fp8() && !taps;
   auto ln = [&](const uint16_t* shift, const uint16_t* scale) {
     LnModArgs l = ln_args(x, fuse ? nullptr : c.a, M, D, S, shift, scale, mod_stride, k.norm_eps);
