@@ -46,7 +46,8 @@ Parity status of each function (pins in tests/test_oracle_pins.py):
                               dequantized operands (the pinned attention above), ragged last block;
                               V constant over keys and a single key give V exactly (convex weights);
                               a dominant key selects its V row; within a few percent of the exact
-                              attention on random inputs
+                              attention on random inputs; the lazy reference max against a hand
+                              schedule of three blocks (no move at +0.5 log2, a move at +1.5)
 """
 from .moss_oracle import *  # noqa: F401,F403
 from .moss_oracle import (Config, attention, bf16_round, block, cfg_combine, embed, euler_step,  # noqa
