@@ -139,6 +139,29 @@ def test_forward_vs_oracle(mod_scale):
     assert e_d <= REL_L2_BF16 * (5 if mod_scale == 1.0 else 1)
 
 
+@pytest.mark.parametrize("lat_h,lat_w,T,B", [(16, 24, 7, 3), (24, 8, 1, 1)])
+def test_forward_non_square_latent_odd_text_vs_oracle(lat_h, lat_w, T, B):
+    """Aspect ratios other than 1:1 (a 8x12 and a 12x4 patch grid: the rotary rows and columns and
+    the unpatchify differ), odd text lengths (7 and 1 text tokens: a ragged attention tile) and
+    batches of 3 and 1 with different sigmas and skip sets per sample, against the oracle."""
+    m, w, inp, W, ocfg, _ = model(50.0)
+    log(f"tiny forward latent {lat_h}x{lat_w} T={T} B={B}")
+    rng = np.random.default_rng(lat_h * 100 + lat_w + T)
+    lat = rng.standard_normal((B, ocfg.latent_channels, lat_h, lat_w)).astype(np.float32)
+    txt = rng.standard_normal((B, T, ocfg.hidden)).astype(np.float32)
+    sig = [0.9, 0.4, 0.1][:B]
+    skips = [set(), {1}, {0, 1}][:B]
+    vel = torch.empty((B, ocfg.latent_channels, lat_h, lat_w), dtype=torch.float32, device="cuda")
+    m.moss_dit_forward(torch.from_numpy(lat).cuda(), torch.from_numpy(txt).cuda(), sig, vel,
+                       skip_mask=[sum(1 << l for l in sk) for sk in skips])
+    torch.cuda.synchronize()
+    ref = O.forward(lat.astype(np.float64), txt.astype(np.float64), sig, W, ocfg, skip=skips, mirror=True)
+    v = vel.cpu().numpy().astype(np.float64)
+    errs = [rel_l2(v[b], ref[b]) for b in range(B)]
+    log(f"rel-L2 per sample {[f'{e:.2e}' for e in errs]}")
+    assert max(errs) <= REL_L2_BF16
+
+
 @pytest.mark.parametrize("mod_scale", MODES)
 def test_two_sampling_steps_vs_oracle(mod_scale):
     """2 Euler steps, shift 5, CFG 3, uncond_skip_layers=[1], window 0.01..1.0: step 0 runs full
