@@ -153,7 +153,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py measures one GPU: the denoising step runs on one MI355X and this build has no multi-GPU "
+        log("bench.py measures one GPU: the denoising step runs on one MI355X and the library has no multi-GPU "
             "path (CFG-parallel / Ulysses sharding is a design note only). Run it with --gpus 1.")
         sys.exit(2)
 
