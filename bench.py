@@ -410,7 +410,8 @@ def main():
             model8.close()
             del model8
         fp8["format"] = ("OCP MXFP8 GEMMs (E4M3, E8M0 scale per 32 along K; weights quantized at creation, "
-                         "activations before each block projection); 8-bit attention: INT8 Q (per token) and "
+                         "activations written as MXFP8 by the kernels that produce them); 8-bit attention: INT8 Q "
+                         "(per token) and "
                          "K (per 64-key block), E4M3 P and V (per channel)")
 
     cpu = None
