@@ -30,7 +30,11 @@ int moss_dit_modulation(moss_dit* h, const float* sigma, int32_t batch, void* mo
  *   x1     bf16 [rows, D]   residual after the attention branch
  *   a2     bf16 [rows, D]   LN2-modulated input of the FFN
  *   h      bf16 [rows, F]   SiLU(a2 W_g^T) * (a2 W_u^T)
- *   ffn    fp32 [rows, D]   h W_down^T (branch output before the gated add) */
+ *   ffn    fp32 [rows, D]   h W_down^T (branch output before the gated add)
+ * In the FP8 tier (gemm_precision 1) the kernels that produce a projection's input write its MXFP8
+ * codes themselves and skip the bf16 copy; when taps is given, every such input is written in bf16
+ * and quantized by the separate MXFP8 quantizer instead -- the same bits, so taps do not change the
+ * block's result. */
 typedef struct {
   uint32_t struct_size;
   void *a, *qkv, *o, *attn, *x1, *a2, *h, *ffn;
@@ -46,7 +50,11 @@ int moss_dit_block(moss_dit* h, int32_t layer, void* x, int32_t batch, int32_t t
 
 /* Exact attention at head_dim 128 on packed qkv (device bf16 [B, S, 3*H*128], q | k | v), out device
  * bf16 [B, S, H*128]. rope != 0: q and k of the image rows (sequence index >= text_len, grid of width
- * grid_w) are first turned by the axial rotary embedding (theta 1e4) -- in place, qkv is modified. */
+ * grid_w) are first turned by the axial rotary embedding (theta 1e4) -- in place, qkv is modified.
+ * When the query tiles leave the last round of workgroups on the chip partly empty, the leftover tiles
+ * are split along the keys and merged; their partial results go to a temporary device allocation,
+ * and the call then synchronizes `stream` before returning (a test and measurement entry; the model
+ * path keeps that scratch in its handle's workspace). */
 int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, int32_t text_len,
                    int32_t grid_w, int32_t rope, void* stream);
 
