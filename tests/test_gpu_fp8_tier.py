@@ -366,20 +366,21 @@ def test_fp8_fused_quantization_equals_separate_quantizer_bitwise(attention_mode
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("attention_mode", [0, 1])
-def test_fp8_fused_quantization_equals_separate_quantizer_full_size(attention_mode):
-    """The same at the full size (batch 2, 256 text + 4096 image tokens: the exact attention's
-    key-split tail and merge are in play)."""
-    log(f"fp8 fused vs separate quantizers, full size, attention_mode={attention_mode}")
+@pytest.mark.parametrize("B,T,G", [(2, FT, FGH), (1, 4096, 128)])
+def test_fp8_fused_quantization_equals_separate_quantizer_full_size(attention_mode, B, T, G):
+    """The same at the full sizes: batch 2 with 256 text + 4096 image tokens (the exact attention's
+    key-split tail and merge are in play), and one sample at 2048^2 with a 4096-token prompt
+    (S = 20480: 320 key blocks for the 8-bit attention)."""
+    log(f"fp8 fused vs separate quantizers, full size B={B} T={T} grid {G}x{G}, attention_mode={attention_mode}")
     shape = synth.Shape(num_layers=1)
     w = synth.torch_weights(shape, seed=4, device="cuda", mod_scale=50.0)
     cfg = dt.moss_dit_config_init(num_layers=1, gemm_precision=1, attention_mode=attention_mode)
     model = dt.MossDiT(cfg, w)
     D = cfg.hidden
     rng = np.random.default_rng(22)
-    B = 2
-    xbits = synth.bf16_normal_bits(rng, (B, FS, D))
+    xbits = synth.bf16_normal_bits(rng, (B, T + G * G, D))
     mod = torch.empty((B, model.mod_stride), dtype=torch.bfloat16, device="cuda")
-    model.moss_dit_modulation([0.9, 0.4], mod)
-    a, b = _block_twice(model, 0, xbits, FT, FGH, FGW, mod, [("o", D, torch.bfloat16)])
+    model.moss_dit_modulation([0.9, 0.4][:B], mod)
+    a, b = _block_twice(model, 0, xbits, T, G, G, mod, [("o", D, torch.bfloat16)])
     model.close()
     assert torch.equal(a, b)
