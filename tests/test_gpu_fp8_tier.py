@@ -29,7 +29,7 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import REL_L2_BF16, dev_bf16, dev_weights, host_bf16, log, oracle_cfg, rel_l2
+from tests.gpu_util import REL_L2_BF16, REL_L2_FP32, dev_bf16, dev_weights, host_bf16, log, oracle_cfg, rel_l2
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -384,3 +384,36 @@ def test_fp8_fused_quantization_equals_separate_quantizer_full_size(attention_mo
     a, b = _block_twice(model, 0, xbits, T, G, G, mod, [("o", D, torch.bfloat16)])
     model.close()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("attention_mode", [0, 1])
+@pytest.mark.parametrize("slg_scale", [0.0, 2.5])
+def test_fp8_sample_step_equals_guidance_of_its_forward(attention_mode, slg_scale):
+    """The FP8 tier through moss_sample_step (CFG 3, the negative pass skipping block 1, and with
+    slg_scale > 0 a third row: the conditional pass skipping block 1) against the guidance combine
+    and Euler update of the same rows' velocities from moss_dit_forward, in fp64: rows are computed
+    independently, so only the fp32 guidance arithmetic may differ."""
+    m, inp, W, ocfg = tiny(50.0, precision=1, attention_mode=attention_mode)
+    log(f"fp8 sample step vs forward, attention_mode={attention_mode} slg={slg_scale}")
+    step = 1
+    sig = dt.moss_sigmas(2, 5.0)
+    x0 = torch.from_numpy(inp.latents).cuda()
+    tc = torch.from_numpy(inp.text_cond).cuda()
+    tu = torch.from_numpy(inp.text_uncond).cuda()
+    x = x0.clone()
+    m.moss_sample_step(x, tc, tu, sig, step, cfg_scale=3.0, uncond_skip_layers=[1], slg_scale=slg_scale)
+    rows = 3 if slg_scale > 0 else 2
+    lat = torch.cat([x0] * rows).contiguous()
+    txt = torch.cat([tc, tu, tc][:rows]).contiguous()
+    vel = torch.empty_like(lat)
+    m.moss_dit_forward(lat, txt, [float(sig[step])] * rows, vel, skip_mask=[0, 1 << 1, 1 << 1][:rows])
+    torch.cuda.synchronize()
+    v = vel.cpu().numpy().astype(np.float64)
+    guided = v[1:2] + 3.0 * (v[0:1] - v[1:2])
+    if rows == 3:
+        guided = guided + slg_scale * (v[0:1] - v[2:3])
+    x0n = x0.cpu().numpy().astype(np.float64)
+    d_ref = float(sig[step + 1] - sig[step]) * guided
+    d_got = x.cpu().numpy().astype(np.float64) - x0n
+    assert np.isfinite(d_got).all()
+    assert rel_l2(d_got, d_ref) <= REL_L2_FP32
