@@ -12,6 +12,9 @@ the GPU, against the oracle run with gemm_precision "mxfp8".
 * Full size: one joint block (hidden 3072, 24 heads, FFN 8192, batch 2, 256 text + 4096 image tokens)
   on sampled rows against the oracle's MXFP8 block from the same input, with exact and with 8-bit
   attention.
+* The fused MXFP8 producers (LN-modulation, SwiGLU epilogue, attention output) against the separate
+  quantizer, bit for bit (tiny, 1024^2 and 2048^2); the sampling step and the step cache in the tier
+  against the tier's own forward and uncached steps.
 
 The projections' own error bound: the scaled FP8 MFMA's result on identical MXFP8 operands deviates
 from the exact product by a relative L2 of about 1.4e-5 (it does not sum a 64-product k-tile in
@@ -417,3 +420,30 @@ def test_fp8_sample_step_equals_guidance_of_its_forward(attention_mode, slg_scal
     d_got = x.cpu().numpy().astype(np.float64) - x0n
     assert np.isfinite(d_got).all()
     assert rel_l2(d_got, d_ref) <= REL_L2_FP32
+
+
+@pytest.mark.parametrize("attention_mode", [0, 1])
+def test_fp8_step_cache_threshold_zero_bitwise(attention_mode):
+    """The step cache in the FP8 tier: with a threshold no change can fall below, every call runs in
+    full and the three steps equal the uncached steps bit for bit."""
+    m, inp, W, ocfg = tiny(50.0, precision=1, attention_mode=attention_mode)
+    log(f"fp8 step cache threshold ~0, attention_mode={attention_mode}")
+    sig = dt.moss_sigmas(3, 5.0)
+    tc = torch.from_numpy(inp.text_cond).cuda()
+    tu = torch.from_numpy(inp.text_uncond).cuda()
+
+    def run(**kw):
+        x = torch.from_numpy(inp.latents.copy()).cuda()
+        xs = []
+        for i in range(3):
+            m.moss_sample_step(x, tc, tu, sig, i, cfg_scale=3.0, uncond_skip_layers=[1], **kw)
+            torch.cuda.synchronize()
+            xs.append(x.cpu().numpy().copy())
+        return xs
+
+    plain = run()
+    cached = run(step_cache=True, step_cache_threshold=1e-30)
+    for a, b in zip(plain, cached):
+        np.testing.assert_array_equal(a, b)
+    full, reused, _ = m.moss_step_cache_stats()
+    assert (full, reused) == (3, 0)
