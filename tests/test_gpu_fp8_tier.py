@@ -174,12 +174,13 @@ def test_fp8_drift_from_bf16(mod_scale):
     assert 0 < e_v < 0.1
 
 
-def test_fp8_text_refiner_vs_oracle():
-    m, _, W, ocfg = tiny(1.0)
-    rng = np.random.default_rng(41)
-    B, T = 2, 32
+@pytest.mark.parametrize("attention_mode,T", [(0, 32), (1, 32), (1, 77)])
+def test_fp8_text_refiner_vs_oracle(attention_mode, T):
+    m, _, W, ocfg = tiny(1.0, precision=1, attention_mode=attention_mode)
+    rng = np.random.default_rng(41 + T)
+    B = 2
     enc = rng.standard_normal((B, T, ocfg.text_dim)).astype(np.float32)
-    log(f"fp8 refiner B={B} T={T}")
+    log(f"fp8 refiner B={B} T={T} attention_mode={attention_mode}")
     out = torch.empty((B, T, ocfg.hidden), dtype=torch.float32, device="cuda")
     m.moss_text_refine(torch.from_numpy(enc).cuda(), out)
     torch.cuda.synchronize()
