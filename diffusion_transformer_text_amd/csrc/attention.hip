@@ -161,11 +161,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
   };
   // row max of one tile's scores: in-lane over 32 values, then with lane ^ 32 (same query)
   auto rowmax = [&](const floatx16 (&sc)[2]) {
-    float mx = fmaxf(sc[0][0], sc[0][1]);
+    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = (kb == 0 ? 2 : 0); e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+      for (int e = 0; e < 16; e += 2) mx = max3_f32(mx, sc[kb][e], sc[kb][e + 1]);
     return max_xor32(mx);
   };
   // The running max only moves when a score exceeds it by more than 2^8 in the exp2 domain: with a
@@ -301,7 +301,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
       for (int i = 0; i < 16; ++i) {
         if (i + 2 < 16) vf[(i + 2) % 3] = vfrag(i + 2);
         o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pf[i >> 3][(i >> 2) & 1], o[i & 3], 0, 0, 0);
-        mx = fmaxf(mx, fmaxf(s_next[i >> 3][(2 * i) & 15], s_next[i >> 3][(2 * i + 1) & 15]));
+        mx = max3_f32(mx, s_next[i >> 3][(2 * i) & 15], s_next[i >> 3][(2 * i + 1) & 15]);
+        asm volatile("" : "+v"(mx));   // no instruction: keeps the chain from being rebuilt as a tree after the loop
         __builtin_amdgcn_sched_barrier(0);
       }
       mx_next = fmaxf(mx, __shfl_xor(mx, 32, 64));   // (the VALU exchange here costs a spill)

@@ -109,6 +109,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max(a, b, c) for operands that are never NaN (scores, -inf for masked keys), as IEEE maximum
+// (v_maximum3_f32 on gfx950). fmaxf must quiet signalling NaNs, so on values the compiler cannot
+// prove canonical (MFMA results) it first runs a v_max x, x per operand; maximum propagates NaNs
+// instead and needs no such step. (Not inline asm: the compiler then would not insert the wait
+// states that a VALU read of an MFMA result needs.)
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
+
 // One 32-element MX block held by the lane pair (l, l ^ 32) in the MFMA output layout: this lane's
 // 16 values v[g][e] sit at block positions 8 g + 4 h + e (h = lane / 32), the partner's at the other
 // 16. Rounds them to bf16, writes this lane's four code words at codes + 8 g + 4 h and, from the h == 0
