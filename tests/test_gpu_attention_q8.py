@@ -135,6 +135,25 @@ def test_attention_q8_full_shape_sampled_rows(B, S):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("B,S", [(2, 4352), (1, 20480), (1, 2781)])
+def test_attention_q8_repeat_bitwise_and_fully_written(B, S):
+    """Two calls on the same input give the same bits (no atomics, no timing-dependent reduction
+    order, the workspace fully rewritten by each call) and every output element is written."""
+    H = 24
+    log(f"8-bit attention twice B={B} S={S} H={H}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    qkv = torch.randn((B, S, 3 * H * 128), generator=g, device="cuda").to(torch.bfloat16)
+    outs, ws = [], None
+    for _ in range(2):
+        out = torch.full((B, S, H * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ws = dt.moss_attention_q8(qkv, out, B, S, H, ws=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(outs[0]).any()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_attention_q8_special_cases():
     log("attention_q8 special cases")
     rng = np.random.default_rng(81)

@@ -213,6 +213,28 @@ def test_attention_split_tail_ragged_sampled_rows():
     assert err <= REL_L2_BF16, err
 
 
+@pytest.mark.parametrize("B,T,G", [(2, 256, 64), (1, 4096, 128), (1, 77, 52)])
+def test_attention_repeat_bitwise_and_fully_written(B, T, G):
+    """At the step's shapes (1024^2 batch 2, 2048^2 with a 4096-token prompt) and the split-tail case:
+    the kernel has no atomics and no reduction whose order depends on timing, so a second call on the
+    same input gives the same bits; outputs start as NaN, so every element must have been written
+    (the split tiles' rows by the merge). Each call gets its own copy of the input: with rope the call
+    turns q and k in place."""
+    S, H = T + G * G, 24
+    log(f"attention twice B={B} S={S} (T={T}, grid {G}x{G}) H={H}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    qkv = torch.randn((B, S, 3 * H * 128), generator=g, device="cuda").to(torch.bfloat16)
+    outs = []
+    for _ in range(2):
+        out = torch.full((B, S, H * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dt.moss_attention(qkv.clone(), out, B, S, H, T, G, rope=True)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(outs[0]).any()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_attention_special_cases():
     log("attention special cases")
     # identical keys -> mean of V; one dominant key -> that key's value
