@@ -20,7 +20,8 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import REL_L2_BF16, REL_L2_FP32, dev_bf16, host_bf16, host_bits, log, oracle_cfg, rel_l2
+from tests.gpu_util import (REL_L2_BF16, REL_L2_FP32, dev_bf16, forward_block_chain, host_bf16, host_bits, log,
+                            oracle_cfg, rel_l2)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -32,7 +33,7 @@ T, GH, GW = 256, 64, 64
 S = T + GH * GW
 
 
-def sample_rows(rng, n=20):
+def sample_rows(rng, n=20, T=T, GW=GW, S=S):
     return np.unique(np.concatenate([rng.integers(0, S, n), [0, T - 1, T, T + GW, S - 1]]))
 
 
@@ -43,9 +44,12 @@ def block_model(mod_scale, seed=3):
     return dt.MossDiT(cfg, w), w, oracle_cfg(cfg)
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("mod_scale", [1.0, 50.0])
-def test_full_block_sampled_rows(mod_scale):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mod_scale,T,GH,GW", [(1.0, T, GH, GW), (50.0, T, GH, GW), (50.0, 4096, 128, 128)])
+def test_full_block_sampled_rows(mod_scale, T, GH, GW):
+    """One joint block at full width, stage by stage and whole. The 2048^2 case (4096 text + 16384
+    image tokens, S = 20480, M = 40960 rows per GEMM) is the sampling benchmark's block shape."""
+    S = T + GH * GW
     log(f"full block: D=3072 F=8192 H=24, B=2, S={S}, mod_scale={mod_scale}")
     model, w, ocfg = block_model(mod_scale)
     D, F = ocfg.hidden, ocfg.ffn_hidden
@@ -77,7 +81,7 @@ def test_full_block_sampled_rows(mod_scale):
         m_ref, mf_ref = O.modulation(float(sig[b]), W, ocfg, mirror=True)
         errs.setdefault("modulation", []).append(rel_l2(modv[b], np.concatenate([m_ref.reshape(-1), mf_ref.reshape(-1)])))
         mb = modv[b, :6 * D].reshape(6, D)
-        rows = sample_rows(rng)
+        rows = sample_rows(rng, T=T, GW=GW, S=S)
         a_ref = O.bf16_round(O.ln_modulate(x0[b][rows], mb[0], mb[1], 1e-6))
         errs.setdefault("ln1", []).append(rel_l2(g["a"][b][rows], a_ref))
         # qkv + RoPE from the GPU's own LN output
@@ -114,10 +118,18 @@ def test_full_block_sampled_rows(mod_scale):
 
 
 @pytest.mark.timeout(900)
-def test_full_forward_1024_block_chain():
-    log("full forward 1024^2: 42 blocks, B=2 (uncond skips block 22), T=256")
+@pytest.mark.parametrize("mod_scale", [1.0, 50.0])
+def test_full_forward_1024_block_chain(mod_scale):
+    """The full 42-block forward at 1024^2 (batch 2, the unconditional row skipping block 22), with the
+    literal N(0, 0.02) weights and with the modulation weights x50. Blocks 0, 21 (the last block before
+    the skip), 22 (run on the conditional row alone: M = 4352) and 41 (the last modulation offset) are
+    re-run from the forward's own residual dump with branch taps (tests/gpu_util.forward_block_chain):
+    bitwise equal to the forward's block, gated residual adds recomputed from the taps, and branch
+    outputs, block output and (x50) block update against the oracle on sampled rows. The modulation of
+    all 42 blocks, the embedding and the final layer + unpatchify are checked against the oracle too."""
+    log(f"full forward 1024^2: 42 blocks, B=2 (uncond skips block 22), T=256, mod_scale={mod_scale}")
     L, D = 42, 3072
-    w = synth.torch_weights(synth.FULL, seed=0, device="cuda")
+    w = synth.torch_weights(synth.FULL, seed=0, device="cuda", mod_scale=mod_scale)
     cfg = dt.moss_dit_config_init()
     model = dt.MossDiT(cfg, w)
     ocfg = oracle_cfg(cfg)
@@ -150,17 +162,20 @@ def test_full_forward_1024_block_chain():
     W["mod_w"] = [host_bf16(w["mod_w"][l]) for l in range(L)]
     m, mf = O.modulation(0.5, W, ocfg, mirror=True)
     errs = {}
+    # the modulation the forward used, every block's offset, against the oracle
+    mod = torch.empty((2, model.mod_stride), dtype=torch.bfloat16, device="cuda")
+    model.moss_dit_modulation([0.5, 0.5], mod)
+    torch.cuda.synchronize()
+    modv = host_bf16(mod)
+    mref = np.concatenate([m.reshape(-1), mf.reshape(-1)])
+    errs["modulation"] = max(rel_l2(modv[b], mref) for b in range(2))
     # embedding: text cast + patch embedding of sample 0
     x0_ref = O.embed(lat1[0].double().cpu().numpy(), text_cond[0].double().cpu().numpy(), W, ocfg, mirror=True)
     errs["embed"] = rel_l2(host_bf16(dump[0, 0]), x0_ref)
-    for l in layers:
-        for b in range(2):
-            if b == 1 and l == 22:
-                continue
-            xin = host_bf16(dump[l, b])
-            rows = sample_rows(rng, 12)
-            ref = O.block(xin, m[l], W, l, ocfg, T, GW, mirror=True, rows=rows)
-            errs[f"block{l}_s{b}"] = rel_l2(host_bf16(dump[l + 1, b])[rows], ref)
+    rows = {(l, b): sample_rows(rng, 12) for l in layers for b in range(2)}
+    runs = [(l, [0] if l == 22 else [0, 1]) for l in layers]
+    chain, mism = forward_block_chain(model, torch, dump, mod, runs, T, GH, GW, W, ocfg, [m, m],
+                                      lambda l, b: rows[(l, b)])
     # final layer + unpatchify of both samples from the GPU's last residual
     v = vel.cpu().numpy()
     for b in range(2):
@@ -168,9 +183,15 @@ def test_full_forward_1024_block_chain():
         y = O.final_layer(xl[T:], mf, W, ocfg, mirror=True)
         errs[f"final_s{b}"] = rel_l2(v[b], O.unpatchify(y, 32, 128, 128))
     log({k: f"{e:.2e}" for k, e in errs.items()})
+    log({k: [f"{x:.2e}" for x in e] for k, e in {**chain, **mism}.items()})
     model.close()
     for k, e in errs.items():
         assert e <= REL_L2_BF16, (k, e)
+    for k in ("attn_branch", "ffn_branch", "block"):
+        assert max(chain[k]) <= REL_L2_BF16, (k, chain[k])
+    if mod_scale != 1.0:       # literal init: the update is mostly bf16 rounding (see forward_block_chain)
+        assert max(chain["update"]) <= REL_L2_BF16, chain["update"]
+    assert max(mism["gated_res"]) <= 1e-3, mism
 
 
 def _step_vs_forward(model, T, side, step, slg_scale, seed):

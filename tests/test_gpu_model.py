@@ -8,8 +8,8 @@ import pytest
 
 import oracle as O
 import synth
-from tests.gpu_util import (REL_L2_BF16, REL_L2_FP32, dev_bf16, dev_weights, host_bf16, host_bits, log, oracle_cfg,
-                            rel_l2)
+from tests.gpu_util import (REL_L2_BF16, REL_L2_FP32, dev_bf16, dev_weights, forward_block_chain, host_bf16, host_bits,
+                            log, oracle_cfg, rel_l2)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -126,17 +126,47 @@ def _forward(m, inp, sigma, skip):
 
 @pytest.mark.parametrize("mod_scale", MODES)
 def test_forward_vs_oracle(mod_scale):
+    """The CFG pair's forward (the unconditional row skipping block 1) against the oracle: v, the
+    guidance difference v_c - v_u, and every block of the same forward from the GPU's own input to it
+    (branch outputs, gated residual adds, block output and update; tests/gpu_util.forward_block_chain).
+
+    v_c - v_u is gated in the x50 mode only. Under the literal N(0, 0.02) init the gates are ~5e-3, a
+    block's update is ~6e-4 of the residual and below half a bf16 ulp for most elements, so the two
+    rows' difference is mostly which elements happened to round up: an independent fp64 chain and the
+    GPU's fp32 one disagree on a few 1e-4 of those roundings, which alone is a few percent of that
+    difference. What the literal mode can check sharply is checked per block instead: the branch
+    outputs (their size does not depend on the gates) and the residual adds recomputed from them."""
     m, w, inp, W, ocfg, _ = model(mod_scale)
     log(f"tiny forward mod_scale={mod_scale}")
-    v = _forward(m, inp, [0.6, 0.6], [0, 1 << 1])
-    lat = np.concatenate([inp.latents, inp.latents]).astype(np.float64)
-    txt = np.concatenate([inp.text_cond, inp.text_uncond]).astype(np.float64)
-    ref = O.forward(lat, txt, [0.6, 0.6], W, ocfg, skip=[set(), {1}], mirror=True)
+    L, D, T, gh, gw = ocfg.num_layers, ocfg.hidden, 32, 8, 8
+    S = T + gh * gw
+    lat = torch.from_numpy(np.concatenate([inp.latents, inp.latents])).cuda()
+    txt = torch.from_numpy(np.concatenate([inp.text_cond, inp.text_uncond])).cuda()
+    vel = torch.empty_like(lat)
+    dump = torch.empty((L + 1, 2, S, D), dtype=torch.bfloat16, device="cuda")
+    m.moss_dit_forward(lat, txt, [0.6, 0.6], vel, skip_mask=[0, 1 << 1], residual_dump=dump)
+    torch.cuda.synchronize()
+    v = vel.cpu().numpy()
+    latn = np.concatenate([inp.latents, inp.latents]).astype(np.float64)
+    txtn = np.concatenate([inp.text_cond, inp.text_uncond]).astype(np.float64)
+    ref = O.forward(latn, txtn, [0.6, 0.6], W, ocfg, skip=[set(), {1}], mirror=True)
     e_v = rel_l2(v, ref)
     e_d = rel_l2(v[0] - v[1], ref[0] - ref[1])
-    log(f"rel-L2 v {e_v:.3e}  (v_c - v_u) {e_d:.3e}")
+    log(f"rel-L2 v {e_v:.3e}  (v_c - v_u) {e_d:.3e}{'' if mod_scale != 1.0 else ' (not gated at the literal init)'}")
     assert e_v <= REL_L2_BF16
-    assert e_d <= REL_L2_BF16 * (5 if mod_scale == 1.0 else 1)
+    if mod_scale != 1.0:
+        assert e_d <= REL_L2_BF16
+    mod = torch.empty((2, m.mod_stride), dtype=torch.bfloat16, device="cuda")
+    m.moss_dit_modulation([0.6, 0.6], mod)
+    m_ref = [O.modulation(0.6, W, ocfg, mirror=True)[0]] * 2
+    errs, mism = forward_block_chain(m, torch, dump, mod, [(0, [0, 1]), (1, [0])], T, gh, gw, W, ocfg, m_ref,
+                                     lambda l, b: list(range(S)))
+    log({k: f"{max(e):.2e}" for k, e in {**errs, **mism}.items()})
+    for k in ("attn_branch", "ffn_branch", "block"):
+        assert max(errs[k]) <= REL_L2_BF16, (k, errs[k])
+    if mod_scale != 1.0:
+        assert max(errs["update"]) <= REL_L2_BF16, errs["update"]
+    assert max(mism["gated_res"]) <= 1e-3, mism
 
 
 @pytest.mark.parametrize("lat_h,lat_w,T,B", [(16, 24, 7, 3), (24, 8, 1, 1)])
