@@ -49,6 +49,7 @@ class moss_dit_weights(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("t_w1", C.c_void_p), ("t_w2", C.c_void_p), ("x_embed_w", C.c_void_p),
                 ("mod_w", C.POINTER(C.c_void_p)), ("qkv_w", C.POINTER(C.c_void_p)), ("out_w", C.POINTER(C.c_void_p)),
                 ("gate_up_w", C.POINTER(C.c_void_p)), ("down_w", C.POINTER(C.c_void_p)),
+                ("q_norm_w", C.POINTER(C.c_void_p)), ("k_norm_w", C.POINTER(C.c_void_p)),
                 ("final_mod_w", C.c_void_p), ("final_w", C.c_void_p), ("text_proj_w", C.c_void_p),
                 ("refiner_qkv_w", C.POINTER(C.c_void_p)), ("refiner_out_w", C.POINTER(C.c_void_p)),
                 ("refiner_gate_up_w", C.POINTER(C.c_void_p)), ("refiner_down_w", C.POINTER(C.c_void_p))]

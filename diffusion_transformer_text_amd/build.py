@@ -2,7 +2,7 @@
 
     python diffusion_transformer_text_amd/build.py
 
-Every source under csrc/ is compiled to an object in parallel, then linked into
+Every source under csrc/ (.hip, and the host-only .cpp) is compiled to an object in parallel, then linked into
 diffusion_transformer_text_amd/libmoss_dit.so.
 """
 from __future__ import annotations
@@ -46,11 +46,12 @@ def _compile(src: str, obj: str, extra) -> str:
 
 def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip") or f.endswith(".cpp"))
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     objs = []
     with cf.ThreadPoolExecutor(jobs) as ex:
-        futs = [ex.submit(_compile, os.path.join(CSRC, s), os.path.join(BUILD, s[:-4] + ".o"), list(extra_flags))
+        futs = [ex.submit(_compile, os.path.join(CSRC, s), os.path.join(BUILD, s.rsplit(".", 1)[0] + ".o"),
+                          list(extra_flags))
                 for s in srcs]
         for f in futs:
             objs.append(f.result())

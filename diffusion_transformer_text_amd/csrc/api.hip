@@ -30,28 +30,8 @@ using namespace moss;
 
 namespace {
 
-thread_local std::string g_thread_error;
 
-constexpr int kMaxLatentSide = 512;           // 4096 px / 8
-constexpr double kMaxPixels = 4.2e6;          // 4.2 megapixels
-constexpr int kMaxTextLen = 4096;
-constexpr int kSinusoidDim = 256;
 
-std::string fmt(const char* f, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, f);
-  vsnprintf(buf, sizeof buf, f, ap);
-  va_end(ap);
-  return buf;
-}
-
-void copy_msg(const std::string& m, char* msg, int32_t len) {
-  if (msg && len > 0) {
-    strncpy(msg, m.c_str(), (size_t)len - 1);
-    msg[len - 1] = 0;
-  }
-}
 
 bool env_flag(const char* name) {
   const char* v = getenv(name);
@@ -72,14 +52,8 @@ hipError_t rope_table(float theta, float** out) {
     *out = it->second;
     return hipSuccess;
   }
-  const int Q = kHeadDim / 4;
-  std::vector<float> host(2 * kRopeMaxPos * Q);
-  for (int pos = 0; pos < kRopeMaxPos; ++pos)
-    for (int k = 0; k < Q; ++k) {
-      const double ang = (double)pos * std::pow((double)theta, -(double)k / Q);
-      host[pos * Q + k] = (float)std::cos(ang);
-      host[kRopeMaxPos * Q + pos * Q + k] = (float)std::sin(ang);
-    }
+  std::vector<float> host(kRopeTableFloats);
+  rope_table_host(theta, host.data());
   float* d = nullptr;
   e = hipMalloc(&d, host.size() * sizeof(float));
   if (e != hipSuccess) return e;
@@ -92,8 +66,6 @@ hipError_t rope_table(float theta, float** out) {
   *out = d;
   return hipSuccess;
 }
-
-size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -155,14 +127,36 @@ int fail(moss_dit* h, int status, const std::string& msg) {
     h->err = msg;
     if (status == MOSS_ERR_DEVICE) h->dead = true;
   } else {
-    g_thread_error = msg;
+    thread_error() = msg;
   }
   return status;
 }
 
+// Host-side fault injection for tests of the error path: with MOSS_DIT_FAIL_LAUNCH=n in the
+// environment, the n-th checked HIP call of this thread after the variable took that value reports a
+// launch failure. The call itself ran normally (nothing on the device is affected); the library then
+// takes its device-error path, and the handle is dead as after a real one.
+hipError_t inject_launch_failure(hipError_t e) {
+  thread_local std::string last;
+  thread_local long count = 0;
+  const char* v = getenv("MOSS_DIT_FAIL_LAUNCH");
+  if (!v || !*v) {
+    last.clear();
+    count = 0;
+    return e;
+  }
+  if (last != v) {
+    last = v;
+    count = 0;
+  }
+  const long n = atol(v);
+  if (e == hipSuccess && n > 0 && ++count == n) return hipErrorLaunchFailure;
+  return e;
+}
+
 #define HIP_TRY(h, expr)                                                                          \
   do {                                                                                            \
-    hipError_t e_ = (expr);                                                                       \
+    hipError_t e_ = inject_launch_failure(expr);                                                  \
     if (e_ != hipSuccess) return fail((h), MOSS_ERR_DEVICE, fmt("%s failed: %s", #expr, hipGetErrorString(e_))); \
   } while (0)
 
@@ -197,177 +191,6 @@ hipError_t dev_alloc(void** p, size_t bytes) {
   return hipMalloc(p, bytes);
 }
 
-int check_config(const moss_dit_config* c, std::string& msg) {
-  if (!c) {
-    msg = "config is NULL";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (c->struct_size != sizeof(moss_dit_config)) {
-    msg = fmt("moss_dit_config.struct_size %u, this library expects %zu (fill it with moss_dit_config_init)",
-              c->struct_size, sizeof(moss_dit_config));
-    return MOSS_ERR_ABI_MISMATCH;
-  }
-  if (c->num_layers < 1 || c->hidden < 1 || c->num_heads < 1 || c->head_dim < 1 || c->ffn_hidden < 1 ||
-      c->latent_channels < 1 || c->patch < 1 || c->temb_dim < 1 || !(c->norm_eps > 0.f) ||
-      !(c->rope_theta > 1.f) || !std::isfinite(c->flow_multiplier)) {
-    msg = "config values must be positive";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (c->head_dim != kHeadDim || c->hidden != c->num_heads * c->head_dim || c->hidden % 256 != 0 ||
-      c->hidden > 4096 || c->ffn_hidden % 64 != 0 || c->temb_dim != kSinusoidDim || c->patch != 2 ||
-      c->num_layers > 64 || c->qk_norm != 0 || c->latent_channels * 4 % 128 != 0) {
-    msg = fmt("unsupported configuration (need head_dim 128, hidden = heads*128, hidden %% 256 == 0 and <= 4096, "
-              "ffn %% 64 == 0, temb 256, patch 2, channels*4 %% 128 == 0, <= 64 layers, no qk_norm)");
-    return MOSS_ERR_NOT_SUPPORTED;
-  }
-  if (c->text_dim < 64 || c->text_dim > 16384 || c->text_dim % 64 != 0 || c->refiner_layers < 0 ||
-      c->refiner_layers > 8) {
-    msg = fmt("unsupported text refiner configuration (need text_dim %% 64 == 0 in [64, 16384], 0..8 refiner layers; "
-              "got %d, %d)", c->text_dim, c->refiner_layers);
-    return MOSS_ERR_NOT_SUPPORTED;
-  }
-  if (c->gemm_precision != 0 && c->gemm_precision != 1) {
-    msg = fmt("gemm_precision must be 0 (bf16) or 1 (MXFP8), got %d", c->gemm_precision);
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (c->attention_mode != 0 && c->attention_mode != 1) {
-    msg = fmt("attention_mode must be 0 (exact) or 1 (8-bit), got %d", c->attention_mode);
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (c->gemm_precision == 1 && c->ffn_hidden % 256 != 0) {
-    msg = fmt("the MXFP8 tier needs ffn_hidden %% 256 == 0 (got %d)", c->ffn_hidden);
-    return MOSS_ERR_NOT_SUPPORTED;
-  }
-  return MOSS_OK;
-}
-
-int check_latent(int32_t lh, int32_t lw, std::string& msg) {
-  if (lh <= 0 || lw <= 0 || lh % 2 || lw % 2) {
-    msg = "Height and width must be positive multiples of 16.";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (lh > kMaxLatentSide || lw > kMaxLatentSide) {
-    msg = "Height and width must be at most 4096.";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (64.0 * lh * lw > kMaxPixels) {
-    msg = "The image must be at most 4.2 megapixels.";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  return MOSS_OK;
-}
-
-int check_text_len(int32_t t, std::string& msg) {
-  if (t < 1 || t > kMaxTextLen) {
-    msg = fmt("text_len %d out of range [1, %d]", t, kMaxTextLen);
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  return MOSS_OK;
-}
-
-int validate_forward(const moss_dit_config* c, const moss_forward_args* a, std::string& msg) {
-  int s = check_config(c, msg);
-  if (s) return s;
-  if (!a) {
-    msg = "args is NULL";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (a->struct_size != sizeof(moss_forward_args)) {
-    msg = fmt("moss_forward_args.struct_size %u, this library expects %zu", a->struct_size, sizeof(moss_forward_args));
-    return MOSS_ERR_ABI_MISMATCH;
-  }
-  if (a->batch < 1 || a->batch > kMaxBatch) {
-    msg = fmt("batch %d out of range [1, %d]", a->batch, kMaxBatch);
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if ((s = check_latent(a->latent_h, a->latent_w, msg))) return s;
-  if ((s = check_text_len(a->text_len, msg))) return s;
-  if (!a->latents || !a->text || !a->sigma || !a->velocity) {
-    msg = "latents, text, sigma and velocity must not be NULL";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  for (int b = 0; b < a->batch; ++b) {
-    if (!(a->sigma[b] >= 0.f && a->sigma[b] <= 1.f)) {
-      msg = fmt("sigma[%d] = %g outside [0, 1]", b, (double)a->sigma[b]);
-      return MOSS_ERR_INVALID_ARGUMENT;
-    }
-    if (a->skip_mask && c->num_layers < 64 && (a->skip_mask[b] >> c->num_layers)) {
-      msg = fmt("skip_mask[%d] names a block >= num_layers (%d)", b, c->num_layers);
-      return MOSS_ERR_INVALID_ARGUMENT;
-    }
-  }
-  return MOSS_OK;
-}
-
-int validate_step(const moss_dit_config* c, const moss_step_args* a, std::string& msg) {
-  int s = check_config(c, msg);
-  if (s) return s;
-  if (!a) {
-    msg = "args is NULL";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (a->struct_size != sizeof(moss_step_args)) {
-    msg = fmt("moss_step_args.struct_size %u, this library expects %zu", a->struct_size, sizeof(moss_step_args));
-    return MOSS_ERR_ABI_MISMATCH;
-  }
-  if ((s = check_latent(a->latent_h, a->latent_w, msg))) return s;
-  if ((s = check_text_len(a->text_len, msg))) return s;
-  if (a->num_steps < 1) {
-    msg = "num_steps must be at least 1";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (a->step < 0 || a->step >= a->num_steps) {
-    msg = fmt("step %d out of range [0, %d)", a->step, a->num_steps);
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (!std::isfinite(a->cfg_scale) || a->cfg_scale < 1.f) {
-    msg = "CFG scale must be at least 1.0.";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (!std::isfinite(a->slg_start) || !std::isfinite(a->slg_stop)) {
-    msg = "slg_start and slg_stop must be finite";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (!std::isfinite(a->slg_scale) || a->slg_scale < 0.f) {
-    msg = "slg_scale must be finite and >= 0";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (!std::isfinite(a->cfg_truncation) || a->cfg_truncation < 0.f || a->cfg_truncation > 1.f) {
-    msg = "cfg_truncation must be in [0, 1] (1 = off)";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if ((a->step_cache != 0 && a->step_cache != 1) || !std::isfinite(a->step_cache_threshold)) {
-    msg = "step_cache must be 0 (off) or 1 (First-Block Cache) and step_cache_threshold finite";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (!a->x || !a->text_cond || !a->sigmas) {
-    msg = "x, text_cond and sigmas must not be NULL";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (a->cfg_scale > 1.f && !a->text_uncond) {
-    msg = "text_uncond must not be NULL when cfg_scale > 1";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  if (a->n_skip < 0 || a->n_skip > c->num_layers || (a->n_skip > 0 && !a->uncond_skip_layers)) {
-    msg = fmt("n_skip %d invalid", a->n_skip);
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  for (int i = 0; i < a->n_skip; ++i) {
-    const int l = a->uncond_skip_layers[i];
-    if (l < 0 || l >= c->num_layers) {
-      msg = fmt("Skip layers must be block numbers from 0 to %d (got %d).", c->num_layers - 1, l);
-      return MOSS_ERR_INVALID_ARGUMENT;
-    }
-  }
-  for (int i = 0; i <= a->num_steps; ++i) {
-    if (!std::isfinite(a->sigmas[i])) {
-      msg = fmt("sigmas[%d] is not finite", i);
-      return MOSS_ERR_INVALID_ARGUMENT;
-    }
-  }
-  return MOSS_OK;
-}
-
 // ---- workspace carve ----
 struct Carve {
   uint16_t *x, *a, *qkv, *o, *h, *tokens, *mod;
@@ -381,45 +204,34 @@ struct Carve {
   size_t attn_split_bytes;
 };
 
+// Pointers of the regions of the workspace layout (host_plan.cpp: ws_layout) at `base`; returns its
+// size. base == nullptr only sizes it.
 size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, Carve* c) {
-  const moss_dit_config& k = H->cfg;
-  const size_t D = k.hidden, F = k.ffn_hidden, P = (size_t)k.latent_channels * 4;
-  const size_t M = (size_t)B * S;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    char* p = base ? base + off : nullptr;
-    off += align_up(bytes);
-    return p;
-  };
-  Carve t;
-  t.x = (uint16_t*)take(M * D * 2);
-  t.a = (uint16_t*)take(M * D * 2);
-  t.qkv = (uint16_t*)take(M * 3 * D * 2);
-  t.o = (uint16_t*)take(M * D * 2);
-  t.h = (uint16_t*)take(M * F * 2);
-  t.tokens = (uint16_t*)take((size_t)B * N * P * 2);
-  t.mod = (uint16_t*)take((size_t)B * H->mod_rows() * 2);
-  t.u = (float*)take((size_t)B * k.temb_dim * 4);
-  t.vel = (float*)take((size_t)B * lat_elems * 4);   // one velocity per row of the step's batch
-  t.q8 = t.s8 = t.q8h = t.s8h = nullptr;
-  t.lds8 = (long)(M + 255) / 256 * 256;
-  if (H->fp8()) {
-    const size_t Kmax = D > F ? D : F;
-    t.q8 = (uint8_t*)take(M * Kmax);
-    t.s8 = (uint8_t*)take(Kmax / 128 * (size_t)t.lds8 * 4);
-    t.q8h = (uint8_t*)take(M * F);
-    t.s8h = (uint8_t*)take(F / 128 * (size_t)t.lds8 * 4);
+  const WsLayout L = ws_layout(H->cfg, B, S, N, lat_elems, 2L * device_cu_count());
+  if (c) {
+    auto at = [&](size_t off) -> char* { return (base && off != kNoRegion) ? base + off : nullptr; };
+    Carve t;
+    t.x = (uint16_t*)at(L.x);
+    t.a = (uint16_t*)at(L.a);
+    t.qkv = (uint16_t*)at(L.qkv);
+    t.o = (uint16_t*)at(L.o);
+    t.h = (uint16_t*)at(L.h);
+    t.tokens = (uint16_t*)at(L.tokens);
+    t.mod = (uint16_t*)at(L.mod);
+    t.u = (float*)at(L.u);
+    t.vel = (float*)at(L.vel);
+    t.q8 = (uint8_t*)at(L.q8);
+    t.s8 = (uint8_t*)at(L.s8);
+    t.q8h = (uint8_t*)at(L.q8h);
+    t.s8h = (uint8_t*)at(L.s8h);
+    t.lds8 = L.lds8;
+    t.attn_split = at(L.attn_split);
+    t.attn_split_bytes = t.attn_split ? L.attn_split_bytes : 0;
+    t.attn8 = at(L.attn8);
+    t.attn8_bytes = t.attn8 ? L.attn8_bytes : 0;
+    *c = t;
   }
-  t.attn8 = nullptr;
-  t.attn8_bytes = 0;
-  t.attn_split_bytes = attention_split_workspace(B, S, k.num_heads);
-  t.attn_split = t.attn_split_bytes ? take(t.attn_split_bytes) : nullptr;
-  if (H->q8attn()) {
-    t.attn8_bytes = attention_q8_workspace(B, S, k.num_heads);
-    t.attn8 = take(t.attn8_bytes);
-  }
-  if (c) *c = t;
-  return off;
+  return L.total;
 }
 
 int ensure_ws(moss_dit* H, size_t bytes) {
@@ -803,7 +615,7 @@ int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st, c
 
 int enter(moss_dit* H) {
   if (!H) {
-    g_thread_error = "handle is NULL";
+    thread_error() = "handle is NULL";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   if (H->dead) return fail(H, MOSS_ERR_DEVICE, "the handle hit a device error earlier; destroy it");
@@ -821,125 +633,12 @@ int enter(moss_dit* H) {
 // =============================================================================================
 extern "C" {
 
-int moss_dit_abi_version(void) { return MOSS_DIT_ABI_VERSION; }
-
-const char* moss_status_string(int s) {
-  switch (s) {
-    case MOSS_OK: return "ok";
-    case MOSS_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case MOSS_ERR_NOT_SUPPORTED: return "not supported";
-    case MOSS_ERR_OUT_OF_MEMORY: return "out of device memory";
-    case MOSS_ERR_DEVICE: return "device error";
-    case MOSS_ERR_ABI_MISMATCH: return "ABI mismatch";
-    default: return "unknown status";
-  }
-}
-
-const char* moss_dit_last_error(const moss_dit* h) { return h ? h->err.c_str() : g_thread_error.c_str(); }
-
-void moss_dit_config_init(moss_dit_config* c, uint32_t size) {
-  if (!c) return;
-  moss_dit_config d;
-  d.struct_size = size;
-  d.num_layers = 42;
-  d.hidden = 3072;
-  d.num_heads = 24;
-  d.head_dim = 128;
-  d.ffn_hidden = 8192;
-  d.latent_channels = 32;
-  d.patch = 2;
-  d.temb_dim = 256;
-  d.qk_norm = 0;
-  d.rope_theta = 1.0e4f;
-  d.norm_eps = 1.0e-6f;
-  d.flow_multiplier = 1000.f;
-  d.text_dim = 4096;
-  d.refiner_layers = 2;
-  d.gemm_precision = 0;
-  d.attention_mode = 0;
-  memcpy(c, &d, size < sizeof d ? size : sizeof d);
-}
-
-void moss_dit_weights_init(moss_dit_weights* w, uint32_t size) {
-  if (!w) return;
-  moss_dit_weights d;
-  memset(&d, 0, sizeof d);
-  d.struct_size = size;
-  memcpy(w, &d, size < sizeof d ? size : sizeof d);
-}
-
-void moss_forward_args_init(moss_forward_args* a, uint32_t size) {
-  if (!a) return;
-  moss_forward_args d;
-  memset(&d, 0, sizeof d);
-  d.struct_size = size;
-  d.batch = 1;
-  d.latent_h = d.latent_w = 128;
-  d.text_len = 256;
-  memcpy(a, &d, size < sizeof d ? size : sizeof d);
-}
-
-static const int32_t kDefaultSkip[1] = {22};
-
-void moss_step_args_init(moss_step_args* a, uint32_t size) {
-  if (!a) return;
-  moss_step_args d;
-  memset(&d, 0, sizeof d);
-  d.struct_size = size;
-  d.latent_h = d.latent_w = 128;
-  d.text_len = 256;
-  d.num_steps = 50;
-  d.step = 0;
-  d.cfg_scale = 3.0f;
-  d.slg_start = 0.01f;
-  d.slg_stop = 1.0f;
-  d.uncond_skip_layers = kDefaultSkip;
-  d.n_skip = 1;
-  d.slg_scale = 0.0f;
-  d.cfg_truncation = 1.0f;
-  d.step_cache = 0;
-  d.step_cache_threshold = 0.0f;
-  memcpy(a, &d, size < sizeof d ? size : sizeof d);
-}
-
-void moss_block_taps_init(moss_block_taps* t, uint32_t size) {
-  if (!t) return;
-  moss_block_taps d;
-  memset(&d, 0, sizeof d);
-  d.struct_size = size;
-  memcpy(t, &d, size < sizeof d ? size : sizeof d);
-}
-
-int moss_sigmas(int32_t num_steps, float shift, float* sigmas) {
-  if (num_steps < 1 || !sigmas || !(shift > 0.f) || !std::isfinite(shift)) {
-    g_thread_error = "num_steps must be >= 1, shift > 0 and sigmas non-NULL";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  for (int i = 0; i <= num_steps; ++i) {
-    const double s = (double)(num_steps - i) / (double)num_steps;
-    sigmas[i] = (float)((double)shift * s / (1.0 + ((double)shift - 1.0) * s));
-  }
-  return MOSS_OK;
-}
-
-int moss_validate_forward_args(const moss_dit_config* cfg, const moss_forward_args* a, char* msg, int32_t msg_len) {
-  std::string m;
-  const int s = validate_forward(cfg, a, m);
-  copy_msg(s ? m : std::string("ok"), msg, msg_len);
-  return s;
-}
-
-int moss_validate_step_args(const moss_dit_config* cfg, const moss_step_args* a, char* msg, int32_t msg_len) {
-  std::string m;
-  const int s = validate_step(cfg, a, m);
-  copy_msg(s ? m : std::string("ok"), msg, msg_len);
-  return s;
-}
+const char* moss_dit_last_error(const moss_dit* h) { return h ? h->err.c_str() : thread_error().c_str(); }
 
 int moss_dit_create(const moss_dit_config* cfg, const moss_dit_weights* w, int weights_on_device, void* stream,
                     moss_dit** out) {
   if (!out) {
-    g_thread_error = "out is NULL";
+    thread_error() = "out is NULL";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   *out = nullptr;
@@ -1175,17 +874,10 @@ int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream) {
   std::string msg;
   if ((s = validate_step(&h->cfg, a, msg))) return fail(h, s, msg);
   const moss_dit_config& k = h->cfg;
-  // Rows of the batch: [cond | uncond (negative branch) | cond skipping layers (three-pass SLG)].
-  // The skip-layer window is on the progress step/num_steps, inclusive at both ends; the negative
-  // branch runs for cfg > 1 until step cfg_truncation * num_steps.
-  const double prog = (double)a->step / (double)a->num_steps;
-  const bool window = (double)a->slg_start <= prog && prog <= (double)a->slg_stop;
-  uint64_t mask = 0;
-  if (window)
-    for (int i = 0; i < a->n_skip; ++i) mask |= 1ULL << a->uncond_skip_layers[i];
-  const bool neg = a->cfg_scale > 1.f && (double)a->step < (double)a->cfg_truncation * (double)a->num_steps;
-  const bool third = a->slg_scale > 0.f && mask != 0;
-  const int B = 1 + (neg ? 1 : 0) + (third ? 1 : 0);
+  // Rows of the batch: [cond | uncond (negative branch) | cond skipping layers (three-pass SLG)]
+  const StepPlan plan = step_plan(a);
+  const bool neg = plan.neg, third = plan.third;
+  const int B = plan.rows;
   const int N = (a->latent_h / 2) * (a->latent_w / 2), S = a->text_len + N;
   const int lat = k.latent_channels * a->latent_h * a->latent_w;
   if ((s = ensure_ws(h, carve(h, B, S, N, lat, nullptr, nullptr)))) return s;
@@ -1203,7 +895,7 @@ int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream) {
     p.lat.p[r] = a->x;
     p.txt.p[r] = is_uncond ? a->text_uncond : a->text_cond;
     p.sigma[r] = sig;
-    p.skip[r] = r == 0 ? 0 : mask;
+    p.skip[r] = plan.skip[r];
   }
   p.vel = c.vel;
   FbcCall fc{a->step_cache_threshold > 0.f ? a->step_cache_threshold : 0.02f};
@@ -1225,7 +917,7 @@ int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream) {
 
 int moss_step_cache_stats(const moss_dit* h, int32_t* full_calls, int32_t* reused_calls, float* last_change) {
   if (!h) {
-    g_thread_error = "handle is NULL";
+    thread_error() = "handle is NULL";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   if (full_calls) *full_calls = h->fbc.full;
@@ -1278,17 +970,17 @@ int moss_text_refine(moss_dit* h, int32_t batch, int32_t text_len, const float* 
 int moss_cfg_euler(const float* v_cond, const float* v_uncond, float* x, int64_t n, float cfg, float sigma,
                    float sigma_next, void* stream) {
   if (!v_cond || !x || n < 0 || !std::isfinite(cfg) || cfg < 1.f || (!v_uncond && cfg != 1.f)) {
-    g_thread_error = "moss_cfg_euler: v_cond and x must be non-NULL, cfg >= 1, and v_uncond NULL only when cfg == 1";
+    thread_error() = "moss_cfg_euler: v_cond and x must be non-NULL, cfg >= 1, and v_uncond NULL only when cfg == 1";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   if ((reinterpret_cast<uintptr_t>(v_cond) | reinterpret_cast<uintptr_t>(v_uncond) | reinterpret_cast<uintptr_t>(x)) & 15) {
-    g_thread_error = "moss_cfg_euler: pointers must be 16-byte aligned";
+    thread_error() = "moss_cfg_euler: pointers must be 16-byte aligned";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   const hipError_t e = launch_cfg_euler(v_cond, cfg == 1.f ? nullptr : v_uncond, x, n, cfg, sigma, sigma_next,
                                         (hipStream_t)stream);
   if (e != hipSuccess) {
-    g_thread_error = fmt("moss_cfg_euler launch failed: %s", hipGetErrorString(e));
+    thread_error() = fmt("moss_cfg_euler launch failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;
@@ -1297,18 +989,18 @@ int moss_cfg_euler(const float* v_cond, const float* v_uncond, float* x, int64_t
 int moss_guidance_euler(const float* v_cond, const float* v_uncond, const float* v_skip, float* x, int64_t n,
                         float cfg, float slg, float sigma, float sigma_next, void* stream) {
   if (!v_cond || !x || n < 0 || !std::isfinite(cfg) || cfg < 1.f || !std::isfinite(slg)) {
-    g_thread_error = "moss_guidance_euler: v_cond and x must be non-NULL, cfg >= 1 and slg finite";
+    thread_error() = "moss_guidance_euler: v_cond and x must be non-NULL, cfg >= 1 and slg finite";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   if ((reinterpret_cast<uintptr_t>(v_cond) | reinterpret_cast<uintptr_t>(v_uncond) |
        reinterpret_cast<uintptr_t>(v_skip) | reinterpret_cast<uintptr_t>(x)) & 15) {
-    g_thread_error = "moss_guidance_euler: pointers must be 16-byte aligned";
+    thread_error() = "moss_guidance_euler: pointers must be 16-byte aligned";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   const hipError_t e = launch_guidance_euler(v_cond, v_uncond, v_skip, x, n, cfg, slg, sigma, sigma_next,
                                              (hipStream_t)stream);
   if (e != hipSuccess) {
-    g_thread_error = fmt("moss_guidance_euler launch failed: %s", hipGetErrorString(e));
+    thread_error() = fmt("moss_guidance_euler launch failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;
@@ -1348,21 +1040,13 @@ int moss_dit_block(moss_dit* h, int32_t layer, void* x, int32_t batch, int32_t t
 
 int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, int32_t text_len, int32_t grid_w,
                    int32_t rope, void* stream) {
-  if (!qkv || !out || batch < 1 || seq < 1 || heads < 1 || text_len < 0 || text_len > seq) {
-    g_thread_error = "moss_attention: bad arguments";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
-  const int n_img = seq - text_len;
-  if (rope && (grid_w < 1 || n_img % grid_w != 0 || grid_w > kRopeMaxPos || n_img / grid_w > kRopeMaxPos)) {
-    g_thread_error = "moss_attention: image rows must fill a grid of width grid_w (<= 256 per side)";
+  std::string msg;
+  if (check_attention_args(qkv, out, batch, seq, heads, text_len, grid_w, rope, msg) != MOSS_OK) {
+    thread_error() = "moss_attention: " + msg;
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   hipStream_t st = (hipStream_t)stream;
   const long D = (long)heads * kHeadDim;
-  if (2L * seq * 3 * D > 0x7fffffffL) {
-    g_thread_error = "moss_attention: one sample's qkv rows must stay below 2 GiB";
-    return MOSS_ERR_INVALID_ARGUMENT;
-  }
   hipError_t e = hipSuccess;
   if (rope) {
     float* tab = nullptr;
@@ -1396,7 +1080,7 @@ int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t hea
     }
   }
   if (e != hipSuccess) {
-    g_thread_error = fmt("moss_attention failed: %s", hipGetErrorString(e));
+    thread_error() = fmt("moss_attention failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;
@@ -1410,17 +1094,17 @@ int64_t moss_attention_q8_workspace(int32_t batch, int32_t seq, int32_t heads) {
 int moss_attention_q8(const void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, void* ws,
                       int64_t ws_bytes, void* stream) {
   if (!qkv || !out || !ws || batch < 1 || seq < 1 || heads < 1 || batch > 65535 || heads > 65535) {
-    g_thread_error = "moss_attention_q8: bad arguments";
+    thread_error() = "moss_attention_q8: bad arguments";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   if (ws_bytes < (int64_t)attention_q8_workspace(batch, seq, heads) || (reinterpret_cast<uintptr_t>(ws) & 255)) {
-    g_thread_error = "moss_attention_q8: the workspace must be 256-byte aligned and hold moss_attention_q8_workspace bytes";
+    thread_error() = "moss_attention_q8: the workspace must be 256-byte aligned and hold moss_attention_q8_workspace bytes";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   const long D = (long)heads * kHeadDim;
   const long nblk = (seq + 63) / 64;
   if (2L * seq * 3 * D > 0x7fffffffL || (long)seq * D > 0x7fffffffL || (long)batch * heads * kHeadDim * nblk * 64 > 0x7fffffffL) {
-    g_thread_error = "moss_attention_q8: one sample's qkv rows and the whole V^T copy must stay below 2 GiB";
+    thread_error() = "moss_attention_q8: one sample's qkv rows and the whole V^T copy must stay below 2 GiB";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   AttnArgs at;
@@ -1434,7 +1118,7 @@ int moss_attention_q8(const void* qkv, void* out, int32_t batch, int32_t seq, in
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
   const hipError_t e = launch_attention_q8(at, ws, (size_t)ws_bytes, (hipStream_t)stream);
   if (e != hipSuccess) {
-    g_thread_error = fmt("moss_attention_q8 failed: %s", hipGetErrorString(e));
+    thread_error() = fmt("moss_attention_q8 failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;
@@ -1442,13 +1126,13 @@ int moss_attention_q8(const void* qkv, void* out, int32_t batch, int32_t seq, in
 
 int moss_gemm_bf16(const void* A, const void* W, float* out, int32_t M, int32_t N, int32_t K, void* stream) {
   if (!A || !W || !out || M < 1 || N < 1 || K < 1 || K % 64 != 0 || N % 128 != 0) {
-    g_thread_error = "moss_gemm_bf16: need non-NULL pointers, K % 64 == 0, N % 128 == 0";
+    thread_error() = "moss_gemm_bf16: need non-NULL pointers, K % 64 == 0, N % 128 == 0";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   const hipError_t e = launch_gemm(gemm_args((const uint16_t*)A, (const uint16_t*)W, M, N, K, out, N), EPI_F32,
                                    (hipStream_t)stream);
   if (e != hipSuccess) {
-    g_thread_error = fmt("moss_gemm_bf16 failed: %s", hipGetErrorString(e));
+    thread_error() = fmt("moss_gemm_bf16 failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;
@@ -1459,13 +1143,13 @@ int moss_mx_quantize(const void* x, int32_t rows, int32_t K, void* codes, void* 
   if (!x || !codes || !scales || rows < 1 || K < 256 || K % 256 != 0 || ld_scale < rows ||
       (reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(codes) & 15) ||
       (reinterpret_cast<uintptr_t>(scales) & 3)) {
-    g_thread_error = "moss_mx_quantize: need non-NULL 16-byte aligned x and codes, K % 256 == 0, ld_scale >= rows";
+    thread_error() = "moss_mx_quantize: need non-NULL 16-byte aligned x and codes, K % 256 == 0, ld_scale >= rows";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   const hipError_t e = launch_mx_quant((const uint16_t*)x, K, rows, K, (uint8_t*)codes, (uint8_t*)scales, ld_scale,
                                        (hipStream_t)stream);
   if (e != hipSuccess) {
-    g_thread_error = fmt("moss_mx_quantize failed: %s", hipGetErrorString(e));
+    thread_error() = fmt("moss_mx_quantize failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;
@@ -1475,7 +1159,7 @@ int moss_gemm_mxfp8(const void* A, const void* A_scales, int64_t lds_a, const vo
                     int64_t lds_w, float* out, int32_t M, int32_t N, int32_t K, void* stream) {
   if (!A || !A_scales || !W || !W_scales || !out || M < 1 || N < 1 || K < 1 || N % 256 != 0 || K % 256 != 0 ||
       lds_a % 256 != 0 || lds_a < (M + 255) / 256 * 256 || lds_w % 256 != 0 || lds_w < N) {
-    g_thread_error = "moss_gemm_mxfp8: need non-NULL pointers, N % 256 == 0, K % 256 == 0, lds_a >= M rounded up "
+    thread_error() = "moss_gemm_mxfp8: need non-NULL pointers, N % 256 == 0, K % 256 == 0, lds_a >= M rounded up "
                      "to 256, lds_w >= N, both multiples of 256";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
@@ -1486,7 +1170,7 @@ int moss_gemm_mxfp8(const void* A, const void* A_scales, int64_t lds_a, const vo
   g.lds_w = lds_w;
   const hipError_t e = launch_gemm_mxfp8(g, EPI_F32, (hipStream_t)stream);
   if (e != hipSuccess) {
-    g_thread_error = fmt("moss_gemm_mxfp8 failed: %s", hipGetErrorString(e));
+    thread_error() = fmt("moss_gemm_mxfp8 failed: %s", hipGetErrorString(e));
     return MOSS_ERR_DEVICE;
   }
   return MOSS_OK;

@@ -22,8 +22,8 @@ namespace moss {
 namespace {
 
 constexpr int D = kHeadDim;   // 128
-constexpr int BQ = 128;
-constexpr int BKV = 64;
+constexpr int BQ = kAttnBQ;   // 128
+constexpr int BKV = kAttnBKV; // 64
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -445,25 +445,13 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
   orow[1] = make_uint2(pack2_bf16(acc[4] * inv, acc[5] * inv), pack2_bf16(acc[6] * inv, acc[7] * inv));
 }
 
-// The split plan: `slots` workgroups fit on the chip at once (two per CU); whole rounds stay unsplit,
-// and a last round holding at most half the slots is split into parts filling it.
+// The split plan (host_plan.cpp): `slots` workgroups fit on the chip at once (two per CU).
 AttnSplit split_plan(int B, int S, int H) {
+  const AttnSplitPlan pl = attention_split_plan(B, S, H, 2L * device_cu_count());
   AttnSplit sp{};
-  const long total = (long)((S + BQ - 1) / BQ) * H * B;
-  const int ntiles = (S + BKV - 1) / BKV;
-  const long slots = 2L * device_cu_count();
-  sp.n_full = (int)total;
-  sp.n_split = 0;
-  sp.parts = 1;
-  if (total > slots) {
-    const long rem = total % slots;
-    const int parts = rem > 0 ? (int)std::min<long>(std::min<long>(slots / rem, ntiles / 2), 8) : 1;
-    if (rem > 0 && rem * 2 <= slots && parts >= 2) {
-      sp.n_full = (int)(total - rem);
-      sp.n_split = (int)rem;
-      sp.parts = parts;
-    }
-  }
+  sp.n_full = pl.n_full;
+  sp.n_split = pl.n_split;
+  sp.parts = pl.parts;
   return sp;
 }
 
@@ -504,9 +492,7 @@ int device_cu_count() {
 }
 
 size_t attention_split_workspace(int B, int S, int H) {
-  const AttnSplit sp = split_plan(B, S, H);
-  const size_t rows = (size_t)sp.n_split * sp.parts * BQ;
-  return rows == 0 ? 0 : rows * D * 4 + rows * 2 * 4 + 256;
+  return attention_split_bytes(B, S, H, 2L * device_cu_count());
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, void* ws, size_t ws_bytes) {

@@ -433,10 +433,8 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
 }  // namespace
 
 size_t attention_q8_workspace(int B, int S, int H) {
-  const size_t nblk = (size_t)(S + KB - 1) / KB, M = (size_t)B * S, DM = (size_t)H * D;
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al(M * DM) * 2 + al((size_t)B * H * D * nblk * KB) + al(M * H * 4) + al((size_t)B * H * nblk * 4) +
-         al((size_t)B * H * D * 4) + al((size_t)B * H * nblk * D * 4);
+  static_assert(KB == kAttnBKV && D == kHeadDim, "the workspace size assumes 64-key blocks of 128 dims");
+  return attention_q8_bytes(B, S, H);
 }
 
 hipError_t launch_attention_q8(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -4,11 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace moss {
+#include "host_plan.h"
 
-constexpr int kMaxBatch = 8;       // samples per forward call
-constexpr int kRopeMaxPos = 256;   // grid side limit: 4096 px / 16 px per token
-constexpr int kHeadDim = 128;
+namespace moss {
 
 // ---------------------------------------------------------------------------------------------
 // bf16 MFMA GEMM: out[m, n] = epilogue(sum_k A[m, k] * W[n, k]); A [M, K] and W [N, K] row-major.

@@ -102,6 +102,12 @@ typedef struct {
   const void* const* out_w;        /* L x [hidden, hidden]                                             */
   const void* const* gate_up_w;    /* L x [2*ffn, hidden]: rows [gate | up]                             */
   const void* const* down_w;       /* L x [hidden, ffn]                                                */
+  /* Per-head RMSNorm weights of q and k (L x [head_dim]) for a model with QK-norm. The pages mention a
+   * Q/K normalization only for another single-stream DiT (Qwen-Image 2.1 cookbook, "Lossless Q/K
+   * normalization"); MOSS-Image is read as having none, so qk_norm must be 0 and these are ignored
+   * (leave them NULL). The fields keep the struct's layout stable for a later QK-norm build. */
+  const void* const* q_norm_w;
+  const void* const* k_norm_w;
   const void* final_mod_w;         /* [2*hidden, temb]: (shift_f, scale_f)                              */
   const void* final_w;             /* [C*p*p, hidden] output projection                                */
   /* Text refiner (optional: text_proj_w == NULL leaves it out and moss_text_refine returns
@@ -158,8 +164,13 @@ int moss_validate_forward_args(const moss_dit_config* cfg, const moss_forward_ar
 int moss_text_refine(moss_dit* h, int32_t batch, int32_t text_len, const float* enc, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Sigma schedule: sigmas[i] = shift*s/(1 + (shift-1)*s), s = (num_steps - i)/num_steps, i = 0..num_steps
- * (computed in double, stored fp32; sigmas[0] = 1, sigmas[num_steps] = 0). Host only. */
+ * Sigma schedule of the flow-matching Euler sampler with flow shift `shift` (5 by default: "MOSS-Image"
+ * SGLang cookbook, "3. Guidance and precision"; "MOSS-Image: specs, settings, VRAM and text rendering
+ * tested", "Recommended settings": 50 steps, flow-matching Euler, shift 5). The pages name the shift
+ * but print no formula; the reading is the usual shifted flow-matching time grid:
+ *   sigmas[i] = shift*s/(1 + (shift-1)*s), s = (num_steps - i)/num_steps, i = 0..num_steps
+ * (computed in double, stored fp32; sigmas[0] = 1, sigmas[num_steps] = 0). Host only.
+ * Errors: MOSS_ERR_INVALID_ARGUMENT for num_steps < 1, shift <= 0 or not finite, sigmas == NULL. */
 int moss_sigmas(int32_t num_steps, float shift, float* sigmas /* host [num_steps + 1] */);
 
 /* ---------------------------------------------------------------------------------------------
@@ -214,7 +225,14 @@ int moss_validate_step_args(const moss_dit_config* cfg, const moss_step_args* a,
 /* ---------------------------------------------------------------------------------------------
  * The fused FP32 guidance + Euler kernel on its own: x[i] += (sigma_next - sigma) * v[i] with
  * v = v_uncond + cfg*(v_cond - v_uncond), or v = v_cond when v_uncond == NULL (requires cfg == 1).
- * All pointers device fp32 [n], 16-byte aligned. */
+ * Guidance and scheduler arithmetic are FP32 ("MOSS-Image" SGLang cookbook, "3. Guidance and
+ * precision"); the combine is the ordinary linear one (Qwen-Image 2.1 cookbook, "5. Runtime features",
+ * for a sibling single-stream DiT); CFG 1 turns guidance off (InvokeAI guide "MOSS-Image", "Generation
+ * settings"). The Euler update of a flow-matching velocity moves x along v by the sigma step.
+ * All pointers device fp32 [n], 16-byte aligned, owned by the caller; x is updated in place.
+ * Errors (host-side, nothing enqueued): MOSS_ERR_INVALID_ARGUMENT for NULL v_cond / x, n < 0, cfg < 1
+ * or not finite, v_uncond == NULL with cfg != 1, misaligned pointers; MOSS_ERR_DEVICE when the launch
+ * fails. */
 int moss_cfg_euler(const float* v_cond, const float* v_uncond, float* x, int64_t n, float cfg,
                    float sigma, float sigma_next, void* stream);
 

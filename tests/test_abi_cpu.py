@@ -48,15 +48,17 @@ def test_abi_version():
 def test_struct_layouts_match_c_compiler(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moss_dit_ops.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moss_dit_config), '
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moss_dit_config), '
                    'sizeof(moss_dit_weights), sizeof(moss_forward_args), sizeof(moss_step_args), sizeof(moss_block_taps), '
-                   'offsetof(moss_step_args, cfg_scale), offsetof(moss_step_args, n_skip), offsetof(moss_forward_args, sigma));}\n')
+                   'offsetof(moss_step_args, cfg_scale), offsetof(moss_step_args, n_skip), offsetof(moss_forward_args, sigma), '
+                   'offsetof(moss_dit_weights, q_norm_w), offsetof(moss_dit_weights, final_mod_w));}\n')
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     want = [C.sizeof(dt.moss_dit_config), C.sizeof(dt.moss_dit_weights), C.sizeof(dt.moss_forward_args),
             C.sizeof(dt.moss_step_args), C.sizeof(dt.moss_block_taps), dt.moss_step_args.cfg_scale.offset,
-            dt.moss_step_args.n_skip.offset, dt.moss_forward_args.sigma.offset]
+            dt.moss_step_args.n_skip.offset, dt.moss_forward_args.sigma.offset, dt.moss_dit_weights.q_norm_w.offset,
+            dt.moss_dit_weights.final_mod_w.offset]
     assert got == want
 
 
@@ -118,12 +120,12 @@ def test_validate_step_accepts_defaults_and_2048():
 
 
 @pytest.mark.parametrize("field,value,status,needle", [
-    ("latent_h", 127, 1, "multiples of 16"),
-    ("latent_w", 0, 1, "multiples of 16"),
-    ("latent_w", 514, 1, "at most 4096"),
+    ("latent_h", 127, 1, "multiple of 16 px"),
+    ("latent_w", 0, 1, "multiple of 16 px"),
+    ("latent_w", 514, 1, "4096 px"),
     ("text_len", 0, 1, "text_len"),
     ("text_len", 4097, 1, "text_len"),
-    ("cfg_scale", 0.5, 1, "CFG"),
+    ("cfg_scale", 0.5, 1, "cfg_scale"),
     ("step", 50, 1, "step"),
     ("num_steps", 0, 1, "num_steps"),
     ("struct_size", 8, 5, "struct_size"),
