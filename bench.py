@@ -85,6 +85,75 @@ def measured_traffic(kernel_class):
         return None
 
 
+class ClockSampler:
+    """Shader clock of the GPU while it works: a thread reads the current frequency from the driver's
+    DPM table (sysfs pp_dpm_sclk of the card whose PCI address is torch's device 0; the line marked
+    '*') every `period` seconds between start() and stop(). Nothing is read from the GPU itself."""
+
+    def __init__(self, period=0.05):
+        self.period = period
+        self.path = None
+        self.error = None
+        try:
+            import glob
+            import torch
+            pr = torch.cuda.get_device_properties(0)
+            bus = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}"
+            for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+                if bus in os.path.realpath(os.path.dirname(f)):
+                    self.path = f
+                    break
+            if self.path is None:
+                self.error = f"no pp_dpm_sclk for PCI {bus}"
+        except Exception as e:          # the record then says why there is no clock
+            self.error = repr(e)
+        self.samples = []
+
+    def read(self):
+        if not self.path:
+            return None
+        try:
+            for line in open(self.path):
+                if "*" in line:
+                    return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        except Exception as e:
+            self.error = repr(e)
+        return None
+
+    def start(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                v = self.read()
+                if v is not None:
+                    self.samples.append(v)
+                self._stop.wait(self.period)
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+
+    def stop(self):
+        self._stop.set()
+        self._t.join()
+        if not self.samples:
+            return {"median_mhz": None, "n": 0, "error": self.error}
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "n": len(v)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
+
+
 def _host_f64(t):
     import numpy as np
     import torch
@@ -121,6 +190,7 @@ def run_cpu_baseline(weights, nblocks, S, T, gw):
     per_block = el / nblocks
     fwd_s = cfg.num_layers * per_block
     return {"value": 1.0 / fwd_s, "unit": "DiT forwards/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": (f"{nblocks} of 42 joint blocks (+ the modulation MLP) of one sample at 1024^2 "
                        f"(S = {S}: {T} text + {S - T} image tokens), float64 numpy with bf16 storage points "
                        f"mirrored; {el:.1f} s wall; forwards/s = 1 / (42 x {per_block:.2f} s per block)")}
@@ -139,7 +209,9 @@ def main():
     ap.add_argument("--variant-steps", type=int, default=3,
                     help="steps timed for each guidance variant (three-pass SLG, CFG truncation; 0 = skip)")
     ap.add_argument("--steps-2048", type=int, default=2,
-                    help="window steps timed at 2048^2 with 4096 text tokens, for its s/image (0 = skip)")
+                    help="window steps timed at 2048^2 with 4096 text tokens (0 = skip everything at 2048^2)")
+    ap.add_argument("--image-steps-2048", type=int, default=50,
+                    help="steps of the full-image wall time at 2048^2 (seed 42; 0 = skip)")
     ap.add_argument("--step-cache-threshold", type=float, default=0.02,
                     help="a 50-step image with the step cache at this threshold (0 = skip)")
     ap.add_argument("--refiner-reps", type=int, default=3,
@@ -207,14 +279,19 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
+    clock = ClockSampler()
+    clocks = {"idle_before_mhz": clock.read()}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    clock.start()
     start.record()
     for k in range(args.steps):
         step(k)
     end.record()
     end.synchronize()
     torch.cuda.synchronize()
+    clocks["timed_steps"] = clock.stop()
+    clocks["idle_after_mhz"] = clock.read()
     ms_step = start.elapsed_time(end) / args.steps
     fwd_per_s = 2.0 * 1000.0 / ms_step
     def flops_of_step(block_samples, rows, S_, N_):
@@ -253,6 +330,8 @@ def main():
     if dom.startswith("gemm") or dom == "attention":
         roof = {"bound": "mfma", "achieved": kernels[dom]["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": kernels[dom]["frac_mfma_peak"], "traffic": measured_traffic(dom), "kernel": dom,
+                "sclk_mhz_timed_steps": clocks["timed_steps"].get("median_mhz"),
+                "peak_note": "published 2.5 PFLOP/s = 2.4 GHz x 1024 flop/clk per SIMD; see sclk for the clock held",
                 "flops_per_launch": fl / launches, "avg_launch_ms": kernels[dom]["ms_per_step"] / launches}
     else:
         roof = {"bound": "hbm", "achieved": kernels[dom]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -266,11 +345,13 @@ def main():
         x.copy_(x0)
         sig_i = dt.moss_sigmas(args.image_steps, 5.0)
         torch.cuda.synchronize()
+        clock.start()
         start.record()
         for i in range(args.image_steps):
             model.moss_sample_step(x, text_cond, text_uncond, sig_i, i, cfg_scale=3.0, uncond_skip_layers=[22])
         end.record()
         end.synchronize()
+        clocks["image_1024"] = clock.stop()
         s_image = start.elapsed_time(end) / 1000.0
         assert torch.isfinite(x).all().item()
         log(f"[bench] {args.image_steps}-step image: {s_image:.2f} s (DiT + guidance only)")
@@ -328,29 +409,63 @@ def main():
         }
         log(f"[bench] guidance variants: {json.dumps(variants)}")
 
-    # ---- 2048^2 with a 4096-token prompt (16384 image tokens, S = 20480): step 0 (full CFG) and
-    # window steps, 50-step image = step 0 + 49 window steps ----
+    # ---- 2048^2 with a 4096-token prompt (16384 image tokens, S = 20480), seed 42: its own random
+    # weights and inputs; one full 50-step image timed as one wall time (step 0 full CFG, steps 1..49
+    # with the negative pass skipping block 22), plus the step-0 + 49 x window-step estimate as a
+    # cross-check ----
     big = None
     if args.steps_2048 > 0:
-        T2, side2 = 4096, 256
+        T2, side2, seed2 = 4096, 256, 42
         N2 = (side2 // 2) ** 2
         S2 = T2 + N2
-        tc2 = torch.randn((1, T2, D), generator=g, device="cuda", dtype=torch.float32)
+        t0 = time.time()
+        w42 = synth.torch_weights(synth.FULL, seed=seed2, device="cuda")
+        model42 = dt.MossDiT(cfg, w42)
+        del w42
+        g42 = torch.Generator(device="cuda")
+        g42.manual_seed(seed2)
+        tc2 = torch.randn((1, T2, D), generator=g42, device="cuda", dtype=torch.float32)
         tu2 = torch.zeros_like(tc2)
-        x2 = torch.randn((1, 32, side2, side2), generator=g, device="cuda", dtype=torch.float32)
+        x2_0 = torch.randn((1, 32, side2, side2), generator=g42, device="cuda", dtype=torch.float32)
+        x2 = x2_0.clone()
         sig2 = dt.moss_sigmas(50, 5.0)
-        ms0 = timed(lambda k: model.moss_sample_step(x2, tc2, tu2, sig2, 0, cfg_scale=3.0, uncond_skip_layers=[22]), 1)
-        msw = timed(lambda k: model.moss_sample_step(x2, tc2, tu2, sig2, 1 + k, cfg_scale=3.0,
-                                                     uncond_skip_layers=[22]), args.steps_2048)
+        log(f"[bench] 2048^2 model (seed {seed2}) created in {time.time() - t0:.1f} s")
+        ms0 = timed(lambda k: model42.moss_sample_step(x2, tc2, tu2, sig2, 0, cfg_scale=3.0,
+                                                       uncond_skip_layers=[22]), 1)
+        msw = timed(lambda k: model42.moss_sample_step(x2, tc2, tu2, sig2, 1 + k, cfg_scale=3.0,
+                                                       uncond_skip_layers=[22]), args.steps_2048)
+        s_img2 = None
+        if args.image_steps_2048 > 0:
+            x2.copy_(x2_0)
+            sig_i2 = dt.moss_sigmas(args.image_steps_2048, 5.0)
+            torch.cuda.synchronize()
+            clock.start()
+            start.record()
+            for i in range(args.image_steps_2048):
+                model42.moss_sample_step(x2, tc2, tu2, sig_i2, i, cfg_scale=3.0, uncond_skip_layers=[22],
+                                         slg_start=0.01, slg_stop=1.0)
+                if i % 10 == 9:
+                    log(f"[bench] 2048^2 image: step {i + 1} of {args.image_steps_2048} enqueued")
+            end.record()
+            end.synchronize()
+            clocks["image_2048"] = clock.stop()
+            s_img2 = start.elapsed_time(end) / 1000.0
         assert torch.isfinite(x2).all().item()
         fw = flops_of_step(2 * L - 1, 2, S2, N2)
-        big = {"s_per_image": round((ms0 + 49 * msw) / 1000.0, 3), "ms_step0": round(ms0, 2),
-               "ms_per_window_step": round(msw, 2), "seq_len": S2, "text_len": T2, "image_tokens": N2,
-               "tflops": round(fw / (msw * 1e-3) / 1e12, 1),
-               "mfma_fraction": round(fw / (msw * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
-               "method": "step 0 (full CFG) + 49 x the mean of the timed window steps (negative pass skips 22)"}
+        fw0 = flops_of_step(2 * L, 2, S2, N2)
+        big = {"s_per_image": round(s_img2, 3) if s_img2 else None, "image_steps": args.image_steps_2048,
+               "seed": seed2, "method": "wall time of the 50 moss_sample_step calls between two events",
+               "s_per_image_estimate": round((ms0 + 49 * msw) / 1000.0, 3),
+               "estimate_method": "step 0 (full CFG) + 49 x the mean of the timed window steps",
+               "ms_step0": round(ms0, 2), "ms_per_window_step": round(msw, 2), "seq_len": S2, "text_len": T2,
+               "image_tokens": N2, "tflops": round(fw / (msw * 1e-3) / 1e12, 1),
+               "mfma_fraction": round(fw / (msw * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)}
+        if s_img2:
+            img_flops = fw0 + (args.image_steps_2048 - 1) * fw
+            big["image_mfma_fraction"] = round(img_flops / s_img2 / (PEAK_BF16_TFLOPS * 1e12), 4)
         log(f"[bench] 2048^2: {json.dumps(big)}")
-        del tc2, tu2, x2
+        model42.close()
+        del model42, tc2, tu2, x2, x2_0
 
     # ---- text refiner (projection 4096 -> 3072 + two text-only blocks), once per prompt ----
     refiner = None
@@ -440,6 +555,7 @@ def main():
         "text_refiner": refiner,
         "fp8_tier": fp8,
         "cpu_baseline": cpu,
+        "clocks": clocks,
     }
     print(json.dumps(out), flush=True)
     model.close()
