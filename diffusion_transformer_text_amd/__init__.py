@@ -107,6 +107,7 @@ _sig("moss_dit_block", C.c_int, _P, C.c_int32, _P, C.c_int32, C.c_int32, C.c_int
 _sig("moss_step_cache_stats", C.c_int, _P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_float))
 _sig("moss_text_refine", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, _P)
 _sig("moss_attention", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P)
+_sig("moss_attention_noalloc", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_gemm_bf16", C.c_int, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_mx_quantize", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, C.c_int64, _P)
 _sig("moss_attention_q8_workspace", C.c_int64, C.c_int32, C.c_int32, C.c_int32)
@@ -124,7 +125,7 @@ EXPORTED = ["moss_dit_abi_version", "moss_status_string", "moss_dit_last_error",
             "moss_dit_forward", "moss_validate_forward_args", "moss_sigmas", "moss_step_args_init",
             "moss_sample_step", "moss_validate_step_args", "moss_cfg_euler", "moss_guidance_euler",
             "moss_text_refine", "moss_step_cache_stats", "moss_dit_modulation",
-            "moss_block_taps_init", "moss_dit_block", "moss_attention", "moss_gemm_bf16",
+            "moss_block_taps_init", "moss_dit_block", "moss_attention", "moss_attention_noalloc", "moss_gemm_bf16",
             "moss_mx_quantize", "moss_gemm_mxfp8", "moss_attention_q8_workspace", "moss_attention_q8",
             "moss_dit_profile_enable", "moss_dit_profile_read"]
 
@@ -239,6 +240,18 @@ def moss_attention(qkv, out, batch: int, seq: int, heads: int, text_len: int, gr
     if qkv.numel() != batch * seq * 3 * heads * 128 or out.numel() != batch * seq * heads * 128:
         raise ValueError("qkv / out sizes do not match batch, seq, heads")
     _check(_lib.moss_attention(_ptr(qkv), _ptr(out), batch, seq, heads, text_len, grid_w, int(rope), _stream(stream)))
+
+
+def moss_attention_noalloc(qkv, out, batch: int, seq: int, heads: int, text_len: int, grid_w: int, rope: bool = True,
+                           stream=None):
+    """moss_attention on the library's static per-GPU scratch: no device allocation, no synchronisation."""
+    import torch
+    _check_dev(qkv, torch.bfloat16, "qkv")
+    _check_dev(out, torch.bfloat16, "out")
+    if qkv.numel() != batch * seq * 3 * heads * 128 or out.numel() != batch * seq * heads * 128:
+        raise ValueError("qkv / out sizes do not match batch, seq, heads")
+    _check(_lib.moss_attention_noalloc(_ptr(qkv), _ptr(out), batch, seq, heads, text_len, grid_w, int(rope),
+                                       _stream(stream)))
 
 
 def moss_gemm_bf16(A, W, out, stream=None):

@@ -58,6 +58,21 @@ int moss_dit_block(moss_dit* h, int32_t layer, void* x, int32_t batch, int32_t t
 int moss_attention(void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, int32_t text_len,
                    int32_t grid_w, int32_t rope, void* stream);
 
+/* moss_attention for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments, kernels and results (bit for
+ * bit), but no allocation and no synchronisation. The split tail's partial results go to a static
+ * device array of MOSS_ATTENTION_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends, and the
+ * RoPE table to a second static array; the first call on each device sets them up (their device
+ * addresses, and a synchronous host-to-device copy of the table), so make that first call outside
+ * graph capture. Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (different streams, or different threads) race; serialise them. Returns MOSS_ERR_INVALID_ARGUMENT
+ * for the arguments moss_attention refuses and when a shape's split needs more scratch than the array
+ * holds (only possible on a chip with more than 256 compute units), MOSS_ERR_DEVICE when the set-up or
+ * a launch fails. */
+#define MOSS_ATTENTION_NOALLOC_SCRATCH_BYTES (33L << 20)
+int moss_attention_noalloc(void* qkv, void* out, int32_t batch, int32_t seq, int32_t heads, int32_t text_len,
+                           int32_t grid_w, int32_t rope, void* stream);
+
 /* 8-bit attention (the FP8 tier's attention: the pages' q8_fp8 mode -- 8-bit Q and K, FP8 P V; MossInfer
  * integration guide, "Quality tier" and its attention modes). Reading (the pages give no formula): Q
  * symmetric INT8 per token and head (scale amax/127), K symmetric INT8 per block of 64 consecutive keys
