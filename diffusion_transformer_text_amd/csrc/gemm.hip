@@ -281,21 +281,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_kernel(Ge
 }
 
 // ---------------------------------------------------------------------------------------------
-// Deep-pipelined variant for the big projections: BK = 32 and four LDS stages (the same 128 KB as two
-// stages of BK = 64), so a k-tile's global -> LDS copies are issued three k-tiles before it is used
-// and have about three times as long to land. The stages are four separate LDS arrays and the k loop
-// is unrolled by four, so every LDS access names a fixed array: the compiler then sees that reading
-// one stage does not alias the copies still landing in the others and does not wait for them. The
-// wait for a k-tile is explicit (s_waitcnt vmcnt(N) with N = the copies issued after that k-tile),
-// followed by a barrier; the barrier sits between the two k16 slices of the previous k-tile, so the
-// next k-tile's first fragment reads overlap the second slice's MFMAs.
+// Big projections: BK = 32 and four LDS stages (the same 128 KB as two stages of BK = 64), so a
+// k-tile's global -> LDS copies are issued three k-tiles before it is used. The stages are four
+// separate LDS arrays and the k loop is unrolled by four, so every LDS access names a fixed array:
+// the compiler then sees that reading one stage does not alias the copies still landing in the others
+// and does not wait for them. The wait for a k-tile is explicit (s_waitcnt vmcnt(N) with N = the
+// copies issued after that k-tile), followed by a barrier.
 // LDS rows are 32 bf16 (64 bytes, four 16-byte chunks); chunk c of row r is stored at chunk
 // c ^ ((r >> 2) & 3): the 16 rows a ds_read_b128 phase reads then cover 16 distinct (bank quarter,
 // chunk) slots (conflict-free), and a 1 KB copy window holds 16 whole rows.
 constexpr int BK2 = 32;
 __device__ __forceinline__ int swz2(int r, int c) { return r * BK2 + ((c ^ ((r >> 2) & 3)) << 3); }
 
-// Workgroup barrier for the deep pipeline: s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier. vmcnt(N)
+// Workgroup barrier of the pipeline: s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier. vmcnt(N)
 // leaves only the N newest copies in flight (the main loop issues no other vector-memory
 // instruction, and they complete in order), lgkmcnt(0) finishes this wave's LDS reads (so a stage
 // may be refilled after the barrier). The barrier is written as asm with a memory clobber on
@@ -309,9 +307,35 @@ __device__ __forceinline__ void copy_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_deep_kernel(GemmArgs p) {
-  using T = Tile<BM, BN, WAVES_M, WAVES_N>;
+// ---------------------------------------------------------------------------------------------
+// Ping-pong GEMM for the big projections: a 256 x 256 tile, BK = 32 k-tiles in four LDS stages, eight
+// waves in two groups of four (waves 0-3 and 4-7; wave w runs on SIMD w % 4, so every SIMD holds one
+// wave of each group). Group g owns rows [128 g, 128 g + 128) of the tile, each of its waves 128 rows x
+// 64 features (4 x 2 accumulator blocks of 32 x 32). The groups alternate, half a k-tile apart, between
+// a COMPUTE phase -- the 16 MFMAs of one k-tile on fragments already in registers, with no memory
+// instruction in between, at raised wave priority -- and a MEMORY phase -- this wave's four global ->
+// LDS copies three k-tiles ahead and the twelve fragment reads of its next k-tile. While one wave of a
+// SIMD computes, the other loads, so the matrix pipe always has a wave with its operands ready; a
+// workgroup barrier separates consecutive phases.
+//
+// Phases (k-tile t, KT k-tiles): phase 2t: group 0 computes t, group 1 loads t; phase 2t + 1: group 1
+// computes t, group 0 loads t + 1 (group 0 loads k-tile 0 in phase -1). Each memory phase for k-tile t
+// issues the copies of k-tile t + 3 into the stage of k-tile t - 1, which both groups finished reading
+// before the previous barrier. Every wave issues 4 copies per memory phase (copies past the last
+// k-tile point beyond the buffer: the range check writes zeros to a stage no longer read), so before
+// every barrier `vmcnt(8)` leaves exactly the two newest k-tiles' copies in flight and k-tile t + 1 is
+// in LDS, from every wave, by the start of the phase that first reads it.
+//
+// Measured against the same tile computed by eight waves that each interleave copies, fragment reads
+// and MFMAs (one barrier per k-tile; bit-identical results): 5-7 % faster on the four projections.
+// Under this load the chip is power-limited: the ping-pong raises the matrix pipe's busy fraction to
+// about 0.67 while the clock falls to about 1.7 GHz (rocprofv3 GRBM_GUI_ACTIVE over the kernel), a
+// register-only MFMA loop with random operands runs at about 1.77 GHz; two k-tiles per phase (half the
+// barriers) and splitting the fragment reads between the two phases were slower or equal.
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(GemmArgs p) {
+  constexpr int BM = 256, BN = 256;
+  using T = Tile<BM, BN, 2, 4>;                           // wave tile 128 x 64: TM = 4, TN = 2
   constexpr int SZ = (BM + BN) * BK2;                     // elements per stage: A rows, then W rows
   __shared__ __attribute__((aligned(16))) uint16_t st0[SZ];
   __shared__ __attribute__((aligned(16))) uint16_t st1[SZ];
@@ -319,7 +343,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_deep_kern
   __shared__ __attribute__((aligned(16))) uint16_t st3[SZ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wm = wave >> 2, wn = wave & 3;               // wm = the wave's group
   const int nN = p.N / BN, nM = (p.M + BM - 1) / BM;
   int tm, tn;
   tile_coords(nM, nN, tm, tn);
@@ -327,11 +351,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_deep_kern
 
   // copy windows: 16 rows x 64 bytes; lane i writes LDS bytes 16 i (row i / 4, physical chunk i % 4)
   // and so reads logical chunk (i % 4) ^ ((row >> 2) & 3) = (i % 4) ^ ((i >> 4) & 3) of its row
-  constexpr int A_WIN = BM / 16, W_WIN = BN / 16;
-  constexpr int A_PER_WAVE = A_WIN / T::NW, W_PER_WAVE = W_WIN / T::NW;
-  constexpr int LOADS = A_PER_WAVE + W_PER_WAVE;          // copies per wave per k-tile
-  static_assert(A_WIN % T::NW == 0 && W_WIN % T::NW == 0, "windows must split evenly over the waves");
-  static_assert(2 * LOADS < 16, "vmcnt immediate");
+  constexpr int A_PER_WAVE = BM / 16 / T::NW, W_PER_WAVE = BN / 16 / T::NW;   // 2 + 2 copy windows
+  constexpr int LOADS = A_PER_WAVE + W_PER_WAVE;
+  static_assert(LOADS == 4, "the vmcnt counts below assume four copies per wave per k-tile");
   const int win_row = lane >> 2, win_chunk = (lane & 3) ^ ((lane >> 4) & 3);
   uint32_t a_off[A_PER_WAVE], w_off[W_PER_WAVE];
 #pragma unroll
@@ -344,16 +366,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_deep_kern
     const int r = n0 + (wave + T::NW * j) * 16 + win_row;
     w_off[j] = (uint32_t)(r * p.ldw + win_chunk * 8);
   }
-  // copies go through buffer resources over A and W (byte offsets < 2^31, checked at launch)
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (int)(2L * p.M * p.lda));
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, (int)(2L * p.N * p.ldw));
+  const int KT = p.K / BK2;                               // a multiple of 4 (checked at launch)
   auto issue = [&](int kt, uint16_t* st) {
+    const bool real = kt < KT;
     const int k0 = kt * BK2;
 #pragma unroll
-    for (int j = 0; j < A_PER_WAVE; ++j) buf_load_lds_16(rA, st + (wave + T::NW * j) * 512, 2 * (int)(a_off[j] + k0));
+    for (int j = 0; j < A_PER_WAVE; ++j)
+      buf_load_lds_16(rA, st + (wave + T::NW * j) * 512, real ? 2 * (int)(a_off[j] + k0) : 0x7ffffff0);
 #pragma unroll
     for (int j = 0; j < W_PER_WAVE; ++j)
-      buf_load_lds_16(rW, st + BM * BK2 + (wave + T::NW * j) * 512, 2 * (int)(w_off[j] + k0));
+      buf_load_lds_16(rW, st + BM * BK2 + (wave + T::NW * j) * 512, real ? 2 * (int)(w_off[j] + k0) : 0x7ffffff0);
   };
 
   floatx16 acc[T::TM][T::TN];
@@ -366,59 +390,89 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void gemm_bf16_deep_kern
 
   const int fr = lane & 31, fh = lane >> 5;
   const int a_row0 = wm * T::WM + fr, w_row0 = wn * T::WN + fr;
-  bf16x8 fa[2][T::TM], fw[2][T::TN];
-  auto load_frags = [&](const uint16_t* st, int s, int buf) {
+  bf16x8 fa[2][T::TM], fw[2][T::TN];                      // [k16 slice][block] of the next k-tile
+  // memory phase: copies of k-tile `kt_issue` into `fill`, then the fragments of the k-tile in `cur`
+  auto mem = [&](const uint16_t* cur, int kt_issue, uint16_t* fill) {
+    issue(kt_issue, fill);
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-      fa[buf][i] = *reinterpret_cast<const bf16x8*>(st + swz2(a_row0 + i * 32, 2 * s + fh));
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int j = 0; j < T::TN; ++j)
-      fw[buf][j] = *reinterpret_cast<const bf16x8*>(st + BM * BK2 + swz2(w_row0 + j * 32, 2 * s + fh));
-  };
-  auto mfmas = [&](int buf) {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i)
+      for (int i = 0; i < T::TM; ++i)
+        fa[s][i] = *reinterpret_cast<const bf16x8*>(cur + swz2(a_row0 + i * 32, 2 * s + fh));
 #pragma unroll
       for (int j = 0; j < T::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+        fw[s][j] = *reinterpret_cast<const bf16x8*>(cur + BM * BK2 + swz2(w_row0 + j * 32, 2 * s + fh));
+    }
+  };
+  auto compute = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s][j], fa[s][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  const int KT = p.K / BK2;                               // a multiple of 4 (checked at launch)
+  auto bar = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    copy_barrier<2 * LOADS>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   issue(0, st0);
   issue(1, st1);
   issue(2, st2);
-  copy_barrier<2 * LOADS>();                              // k-tile 0 has landed
-  load_frags(st0, 0, 0);
-  // Step t: k-tile t is in stage t % 4 and its slice-0 fragments are in flight in buffer 0. ISSUE:
-  // copy k-tile t + 3 into `fill` (the stage of k-tile t - 1, whose last reads finished before the
-  // previous barrier). AFTER: k-tiles issued after k-tile t + 1 (2 in steady state; -1 = no next).
-  auto step = [&](auto issue_c, auto after_c, int t, const uint16_t* cur, const uint16_t* nxt, uint16_t* fill) {
-    constexpr bool ISSUE = decltype(issue_c)::value;
-    constexpr int AFTER = decltype(after_c)::value;
-    if constexpr (ISSUE) issue(t + 3, fill);
-    load_frags(cur, 1, 1);
-    mfmas(0);
-    if constexpr (AFTER >= 0) {
-      copy_barrier<AFTER * LOADS>();
-      load_frags(nxt, 0, 0);
+  bar();                                                  // k-tile 0 has landed (phase -1 starts)
+  if (wm == 0) {
+    mem(st0, 3, st3);                                     // phase -1: load k-tile 0
+    bar();
+    for (int t = 0; t < KT; t += 4) {                     // k-tiles t .. t + 3 (stages 0 .. 3)
+      compute();                                          // phase 2t
+      bar();
+      mem(st1, t + 4, st0);                               // phase 2t + 1: load t + 1, copy t + 4
+      bar();
+      compute();
+      bar();
+      mem(st2, t + 5, st1);
+      bar();
+      compute();
+      bar();
+      mem(st3, t + 6, st2);
+      bar();
+      compute();                                          // k-tile t + 3
+      bar();
+      if (t + 4 < KT) {
+        mem(st0, t + 7, st3);
+        bar();
+      }
     }
-    mfmas(1);
-  };
-  using Y = std::true_type;
-  using N = std::false_type;
-  using A2 = std::integral_constant<int, 2>;
-  int t = 0;
-  for (; t + 4 < KT; t += 4) {                            // steady state: straight-line code
-    step(Y{}, A2{}, t, st0, st1, st3);
-    step(Y{}, A2{}, t + 1, st1, st2, st0);
-    step(Y{}, A2{}, t + 2, st2, st3, st1);
-    step(Y{}, A2{}, t + 3, st3, st0, st2);
+  } else {
+    bar();                                                // phase -1: nothing to do
+    for (int t = 0; t < KT; t += 4) {
+      mem(st0, t + 3, st3);                               // phase 2t: load t, copy t + 3
+      bar();
+      compute();                                          // phase 2t + 1
+      bar();
+      mem(st1, t + 4, st0);
+      bar();
+      compute();
+      bar();
+      mem(st2, t + 5, st1);
+      bar();
+      compute();
+      bar();
+      mem(st3, t + 6, st2);
+      bar();
+      compute();                                          // k-tile t + 3
+      if (t + 4 < KT) bar();
+    }
   }
-  step(Y{}, A2{}, t, st0, st1, st3);                      // last four k-tiles: t = KT - 4
-  step(N{}, std::integral_constant<int, 1>{}, t + 1, st1, st2, st0);
-  step(N{}, std::integral_constant<int, 0>{}, t + 2, st2, st3, st1);
-  step(N{}, std::integral_constant<int, -1>{}, t + 3, st3, st0, st2);
+  // the look-ahead copies (zeros into unused stages) land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);                     // vmcnt(0)
   store_tile<T, EPI>(p, acc, m0, n0, wm, wn, fr, fh);
 }
 
@@ -649,12 +703,10 @@ __global__ void interleave_gate_up_kernel(const uint16_t* __restrict__ src, uint
 
 }  // namespace
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-hipError_t launch_tile_deep(const GemmArgs& a, int epi, hipStream_t stream) {
-  const int nM = (a.M + BM - 1) / BM, nN = a.N / BN;
-  dim3 grid(nM * nN), block(64 * WAVES_M * WAVES_N);
-#define MOSS_GEMM_LAUNCH(E) \
-  hipLaunchKernelGGL((gemm_bf16_deep_kernel<BM, BN, WAVES_M, WAVES_N, E>), grid, block, 0, stream, a)
+static hipError_t launch_tile_pp(const GemmArgs& a, int epi, hipStream_t stream) {
+  const int nM = (a.M + 255) / 256, nN = a.N / 256;
+  dim3 grid(nM * nN), block(512);
+#define MOSS_GEMM_LAUNCH(E) hipLaunchKernelGGL((gemm_bf16_pp_kernel<E>), grid, block, 0, stream, a)
   switch (epi) {
     case EPI_BF16: MOSS_GEMM_LAUNCH(EPI_BF16); break;
     case EPI_QKV_ROPE: MOSS_GEMM_LAUNCH(EPI_QKV_ROPE); break;
@@ -678,7 +730,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t stream) {
   // 256 x 256 tiles from half a round of the chip on: one batch-1 out / down projection (204 tiles)
   // runs 25-30 % faster on them than as 816 tiles of 128 x 128 (measured)
   if (big_n && epi != EPI_F32_UNPATCH && a.M > 1024 && tiles256 >= 128) {
-    if (fits32 && a.K % (4 * BK2) == 0) return launch_tile_deep<256, 256, 2, 4>(a, epi, stream);
+    if (fits32 && a.K % (4 * BK2) == 0) return launch_tile_pp(a, epi, stream);
     return launch_tile<256, 256, 2, 4>(a, epi, stream);
   }
   if (a.N % 128 == 0) return launch_tile<128, 128, 2, 2>(a, epi, stream);
