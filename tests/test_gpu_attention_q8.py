@@ -11,6 +11,11 @@
   accumulation: bound 4e-3 relative L2.
 * Special cases: one key and V constant over keys give V exactly (convex weights); a dominant key
   gives its dequantized V row (to the bf16 rounding of the output).
+* Independently of the online schedule (the oracle's attention_q8 runs the same blocked softmax with
+  the same lazy reference max, so it cannot catch a schedule error both share): the exact fp64 softmax
+  attention on the dequantized operands, and a per-element bound that holds for any schedule that
+  rounds each probability to E4M3 on the 224 scale against a reference max at most the row max and
+  normalises by the sum of the same rounded probabilities (tests/q8_bound.py).
 
 Each case logs its name and shape before touching the GPU."""
 import numpy as np
@@ -19,6 +24,7 @@ import pytest
 import oracle as O
 from synth import bf16_normal_bits, f32_to_bf16_bits
 from tests.gpu_util import dev_bf16, host_bf16, host_bits, log, rel_l2
+from tests.q8_bound import exact_on_quantized
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -180,3 +186,33 @@ def test_attention_q8_special_cases():
     vc, va = O.fp8_quantize_v(xv[:, 256:])
     # v_hat has up to 12 significant bits: the bf16 output is within half a bf16 unit of it
     np.testing.assert_allclose(got[0], np.tile(vc[37] * va / O.E4M3_MAX, (S, 1)), rtol=2.0 ** -8, atol=0)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B,S,amp", [(2, 200, 1.0), (1, 333, 4.0), (2, 4352, 1.0), (1, 4352, 4.0), (1, 20480, 1.0)])
+def test_attention_q8_within_p_rounding_bound_of_exact_softmax(B, S, amp):
+    """amp scales q and k (amp 4: scores spread over about +-60, the running max moves by far more than
+    a factor 2 in many blocks, so the rescales carry most of the result)."""
+    H = 24 if S >= 4352 else 2
+    log(f"8-bit attention vs exact softmax on quantized operands B={B} S={S} H={H} amp={amp}")
+    rng = np.random.default_rng(90 + S)
+    x = O.from_bf16_bits(bf16_normal_bits(rng, (B, S, 3 * H * 128)))
+    x[..., :2 * H * 128] *= amp
+    bits = f32_to_bf16_bits(x.astype(np.float32))
+    got, _ = _run(bits, B, S, H)
+    x = O.from_bf16_bits(bits)
+    rows = np.arange(S) if S <= 512 else np.unique(np.concatenate([rng.integers(0, S, 10), [0, S - 1]]))
+    worst = 0.0
+    for b in range(B):
+        for h in ([0, 1] if H == 2 else [0, 11, 23]):
+            q = x[b][rows, h * 128:(h + 1) * 128]
+            k = x[b][:, (H + h) * 128:(H + h + 1) * 128]
+            v = x[b][:, (2 * H + h) * 128:(2 * H + h + 1) * 128]
+            ref, bound = exact_on_quantized(q, k, v)
+            g = got[b][rows][:, h * 128:(h + 1) * 128]
+            allowed = bound + np.abs(g) * 2.0 ** -8 + 1e-6     # + the bf16 rounding of the output
+            err = np.abs(g - ref)
+            worst = max(worst, float((err / allowed).max()))
+            assert np.all(err <= allowed), (b, h, float((err - allowed).max()))
+    log(f"  largest error / bound {worst:.3f}")
+
