@@ -44,6 +44,14 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
 }
 
+// Row sum of the probabilities as the P V product sees them: the two bf16 values of a packed pair are
+// added into the fp32 sum by one v_dot2 against (1, 1), half the VALU issues of adding the fp32 values
+// one by one. Numerator and normaliser then weight each value row by the same rounded probability.
+__device__ __forceinline__ float add_pair_bf16(float acc, uint32_t w) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 // Work split of one launch: workgroups [0, n_full) each take a whole query tile (all keys); each of the
 // n_split leftover tiles (tile index n_full + j) is split along its key tiles into `parts` workgroups
 // that write unnormalised partial results (o, running max, sum) for merge_kernel.
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
       m_run = m_new;
     }
   };
-  // P = exp2(s c - m c) as bf16 MFMA operands, and the running row sum
+  // P = exp2(s c - m c) as bf16 MFMA operands, and the running row sum of those bf16 values
   auto probs = [&](const floatx16 (&sc)[2], bf16x8 (&pf)[2][2]) {
     const float mc = m_run * c;
     float lsum = 0.f;
@@ -194,13 +202,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
       for (int hs = 0; hs < 2; ++hs) {
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = __builtin_amdgcn_exp2f(sc[kb][8 * hs + j] * c - mc);
-          lsum += pv[j];
-        }
+        for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(sc[kb][8 * hs + j] * c - mc);
         u32x4 w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = pack2_bf16(pv[2 * j], pv[2 * j + 1]);
+        for (int j = 0; j < 4; ++j) {
+          w[j] = pack2_bf16(pv[2 * j], pv[2 * j + 1]);
+          lsum = add_pair_bf16(lsum, w[j]);
+        }
         pf[kb][hs] = __builtin_bit_cast(bf16x8, w);
       }
     }
@@ -269,8 +277,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
           kf[i & 3] = *reinterpret_cast<const bf16x8*>(tK + (i & 1) * 32 * D + k_ofs[(i + 4) >> 1]);
         const float p0 = __builtin_amdgcn_exp2f(s_cur[i >> 3][2 * (i & 7)] * c - mc);
         const float p1 = __builtin_amdgcn_exp2f(s_cur[i >> 3][2 * (i & 7) + 1] * c - mc);
-        lsum += p0 + p1;
         w[i >> 2][i & 3] = pack2_bf16(p0, p1);
+        lsum = add_pair_bf16(lsum, w[i >> 2][i & 3]);
         __builtin_amdgcn_sched_barrier(0);
       }
       l_run += lsum;
