@@ -70,7 +70,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
   __shared__ __attribute__((aligned(16))) uint16_t sV0[BKV * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[BKV * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index, read once into a scalar register so that per-wave addresses (the LDS windows of
+  // the direct loads) are scalar arithmetic instead of a v_readfirstlane per copy
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, fh = lane >> 5;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). Remap the linear
   // id so that XCD x runs a contiguous range of (sample, head) pairs with all their query tiles:

@@ -226,7 +226,8 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t st3[2 * KB * D];
   __shared__ float s_ka[kMaxKeyBlocks];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register: per-wave addresses (LDS windows of the direct loads) stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, fh = lane >> 5;
   const int nq = (p.S + BQ - 1) / BQ;
   const int total = nq * p.H * p.B;

@@ -342,7 +342,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_pp_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t st2[SZ];
   __shared__ __attribute__((aligned(16))) uint16_t st3[SZ];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register: per-wave addresses (LDS windows of the direct loads) stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;               // wm = the wave's group
   const int nN = p.N / BN, nM = (p.M + BM - 1) / BM;
   int tm, tn;
@@ -527,7 +528,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp8_pp_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t st2[SZ];
   __shared__ __attribute__((aligned(16))) uint8_t st3[SZ];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register: per-wave addresses (LDS windows of the direct loads) stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;               // wm = the wave's group
   const int nN = p.N / BN, nM = (p.M + BM - 1) / BM;
   int tm, tn;
