@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void vt8_quant_kernel(AttnQ8Args p) {
     const int d = 32 * c + e;
     const float a0 = s_va[d] > 0.f ? __fdiv_rn(v[e] * kE4M3Max, s_va[d]) : 0.f;
     const float a1 = s_va[d + 1] > 0.f ? __fdiv_rn(v[e + 1] * kE4M3Max, s_va[d + 1]) : 0.f;
-    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, __float_as_int(a0), false);   // bytes 2-3 unused
     s_t[d][pos] = (uint8_t)(w & 0xff);
     s_t[d + 1][pos] = (uint8_t)((w >> 8) & 0xff);
   }
@@ -345,7 +345,10 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
         a[i] = __builtin_fmaf((float)si[kb][e0 + i], f, -m_b);
         if (MASK && k0 + 32 * kb + 8 * (e0 >> 2) + 4 * fh + i >= S) a[i] = -INFINITY;
       }
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(a[0]), __builtin_amdgcn_exp2f(a[1]), 0, false);
+      // bytes 2-3 of the first conversion's third operand are overwritten by the second: the first
+      // probability's own register serves, so no zero is materialised per word
+      const float p0 = __builtin_amdgcn_exp2f(a[0]);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, __builtin_amdgcn_exp2f(a[1]), __float_as_int(p0), false);
       w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(a[2]), __builtin_amdgcn_exp2f(a[3]), w, true);
       pf[u] = w;
     }

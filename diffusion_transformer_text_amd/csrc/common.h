@@ -82,7 +82,10 @@ __device__ __forceinline__ float mx_inv_scale(int ex) { return __uint_as_float((
 __device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d, float inv) {
   const float a0 = fminf(fmaxf(a * inv, -448.f), 448.f), a1 = fminf(fmaxf(b * inv, -448.f), 448.f);
   const float a2 = fminf(fmaxf(c * inv, -448.f), 448.f), a3 = fminf(fmaxf(d * inv, -448.f), 448.f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  // The first conversion writes bytes 0-1 and keeps bytes 2-3 of its third operand, which the second
+  // conversion then overwrites: a0's own bits serve as that operand, so the result is written in place
+  // of a dead register instead of a zero materialised first.
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, __float_as_int(a0), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, w, true);
   return (uint32_t)w;
 }
