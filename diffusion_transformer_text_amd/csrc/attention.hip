@@ -153,7 +153,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // running max in the exp2 domain (m c, m the largest score seen when it last moved) and running sum of
+  // the bf16 probabilities
+  float mc_run = 0.f, l_run = 0.f;
   const float c = p.scale_log2;
 
   // S^T = K Q^T for the 64 keys of one LDS tile (2 blocks of 32 keys)
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
       }
     }
   };
-  // row max of one tile's scores: in-lane over 32 values, then with lane ^ 32 (same query)
+  // row max of one tile's values: in-lane over 32 values, then with lane ^ 32 (same query)
   auto rowmax = [&](const floatx16 (&sc)[2]) {
     float mx = -INFINITY;
 #pragma unroll
@@ -178,25 +180,42 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
       for (int e = 0; e < 16; e += 2) mx = max3_f32(mx, sc[kb][e], sc[kb][e + 1]);
     return max_xor32(mx);
   };
-  // The running max only moves when a score exceeds it by more than 2^8 in the exp2 domain: with a
-  // stale max the probabilities stay below 256 (exact in fp32, same relative precision in bf16), the
-  // final normalisation divides by the sum taken against the same max, so the result is unchanged
-  // while the O rescale (64 multiplies per lane) runs only a few times per row.
-  auto maybe_rescale = [&](float mx) {
-    if (__any((mx - m_run) * c > 8.0f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+  // keys of tile t past the end of the sequence (only the last tile has any) get -inf
+  auto mask_tail = [&](floatx16 (&sc)[2], int t) {
+    const int k0 = t * BKV;
+    if (k0 + BKV <= S) return;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * fh + (e & 3);
+        if (key >= S) sc[kb][e] = -INFINITY;
+      }
+  };
+  // A tile's scores are turned into x = s c - m c (one fma each) as soon as they exist, and its
+  // probabilities are exp2(x). The running max only moves when a tile's largest x exceeds 8 (2^8 in
+  // the probabilities): with a stale max the probabilities stay below 256 (exact in fp32, the same
+  // relative precision in bf16), and the final normalisation divides by the sum taken against the same
+  // max, so the result is unchanged while the O rescale (64 multiplies per lane) runs only a few times
+  // per row. A move by d rescales O and the sum by 2^-d and shifts the tile's x by -d.
+  auto maybe_shift = [&](float mx, floatx16 (&x)[2]) {
+    if (__any(mx > 8.0f)) {
+      const float d = mx > 8.0f ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-d);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-      m_run = m_new;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[kb][e] -= d;
+      mc_run += d;
     }
   };
-  // P = exp2(s c - m c) as bf16 MFMA operands, and the running row sum of those bf16 values
-  auto probs = [&](const floatx16 (&sc)[2], bf16x8 (&pf)[2][2]) {
-    const float mc = m_run * c;
+  // P = exp2(x) as bf16 MFMA operands, and the running row sum of those bf16 values
+  auto probs = [&](const floatx16 (&x)[2], bf16x8 (&pf)[2][2]) {
     float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -204,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
       for (int hs = 0; hs < 2; ++hs) {
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(sc[kb][8 * hs + j] * c - mc);
+        for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(x[kb][8 * hs + j]);
         u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -246,21 +265,27 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
   lds_copy_barrier();
   floatx16 s_cur[2];
   scores(sK0, s_cur);
-  float mx_cur = rowmax(s_cur);
-  // s_cur holds S(t) on entry; S(t+1) is written to s_next (the unrolled pair swaps the two)
+  mask_tail(s_cur, t_begin);         // a first tile that is also the last one: mask before the first max
+  mc_run = rowmax(s_cur) * c;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s_cur[kb][e] = s_cur[kb][e] * c - mc_run;
+  float mx_cur = 0.f;                // the first tile's x are relative to its own max
+  // s_cur holds x(t) on entry; S(t+1) is written to s_next and turned into x(t+1) there (the unrolled
+  // pair swaps the two)
   auto iteration = [&](int t, uint16_t* kFree, const uint16_t* kNext, uint16_t* vFree, const uint16_t* vCur,
                        floatx16 (&s_cur)[2], floatx16 (&s_next)[2]) {
     lds_copy_barrier();              // K(t+1) and V(t) have landed; kFree and vFree are no longer read
     if (t + 2 < t_end) issue_k(t + 2, kFree);
     issue_v(t + 1, vFree);
-    maybe_rescale(mx_cur);
-    // region A: S(t+1) on the matrix core while the VALU turns S(t) into probabilities. Step i issues
+    maybe_shift(mx_cur, s_cur);
+    // region A: S(t+1) on the matrix core while the VALU turns x(t) into probabilities. Step i issues
     // one MFMA (accumulators alternate so consecutive MFMAs are independent), the LDS read of the K
-    // fragment four steps ahead, and the exp2/sum/pack of two scores; sched_barrier keeps that order.
+    // fragment four steps ahead, and the exp2/pack/sum of two scores; sched_barrier keeps that order.
     bf16x8 pf[2][2];
     {
       const uint16_t* tK = kNext;
-      const float mc = m_run * c;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -277,8 +302,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
         s_next[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], qf[i >> 1], s_next[i & 1], 0, 0, 0);
         if (i + 4 < 16)
           kf[i & 3] = *reinterpret_cast<const bf16x8*>(tK + (i & 1) * 32 * D + k_ofs[(i + 4) >> 1]);
-        const float p0 = __builtin_amdgcn_exp2f(s_cur[i >> 3][2 * (i & 7)] * c - mc);
-        const float p1 = __builtin_amdgcn_exp2f(s_cur[i >> 3][2 * (i & 7) + 1] * c - mc);
+        const float p0 = __builtin_amdgcn_exp2f(s_cur[i >> 3][2 * (i & 7)]);
+        const float p1 = __builtin_amdgcn_exp2f(s_cur[i >> 3][2 * (i & 7) + 1]);
         w[i >> 2][i & 3] = pack2_bf16(p0, p1);
         lsum = add_pair_bf16(lsum, w[i >> 2][i & 3]);
         __builtin_amdgcn_sched_barrier(0);
@@ -289,9 +314,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) pf[kb][hs] = __builtin_bit_cast(bf16x8, w[2 * kb + hs]);
     }
-    // region B: P(t) V(t) on the matrix core while the VALU finds the row max of S(t+1). Step i
-    // (16 per tile: 4 d-blocks x 2 key blocks x 2 halves) is one MFMA into o[i & 3], the two
-    // transpose reads of the V fragment two steps ahead, and the max over two scores.
+    // region B: P(t) V(t) on the matrix core while the VALU turns S(t+1) into x(t+1) and finds its row
+    // max. Step i (16 per tile: 4 d-blocks x 2 key blocks x 2 halves) is one MFMA into o[i & 3], the
+    // two transpose reads of the V fragment two steps ahead, and the fma and max of two scores.
     float mx_next;
     {
       const uint16_t* tV = vCur;
@@ -311,6 +336,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
       for (int i = 0; i < 16; ++i) {
         if (i + 2 < 16) vf[(i + 2) % 3] = vfrag(i + 2);
         o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pf[i >> 3][(i >> 2) & 1], o[i & 3], 0, 0, 0);
+        s_next[i >> 3][(2 * i) & 15] = s_next[i >> 3][(2 * i) & 15] * c - mc_run;
+        s_next[i >> 3][(2 * i + 1) & 15] = s_next[i >> 3][(2 * i + 1) & 15] * c - mc_run;
         mx = max3_f32(mx, s_next[i >> 3][(2 * i) & 15], s_next[i >> 3][(2 * i + 1) & 15]);
         asm volatile("" : "+v"(mx));   // no instruction: keeps the chain from being rebuilt as a tree after the loop
         __builtin_amdgcn_sched_barrier(0);
@@ -335,17 +362,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
     const int t = t_end - 1;
     const int k0 = t * BKV;
     lds_copy_barrier();              // V(t) has landed
-    if (k0 + BKV > S) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * fh + (e & 3);
-          if (key >= S) s_cur[kb][e] = -INFINITY;
-        }
+    if (k0 + BKV > S) {              // x of the keys past the sequence: -inf, and the max without them
+      mask_tail(s_cur, t);
       mx_cur = rowmax(s_cur);
     }
-    maybe_rescale(mx_cur);
+    maybe_shift(mx_cur, s_cur);
     bf16x8 pf[2][2];
     probs(s_cur, pf);
     pv_update(((t - t_begin) & 1) ? sV1 : sV0, pf);
@@ -353,7 +374,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
 
   const float l_tot = sum_xor32(l_run);
   if (part_slot >= 0) {
-    // one part of a split tile: the unnormalised output and the (max, sum) pair it is relative to
+    // one part of a split tile: the unnormalised output and the (max in the exp2 domain, sum) pair it
+    // is relative to
     const long qrow = (long)part_slot * BQ + wave * 32 + fr;
     float* po = sp.part_o + qrow * D;
 #pragma unroll
@@ -362,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
       for (int gg = 0; gg < 4; ++gg)
         *reinterpret_cast<float4*>(po + 32 * db + 8 * gg + 4 * fh) =
             make_float4(o[db][4 * gg], o[db][4 * gg + 1], o[db][4 * gg + 2], o[db][4 * gg + 3]);
-    if (fh == 0) *reinterpret_cast<float2*>(sp.part_ml + 2 * qrow) = make_float2(m_run, l_tot);
+    if (fh == 0) *reinterpret_cast<float2*>(sp.part_ml + 2 * qrow) = make_float2(mc_run, l_tot);
     return;
   }
   // ---- normalise and store: lane holds query my_q, d = 32 db + 8 g + 4 fh + [0, 4) ----
@@ -396,7 +418,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
 
 // Combines the parts of the split tiles: workgroup x covers 16 queries of split tile x / 8; thread
 // (query qi = tid / 16, dims [8 (tid % 16), +8)), so the 16 threads of a query read its 512-byte
-// partial rows contiguously. out = sum_p o_p 2^((m_p - m) c) / sum_p l_p 2^((m_p - m) c), m = max_p m_p.
+// partial rows contiguously. Each part stores its running max in the exp2 domain (mc_p = m_p c):
+// out = sum_p o_p 2^(mc_p - mc) / sum_p l_p 2^(mc_p - mc), mc = max_p mc_p.
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
   constexpr int QPW = 16;                                // queries per workgroup
   const int j = blockIdx.x / (BQ / QPW);
@@ -407,7 +430,6 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
   const int q0 = (idx - bh * nq) * BQ, h = bh % p.H, b = bh / p.H;
   const int q = q0 + qi;
   if (q >= p.S) return;
-  const float c = p.scale_log2;
   float m = -INFINITY;
   for (int pt = 0; pt < sp.parts; ++pt) m = fmaxf(m, sp.part_ml[2 * ((long)(j * sp.parts + pt) * BQ + qi)]);
   float acc[8];
@@ -417,7 +439,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs p, AttnSplit sp) {
   for (int pt = 0; pt < sp.parts; ++pt) {
     const long row = (long)(j * sp.parts + pt) * BQ + qi;
     const float2 ml = *reinterpret_cast<const float2*>(sp.part_ml + 2 * row);
-    const float f = __builtin_amdgcn_exp2f((ml.x - m) * c);
+    const float f = __builtin_amdgcn_exp2f(ml.x - m);
     l += ml.y * f;
     const float4* po = reinterpret_cast<const float4*>(sp.part_o + row * D + d0);
     const float4 v0 = po[0], v1 = po[1];
