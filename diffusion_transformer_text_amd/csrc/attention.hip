@@ -327,15 +327,16 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit
         const v4i16 hi = lds_read_tr16(vp + 8 * D);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8 vf[3];
-      vf[0] = vfrag(0);
-      vf[1] = vfrag(1);
+      constexpr int VA = 2;          // V fragments are read VA steps ahead of their MFMA
+      bf16x8 vf[VA + 1];
+#pragma unroll
+      for (int j = 0; j < VA; ++j) vf[j] = vfrag(j);
       float mx = -INFINITY;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (i + 2 < 16) vf[(i + 2) % 3] = vfrag(i + 2);
-        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pf[i >> 3][(i >> 2) & 1], o[i & 3], 0, 0, 0);
+        if (i + VA < 16) vf[(i + VA) % (VA + 1)] = vfrag(i + VA);
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % (VA + 1)], pf[i >> 3][(i >> 2) & 1], o[i & 3], 0, 0, 0);
         s_next[i >> 3][(2 * i) & 15] = s_next[i >> 3][(2 * i) & 15] * c - mc_run;
         s_next[i >> 3][(2 * i + 1) & 15] = s_next[i >> 3][(2 * i + 1) & 15] * c - mc_run;
         mx = max3_f32(mx, s_next[i >> 3][(2 * i) & 15], s_next[i >> 3][(2 * i + 1) & 15]);
