@@ -7,12 +7,14 @@
 // S x S score matrix never reaches HBM.
 //
 // One workgroup = 4 waves = 128 queries of one (sample, head); each wave owns 32 queries. Per
-// iteration a tile of 64 keys is staged in LDS (double-buffered): K as [key][d] and V transposed as
-// [d][key]. Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so that lane l
-// holds 32 scores of ONE query (l % 32): the row max and row sum are in-lane reductions plus one
-// exchange with lane l ^ 32. The output is also computed transposed, O^T = V^T P^T, which leaves the
-// lane's own query in its accumulator columns: the online-softmax rescale is a per-lane multiply and
-// P feeds the second MFMA straight from the score registers (no LDS round trip for P).
+// iteration a tile of 64 keys of K and of V is staged in LDS (double-buffered), both row-major
+// [key][d]; the V^T fragments come from gfx950's transpose LDS read. Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so that lane l holds 32 scores of ONE query (l % 32): the
+// row max and row sum are in-lane reductions plus one exchange with lane l ^ 32. The output is also
+// computed transposed, O^T = V^T P^T, which leaves the lane's own query in its accumulator columns:
+// the online-softmax rescale is a per-lane multiply and P feeds the second MFMA straight from
+// registers (no LDS round trip for P). Scores become exp2-domain offsets x = s c - m c as soon as they
+// exist, so the probabilities are exp2(x).
 #include <algorithm>
 
 #include "common.h"
