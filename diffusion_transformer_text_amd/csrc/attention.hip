@@ -60,7 +60,7 @@ __device__ __forceinline__ float add_pair_bf16(float acc, uint32_t w) {
 struct AttnSplit {
   int n_full, n_split, parts;
   float* part_o;     // [n_split * parts][BQ queries][128]
-  float* part_ml;    // [n_split * parts][BQ queries][2]: running max, sum
+  float* part_ml;    // [n_split * parts][BQ queries][2]: running max in the exp2 domain (m c), sum
 };
 
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs p, AttnSplit sp) {
