@@ -218,12 +218,6 @@ def main():
                     help="timed text-refiner calls per prompt length (256 and 4096 tokens; 0 = skip)")
     ap.add_argument("--fp8-steps", type=int, default=5,
                     help="steps timed with the FP8 tier (MXFP8 block projections, a second handle; 0 = skip)")
-    ap.add_argument("--one-stream", action="store_true",
-                    help="run every call's blocks on one stream (MOSS_DIT_ONE_STREAM=1): the kernels then never "
-                         "overlap, as in a kernel trace whose per-launch durations are compared with the "
-                         "event pass")
-    ap.add_argument("--stream-ab-steps", type=int, default=5,
-                    help="steps per pass of an alternating two-stream / one-stream timing (3 passes each; 0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="MiB of a plain device-to-device copy run once before the steps (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -235,8 +229,6 @@ def main():
             "path (CFG-parallel / Ulysses sharding is a design note only). Run it with --gpus 1.")
         sys.exit(2)
 
-    if args.one_stream:
-        os.environ["MOSS_DIT_ONE_STREAM"] = "1"
     import numpy as np
     import torch
     import diffusion_transformer_text_amd as dt
@@ -301,7 +293,6 @@ def main():
     clocks["timed_steps"] = clock.stop()
     clocks["idle_after_mhz"] = clock.read()
     ms_step = start.elapsed_time(end) / args.steps
-    streams = model.moss_dit_last_call_streams()
     fwd_per_s = 2.0 * 1000.0 / ms_step
     def flops_of_step(block_samples, rows, S_, N_):
         # blocks run per (sample, block) pair; patch embedding + final projection and the modulation
@@ -313,29 +304,7 @@ def main():
     mfma_frac = step_flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
     log(f"[bench] {ms_step:.2f} ms/step, {fwd_per_s:.2f} forwards/s, whole-step MFMA fraction {mfma_frac:.3f}")
 
-    # ---- the same steps with the blocks on two streams and on one, alternating passes ----
-    stream_ab = None
-    if args.stream_ab_steps > 0 and not args.one_stream:
-        times = {"two_streams": [], "one_stream": []}
-        for _ in range(3):
-            for name in ("two_streams", "one_stream"):
-                if name == "one_stream":
-                    os.environ["MOSS_DIT_ONE_STREAM"] = "1"
-                a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                a_ev.record()
-                for k in range(args.stream_ab_steps):
-                    step(k)
-                b_ev.record()
-                b_ev.synchronize()
-                os.environ.pop("MOSS_DIT_ONE_STREAM", None)
-                times[name].append(round(a_ev.elapsed_time(b_ev) / args.stream_ab_steps, 3))
-        stream_ab = {"ms_per_step": times, "steps_per_pass": args.stream_ab_steps,
-                     "median_ratio": round(float(np.median(times["one_stream"]) / np.median(times["two_streams"])), 4)}
-        log(f"[bench] two streams vs one: {json.dumps(stream_ab)}")
-
-    # ---- per-kernel-class event timing (separate pass over the same steps; per-class profiling keeps
-    # every call on one stream, so each launch runs alone) ----
+    # ---- per-kernel-class event timing (separate pass over the same steps) ----
     model.moss_dit_profile_enable(True)
     for k in range(args.profile_steps):
         step(k)
@@ -576,8 +545,6 @@ def main():
                    "global_batch": 2, "seq_len": S, "parallelism": "none (1 GPU)"},
         "s_per_image": round(s_image, 3) if s_image else None,
         "image_steps": args.image_steps,
-        "streams": streams,
-        "stream_ab": stream_ab,
         "mfma_fraction_step": round(mfma_frac, 4),
         "step_tflop": round(step_flops / 1e12, 2),
         "roofline": roof,

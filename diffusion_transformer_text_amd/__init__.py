@@ -105,7 +105,6 @@ _sig("moss_dit_modulation", C.c_int, _P, C.POINTER(C.c_float), C.c_int32, _P, _P
 _sig("moss_dit_block", C.c_int, _P, C.c_int32, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64,
      C.POINTER(moss_block_taps), _P)
 _sig("moss_step_cache_stats", C.c_int, _P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_float))
-_sig("moss_dit_last_call_streams", C.c_int, _P)
 _sig("moss_text_refine", C.c_int, _P, C.c_int32, C.c_int32, _P, _P, _P)
 _sig("moss_attention", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P)
 _sig("moss_attention_noalloc", C.c_int, _P, _P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P)
@@ -125,7 +124,7 @@ EXPORTED = ["moss_dit_abi_version", "moss_status_string", "moss_dit_last_error",
             "moss_dit_weights_init", "moss_dit_create", "moss_dit_destroy", "moss_forward_args_init",
             "moss_dit_forward", "moss_validate_forward_args", "moss_sigmas", "moss_step_args_init",
             "moss_sample_step", "moss_validate_step_args", "moss_cfg_euler", "moss_guidance_euler",
-            "moss_text_refine", "moss_step_cache_stats", "moss_dit_last_call_streams", "moss_dit_modulation",
+            "moss_text_refine", "moss_step_cache_stats", "moss_dit_modulation",
             "moss_block_taps_init", "moss_dit_block", "moss_attention", "moss_attention_noalloc", "moss_gemm_bf16",
             "moss_mx_quantize", "moss_gemm_mxfp8", "moss_attention_q8_workspace", "moss_attention_q8",
             "moss_dit_profile_enable", "moss_dit_profile_read"]
@@ -441,10 +440,6 @@ class MossDiT:
         f, r, c = C.c_int32(), C.c_int32(), C.c_float()
         _check(_lib.moss_step_cache_stats(self.handle, C.byref(f), C.byref(r), C.byref(c)), self.handle)
         return f.value, r.value, c.value
-
-    def moss_dit_last_call_streams(self) -> int:
-        """Streams the blocks of the last forward / sampling step ran on (2: the two-stream forward)."""
-        return int(_lib.moss_dit_last_call_streams(self.handle))
 
     def moss_text_refine(self, enc, out, stream=None):
         """enc: fp32 [batch, text_len, text_dim] on the GPU -> out: fp32 [batch, text_len, hidden]."""

@@ -12,7 +12,6 @@
 // user-facing validation messages) follow the C API rules of the MossInfer integration guide.
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -110,10 +109,6 @@ struct moss_dit {
     float last_change = NAN;
   } fbc;
   float* rope = nullptr;   // [2][256][32]
-  // the two-stream forward's second stream and its fork / join events (created on first use)
-  hipStream_t lane = nullptr;
-  hipEvent_t lane_fork = nullptr, lane_join = nullptr;
-  int last_streams = 0;    // streams the last forward's blocks ran on
   void* ws = nullptr;
   size_t ws_bytes = 0;
   // per-class event timing (moss_dit_profile_enable)
@@ -207,7 +202,6 @@ struct Carve {
   size_t attn8_bytes;
   void* attn_split;   // exact attention: partial results of the key-split tail tiles
   size_t attn_split_bytes;
-  void* attn_split2;  // the same for the second stream of a two-stream forward (B >= 2)
 };
 
 // Pointers of the regions of the workspace layout (host_plan.cpp: ws_layout) at `base`; returns its
@@ -233,7 +227,6 @@ size_t carve(const moss_dit* H, int B, int S, int N, int lat_elems, char* base, 
     t.lds8 = L.lds8;
     t.attn_split = at(L.attn_split);
     t.attn_split_bytes = t.attn_split ? L.attn_split_bytes : 0;
-    t.attn_split2 = at(L.attn_split2);
     t.attn8 = at(L.attn8);
     t.attn8_bytes = t.attn8 ? L.attn8_bytes : 0;
     *c = t;
@@ -355,12 +348,8 @@ hipError_t project(const moss_dit* H, const Carve& c, GemmArgs g, const moss_dit
 
 // One joint block on nb samples of S rows each (x [nb * S, D], in place). m: the block's six modulation
 // vectors of the first sample ([6 * D]); sample b's are at m + b * mod_stride (stride 0: all share).
-// batch, first (batch 0: nb, 0): the nb samples are samples [first, first + nb) of a batch of `batch`
-// consecutive samples whose block would otherwise run as one launch each; the attention then splits its
-// tiles as that batch launch does, so the rows come out bit for bit the same.
 int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, int S, const uint16_t* m,
-              long mod_stride, const Carve& c, const moss_block_taps* taps, hipStream_t st, int batch = 0,
-              int first = 0) {
+              long mod_stride, const Carve& c, const moss_block_taps* taps, hipStream_t st) {
   const moss_dit_config& k = H->cfg;
   const int D = k.hidden, F = k.ffn_hidden, M = nb * S;
   auto tap_copy = [&](void* dst, const void* src, size_t bytes) -> hipError_t {
@@ -418,7 +407,7 @@ int run_block(moss_dit* H, const BlockW& w, uint16_t* x, int nb, int T, int gw, 
     if (H->q8attn())
       HIP_TRY(H, launch_attention_q8(at, c.attn8, c.attn8_bytes, st));
     else
-      HIP_TRY(H, launch_attention_share(at, batch ? batch : nb, first, st, c.attn_split, c.attn_split_bytes));
+      HIP_TRY(H, launch_attention(at, st, c.attn_split, c.attn_split_bytes));
   }
   HIP_TRY(H, tap_copy(taps ? taps->o : nullptr, c.o, (size_t)M * D * 2));
   // A7: out projection + gated residual
@@ -522,15 +511,6 @@ struct FbcCall {
   float threshold;
 };
 
-// The second stream (non-blocking, so it never waits on the null stream implicitly) and its events,
-// created on the handle's device on first use.
-int ensure_lane(moss_dit* H) {
-  if (!H->lane) HIP_TRY(H, hipStreamCreateWithFlags(&H->lane, hipStreamNonBlocking));
-  if (!H->lane_fork) HIP_TRY(H, hipEventCreateWithFlags(&H->lane_fork, hipEventDisableTiming));
-  if (!H->lane_join) HIP_TRY(H, hipEventCreateWithFlags(&H->lane_join, hipEventDisableTiming));
-  return MOSS_OK;
-}
-
 int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st, const FbcCall* fbc = nullptr) {
   const moss_dit_config& k = H->cfg;
   const int D = k.hidden, L = k.num_layers, P = k.latent_channels * 4;
@@ -597,52 +577,8 @@ int run_forward(moss_dit* H, const FwdPlan& p, const Carve& c, hipStream_t st, c
       first = 1;
     }
   }
-  // Two streams: samples [0, hs) run their blocks on st, [hs, B) on the handle's second stream, each
-  // stream with its own rows of the scratch buffers (a, qkv, o, h) and its own attention partials, so one
-  // stream's kernels can fill the compute units the other's last round of tiles leaves idle. Each run of
-  // consecutive samples that the one-stream order launches together is cut at hs; a kernel computes a
-  // row the same whatever rows are launched beside it, and the attention pieces take their share of the
-  // whole run's key split, so the residual stream is bit for bit the one-stream result.
-  const bool lanes = first < L && B >= 2 && !H->fp8() && !H->q8attn() && !p.dump && !H->prof_on &&
-                     !env_flag("MOSS_DIT_ONE_STREAM");
-  H->last_streams = lanes ? 2 : 1;
-  if (lanes) {
-    if ((s = ensure_lane(H))) return s;
-    const int hs = lane_split(B), F = k.ffn_hidden;
-    HIP_TRY(H, hipEventRecord(H->lane_fork, st));
-    HIP_TRY(H, hipStreamWaitEvent(H->lane, H->lane_fork, 0));
-    for (int l = first; l < L; ++l)
-      for (int lane = 0; lane < 2; ++lane) {
-        const int lb = lane ? hs : 0, le = lane ? B : hs;
-        hipStream_t ls = lane ? H->lane : st;
-        Carve cl = c;
-        cl.a += (size_t)lb * S * D;
-        cl.qkv += (size_t)lb * S * 3 * D;
-        cl.o += (size_t)lb * S * D;
-        cl.h += (size_t)lb * S * F;
-        if (lane) cl.attn_split = c.attn_split2;
-        int b = 0;
-        while (b < B) {
-          if ((p.skip[b] >> l) & 1ULL) {
-            ++b;
-            continue;
-          }
-          int e = b;
-          while (e < B && !((p.skip[e] >> l) & 1ULL)) ++e;
-          const int sb = std::max(b, lb), se = std::min(e, le);
-          if (sb < se &&
-              (s = run_block(H, dit_block(H, l), c.x + (size_t)sb * S * D, se - sb, p.T, gw, S,
-                             c.mod + (size_t)sb * mstride + (size_t)l * 6 * D, mstride, cl, nullptr, ls, e - b, sb - b)))
-            return s;
-          b = e;
-        }
-      }
-    HIP_TRY(H, hipEventRecord(H->lane_join, H->lane));
-    HIP_TRY(H, hipStreamWaitEvent(st, H->lane_join, 0));
-  } else {
-    for (int l = first; l < L; ++l)
-      if ((s = run_layer(l))) return s;
-  }
+  for (int l = first; l < L; ++l)
+    if ((s = run_layer(l))) return s;
   if (fbc) {
     if (reused) {
       ++f.reused;
@@ -900,9 +836,6 @@ void moss_dit_destroy(moss_dit* h) {
       (void)hipEventDestroy(e.first);
       (void)hipEventDestroy(e.second);
     }
-  if (h->lane_fork) (void)hipEventDestroy(h->lane_fork);
-  if (h->lane_join) (void)hipEventDestroy(h->lane_join);
-  if (h->lane) (void)hipStreamDestroy(h->lane);
   if (prev >= 0) (void)hipSetDevice(prev);
   delete h;
 }
@@ -992,8 +925,6 @@ int moss_step_cache_stats(const moss_dit* h, int32_t* full_calls, int32_t* reuse
   if (last_change) *last_change = h->fbc.last_change;
   return MOSS_OK;
 }
-
-int moss_dit_last_call_streams(const moss_dit* h) { return h ? h->last_streams : 0; }
 
 int moss_text_refine(moss_dit* h, int32_t batch, int32_t text_len, const float* enc, float* out, void* stream) {
   int s = enter(h);

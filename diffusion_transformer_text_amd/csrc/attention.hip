@@ -530,30 +530,20 @@ size_t attention_split_workspace(int B, int S, int H) {
   return attention_split_bytes(B, S, H, 2L * device_cu_count());
 }
 
-hipError_t launch_attention_share(const AttnArgs& a, int batch, int first, hipStream_t stream, void* ws,
-                                  size_t ws_bytes) {
+hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, void* ws, size_t ws_bytes) {
   if (a.S <= 0 || a.B <= 0) return hipSuccess;
-  if (first < 0 || first + a.B > batch) return hipErrorInvalidValue;
   if (a.ld_qkv % 8 != 0 || a.ld_out % 4 != 0) return hipErrorInvalidValue;
   if (a.q8 && (!a.s8 || (a.H * D) % 256 != 0 || a.lds8 < (long)a.B * a.S)) return hipErrorInvalidValue;
-  const long tiles = (long)((a.S + BQ - 1) / BQ) * a.H;   // query tiles x heads of one sample
-  if (tiles * batch > 0x7fffffffL) return hipErrorInvalidValue;
+  const long wgs = (long)((a.S + BQ - 1) / BQ) * a.H * a.B;
+  if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
   if (2L * a.S * a.ld_qkv > 0x7fffffffL) return hipErrorInvalidValue;   // 32-bit buffer offsets per sample
-  // the batch launch's split (whole tiles only when the workspace cannot hold its partials), then the
-  // part of it that falls in this launch's samples
-  AttnSplitPlan pl = attention_split_plan(batch, a.S, a.H, 2L * device_cu_count());
-  if ((size_t)pl.n_split * pl.parts == 0 || !ws || ws_bytes < attention_split_workspace(batch, a.S, a.H)) {
-    pl.n_full = (int)(tiles * batch);
-    pl.n_split = 0;
-    pl.parts = 1;
-  }
-  const AttnSplitPlan sh = attention_share_plan(pl, tiles, first, a.B);
-  AttnSplit sp{};
-  sp.n_full = sh.n_full;
-  sp.n_split = sh.n_split;
-  sp.parts = sh.parts;
+  AttnSplit sp = split_plan(a.B, a.S, a.H);
   const size_t rows = (size_t)sp.n_split * sp.parts * BQ;
-  if (rows > 0) {
+  if (rows == 0 || !ws || ws_bytes < attention_split_workspace(a.B, a.S, a.H)) {
+    sp.n_full = (int)wgs;                    // no workspace (or nothing to split): whole tiles only
+    sp.n_split = 0;
+    sp.parts = 1;
+  } else {
     char* base = static_cast<char*>(ws);
     base += (256 - (reinterpret_cast<uintptr_t>(base) & 255)) & 255;
     sp.part_o = reinterpret_cast<float*>(base);
@@ -564,10 +554,6 @@ hipError_t launch_attention_share(const AttnArgs& a, int batch, int first, hipSt
   if (sp.n_split > 0)
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)sp.n_split * (BQ / 16)), dim3(256), 0, stream, a, sp);
   return hipGetLastError();
-}
-
-hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, void* ws, size_t ws_bytes) {
-  return launch_attention_share(a, a.B, 0, stream, ws, ws_bytes);
 }
 
 hipError_t launch_rope_inplace(uint16_t* qkv, int B, int S, int T, int grid_w, int H, long ld,

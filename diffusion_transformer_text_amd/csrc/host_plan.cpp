@@ -278,17 +278,6 @@ AttnSplitPlan attention_split_plan(int B, int S, int H, long slots) {
   return sp;
 }
 
-AttnSplitPlan attention_share_plan(const AttnSplitPlan& batch, long tiles_per_sample, int first, int count) {
-  AttnSplitPlan sp{};
-  const long lo = (long)first * tiles_per_sample, hi = (long)(first + count) * tiles_per_sample;
-  long n_split = 0;
-  if (batch.n_split > 0) n_split = std::max(0L, hi - std::max((long)batch.n_full, lo));
-  sp.n_full = (int)(hi - lo - n_split);
-  sp.n_split = (int)n_split;
-  sp.parts = n_split > 0 ? batch.parts : 1;
-  return sp;
-}
-
 size_t attention_split_bytes(int B, int S, int H, long slots) {
   const AttnSplitPlan sp = attention_split_plan(B, S, H, slots);
   const size_t rows = (size_t)sp.n_split * sp.parts * kAttnBQ;
@@ -333,7 +322,6 @@ WsLayout ws_layout(const moss_dit_config& k, int B, int S, int N, long lat_elems
   }
   t.attn_split_bytes = attention_split_bytes(B, S, k.num_heads, attn_slots);
   t.attn_split = t.attn_split_bytes ? take(t.attn_split_bytes) : kNoRegion;
-  t.attn_split2 = (t.attn_split_bytes && B >= 2) ? take(t.attn_split_bytes) : kNoRegion;
   t.attn8_bytes = 0;
   t.attn8 = kNoRegion;
   if (k.attention_mode == 1) {

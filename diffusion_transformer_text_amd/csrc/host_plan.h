@@ -61,15 +61,6 @@ struct AttnSplitPlan {
   int n_full, n_split, parts;
 };
 AttnSplitPlan attention_split_plan(int B, int S, int H, long slots);
-// The share of a batch launch's split that falls in its samples [first, first + count), as the plan of
-// a launch over those samples alone: tiles are ordered sample-major, so the split tiles are a suffix of
-// the batch launch, and the share splits exactly the tiles of that suffix in its range, into the same
-// parts. tiles_per_sample = query tiles x heads. A launch with the share plan computes every tile as the
-// batch launch does, so its output rows equal the batch launch's bit for bit.
-AttnSplitPlan attention_share_plan(const AttnSplitPlan& batch, long tiles_per_sample, int first, int count);
-// The two streams of a forward over B >= 2 samples: samples [0, lane_split(B)) on the first,
-// [lane_split(B), B) on the second.
-inline int lane_split(int B) { return (B + 1) / 2; }
 // bytes of the partial results of that split (0 = nothing is split)
 size_t attention_split_bytes(int B, int S, int H, long slots);
 // bytes of the 8-bit attention's workspace (quantized q, k, v^T and their scales)
@@ -80,7 +71,6 @@ struct WsLayout {
   size_t x, a, qkv, o, h, tokens, mod, u, vel;   // bf16 activations; fp32 u, vel
   size_t q8, s8, q8h, s8h;                        // FP8 tier (SIZE_MAX when absent)
   size_t attn_split, attn8;                       // exact attention split / 8-bit attention (SIZE_MAX when absent)
-  size_t attn_split2;                             // the split partials of the second stream (B >= 2)
   size_t attn_split_bytes, attn8_bytes;
   long lds8;                                      // scale-word row stride of the FP8 tier
   size_t total;                                   // bytes of the whole workspace

@@ -103,13 +103,6 @@ struct AttnArgs {
 // run side by side, and a merge kernel combines the parts (no ws: no split).
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream, void* ws = nullptr, size_t ws_bytes = 0);
 size_t attention_split_workspace(int B, int S, int H);
-// The same attention where a's a.B samples are samples [first, first + a.B) of a batch launch over
-// `batch` samples (same S and H): the launch takes the part of that launch's key split that falls in its
-// samples, so its output rows equal the batch launch's bit for bit (two streams, each on some of the
-// samples, reproduce the one-launch result). ws: this launch's own partials region, of
-// attention_split_workspace(batch, S, H) bytes to split as the batch launch does.
-hipError_t launch_attention_share(const AttnArgs& a, int batch, int first, hipStream_t stream, void* ws,
-                                  size_t ws_bytes);
 
 // 8-bit attention (the FP8 tier's attention): qkv as above (q and k already rotated). The workspace
 // (attention_q8_workspace bytes, 256-byte aligned) receives the INT8 Q and K, the FP8 V^T and their

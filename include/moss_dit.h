@@ -21,12 +21,6 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Compute calls validate all
  *     arguments on the host first (no device work on error), then enqueue on the stream and return;
  *     device-side faults surface at the caller's next synchronisation.
- *   - A forward over two or more samples (moss_dit_forward without residual_dump, moss_sample_step)
- *     in the bf16 tier with exact attention runs its blocks on two streams: the first half of the
- *     samples on `stream`, the rest on a non-blocking stream the handle owns (created on first use),
- *     forked from `stream` and joined back into it with events, so the call is still ordered on
- *     `stream` as above. The result is bit for bit that of one stream. MOSS_DIT_ONE_STREAM=1 in the
- *     environment (read per call) keeps the whole call on `stream`, as does per-class profiling.
  *   - Every function returns a moss_status. After MOSS_ERR_DEVICE the handle is dead: every later
  *     call on it returns MOSS_ERR_DEVICE; destroy it.
  *   - One call at a time per handle. Different handles may be used from different threads.
@@ -225,9 +219,6 @@ int moss_sample_step(moss_dit* h, const moss_step_args* a, void* stream);
  * calls that reused blocks 1.., and the last measured change (NaN before the first comparison).
  * Host only; any output pointer may be NULL. */
 int moss_step_cache_stats(const moss_dit* h, int32_t* full_calls, int32_t* reused_calls, float* last_change);
-/* Streams the blocks of the handle's last moss_dit_forward / moss_sample_step ran on: 2 for the
- * two-stream forward (see the conventions above), 1 otherwise, 0 before the first such call. Host only. */
-int moss_dit_last_call_streams(const moss_dit* h);
 /* Host-only check of step arguments (no GPU needed). msg (may be NULL) receives the reason. */
 int moss_validate_step_args(const moss_dit_config* cfg, const moss_step_args* a, char* msg, int32_t msg_len);
 

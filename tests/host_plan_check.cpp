@@ -13,7 +13,6 @@
 // Prints "ok <cases>" and exits 0, or prints the failures and exits 1.
 #include <cstdio>
 #include <cstdlib>
-#include <algorithm>
 #include <cstring>
 #include <random>
 #include <string>
@@ -35,11 +34,6 @@ static long g_fail = 0, g_cases = 0;
       }                                                         \
     }                                                           \
   } while (0)
-
-static uint64_t rng_sample() {
-  static std::mt19937_64 r(777);
-  return r();
-}
 
 struct Region {
   const char* name;
@@ -77,48 +71,6 @@ static void check_layout(const moss_dit_config& k, int B, int S, int N, long lat
         "split plan loses query tiles (B %d S %d)", B, S);
   CHECK(sp.n_split == 0 || (sp.parts >= 2 && (long)sp.n_split * sp.parts <= slots), "split plan oversubscribes");
   if (split_rows) r.push_back({"attention split partials", L.attn_split, split_rows * (kHeadDim + 2) * 4});
-  if (split_rows && B >= 2)
-    r.push_back({"attention split partials, second stream", L.attn_split2, split_rows * (kHeadDim + 2) * 4});
-  // Two-stream forward: every run of consecutive samples [gb, ge) that one batch launch would cover is
-  // cut at the lane boundary; each piece's launch takes its share of the batch launch's split. Check,
-  // tile by tile at the boundaries and at sampled tiles, that a tile is split in the piece exactly when
-  // it is split in the batch launch, with the same parts, and that the piece's partials fit its stream's
-  // region whenever the batch launch itself would split (the launch falls back to whole tiles otherwise).
-  if (B >= 2) {
-    const long tps = (long)((S + kAttnBQ - 1) / kAttnBQ) * k.num_heads;
-    const int ls = lane_split(B);
-    for (int gb = 0; gb < B; ++gb)
-      for (int ge = gb + 1; ge <= B; ++ge) {
-        const int nb = ge - gb;
-        const AttnSplitPlan g = attention_split_plan(nb, S, k.num_heads, slots);
-        const size_t g_bytes = attention_split_bytes(nb, S, k.num_heads, slots);
-        long split_sum = 0;
-        const int cuts[2][2] = {{gb, std::min(ge, ls)}, {std::max(gb, ls), ge}};
-        for (const auto& cut : cuts) {
-          if (cut[0] >= cut[1]) continue;
-          const int f = cut[0] - gb, cnt = cut[1] - cut[0];
-          const AttnSplitPlan sh = attention_share_plan(g, tps, f, cnt);
-          split_sum += sh.n_split;
-          CHECK((long)sh.n_full + sh.n_split == cnt * tps, "share loses tiles (nb %d f %d cnt %d)", nb, f, cnt);
-          CHECK(sh.n_split == 0 || sh.parts == g.parts, "share parts %d vs %d", sh.parts, g.parts);
-          const long lo = (long)f * tps, hi = lo + cnt * tps;
-          const long probe[] = {lo, lo + 1, hi - 1, hi - 2, g.n_full - 1L, (long)g.n_full, g.n_full + 1L,
-                                lo + (long)(rng_sample() % (uint64_t)(hi - lo)), lo + (long)(rng_sample() % (uint64_t)(hi - lo))};
-          for (long t : probe) {
-            if (t < lo || t >= hi) continue;
-            const bool in_batch = g.n_split > 0 && t >= g.n_full;
-            const bool in_share = sh.n_split > 0 && t - lo >= sh.n_full;
-            CHECK(in_batch == in_share, "tile %ld split %d in the batch launch, %d in the share (nb %d f %d cnt %d)", t,
-                  (int)in_batch, (int)in_share, nb, f, cnt);
-          }
-          if (g_bytes && g_bytes <= L.attn_split_bytes)
-            CHECK((size_t)sh.n_split * sh.parts * kAttnBQ * (kHeadDim + 2) * 4 <= L.attn_split_bytes,
-                  "share partials exceed the stream's region (nb %d f %d cnt %d)", nb, f, cnt);
-        }
-        CHECK(split_sum == g.n_split, "shares split %ld tiles, the batch launch %d (gb %d ge %d)", split_sum, g.n_split,
-              gb, ge);
-      }
-  }
   if (k.attention_mode == 1) {
     const size_t nblk = (S + 63) / 64, H = k.num_heads;
     // q and k codes, V^T codes, per-token q scale, per-block k scale, per-channel v scale, block maxima

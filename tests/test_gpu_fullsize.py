@@ -142,15 +142,11 @@ def test_full_forward_1024_block_chain(mod_scale):
     vel = torch.empty_like(lat)
     dump = torch.empty((L + 1, 2, S, D), dtype=torch.bfloat16, device="cuda")
     model.moss_dit_forward(lat, text, [0.5, 0.5], vel, skip_mask=[0, 1 << 22], residual_dump=dump)
-    assert model.moss_dit_last_call_streams() == 1
     torch.cuda.synchronize()
     assert torch.isfinite(vel).all().item()
-    # run-to-run determinism at full size, and the residual dump does not change the result. The call
-    # with the dump runs on one stream; the one without runs sample 1 on a second stream, whose attention
-    # takes the one-launch key split of its 96 leftover query tiles (5 parts): bit for bit the same
+    # run-to-run determinism at full size, and the residual dump does not change the result
     vel2 = torch.full_like(lat, float("nan"))
     model.moss_dit_forward(lat, text, [0.5, 0.5], vel2, skip_mask=[0, 1 << 22])
-    assert model.moss_dit_last_call_streams() == 2
     torch.cuda.synchronize()
     assert torch.equal(vel, vel2)
     # the skipped block leaves the unconditional row bit for bit unchanged

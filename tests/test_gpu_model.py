@@ -391,69 +391,3 @@ def test_residual_dump_and_skip_rows():
     # the embedding rows: text cast and patch embedding
     x0 = O.embed(inp.latents[0].astype(np.float64), inp.text_cond[0].astype(np.float64), W, ocfg, mirror=True)
     assert rel_l2(O.from_bf16_bits(d[0, 0]), x0) <= 1e-2
-
-
-# (batch, text tokens, latent side, per-sample skip masks): the batch of 8 at S = 7 + 4096 = 4103 has
-# 8 x 33 x 2 = 528 query tiles, so its one-launch attention splits the last 16 along the keys (8 parts),
-# all in the second stream's samples, and the second stream's rows start at 4 x 4103 (no 256-row tile
-# boundary); the skip masks cut the runs of samples that one launch covers at other places per block
-TWO_STREAM_CASES = [(8, 7, 128, None), (8, 7, 128, [0, 0, 2, 0, 0, 1, 0, 0]), (3, 32, 16, [0, 2, 0]),
-                    (5, 1, 2, [1, 0, 3, 0, 2]), (2, 32, 16, [0, 2])]
-
-
-@pytest.mark.parametrize("B,T,side,skips", TWO_STREAM_CASES)
-def test_two_stream_forward_bitwise(B, T, side, skips, monkeypatch):
-    """A forward over two or more samples runs half of them on a second stream; the velocity equals the
-    one-stream forward's bit for bit (every kernel computes a row the same whatever rows run beside it,
-    and the attention pieces take their share of the one-launch key split)."""
-    m, w, inp, W, ocfg, _ = model(50.0)
-    D = ocfg.hidden
-    log(f"two-stream forward B={B} T={T} latent {side}x{side} skips={skips}")
-    g = torch.Generator(device="cuda")
-    g.manual_seed(1000 * B + T)
-    lat = torch.randn((B, 32, side, side), generator=g, device="cuda", dtype=torch.float32)
-    text = torch.randn((B, T, D), generator=g, device="cuda", dtype=torch.float32)
-    sig = [0.1 + 0.8 * b / (B - 1) for b in range(B)]
-    v2 = torch.full_like(lat, float("nan"))
-    v1 = torch.full_like(lat, float("nan"))
-    monkeypatch.delenv("MOSS_DIT_ONE_STREAM", raising=False)
-    m.moss_dit_forward(lat, text, sig, v2, skip_mask=skips)
-    assert m.moss_dit_last_call_streams() == 2
-    monkeypatch.setenv("MOSS_DIT_ONE_STREAM", "1")
-    m.moss_dit_forward(lat, text, sig, v1, skip_mask=skips)
-    assert m.moss_dit_last_call_streams() == 1
-    torch.cuda.synchronize()
-    assert torch.isfinite(v1).all().item()
-    assert torch.equal(v1, v2)
-    # the samples differ from one another (the streams did not write each other's rows)
-    assert not torch.equal(v1[0], v1[B - 1])
-
-
-def test_two_stream_sampling_with_step_cache_bitwise(monkeypatch):
-    """Three CFG steps with the step cache (threshold high enough that every comparable call reuses
-    blocks 1..), then three steps without it: two streams and one stream give the same latents bit for
-    bit. Step 0 (sigma 1) lies outside the skip window, so step 1's rows differ from it and run in full;
-    step 2 reuses."""
-    m, w, inp, W, ocfg, _ = model(50.0)
-    sig = dt.moss_sigmas(3, 5.0)
-
-    def run(cache):
-        x = torch.from_numpy(inp.latents.copy()).cuda()
-        tc = torch.from_numpy(inp.text_cond).cuda()
-        tu = torch.from_numpy(inp.text_uncond).cuda()
-        for s in range(3):
-            m.moss_sample_step(x, tc, tu, sig, s, cfg_scale=3.0, uncond_skip_layers=[1], step_cache=cache,
-                               step_cache_threshold=10.0)
-        torch.cuda.synchronize()
-        return x.cpu().numpy(), m.moss_step_cache_stats()[:2]
-
-    for cache in (True, False):
-        monkeypatch.delenv("MOSS_DIT_ONE_STREAM", raising=False)
-        x2, st2 = run(cache)
-        monkeypatch.setenv("MOSS_DIT_ONE_STREAM", "1")
-        x1, st1 = run(cache)
-        log(f"step cache {cache}: stats {st2} / {st1}")
-        assert st1 == st2
-        if cache:
-            assert st2 == (2, 1)
-        np.testing.assert_array_equal(x1, x2)
