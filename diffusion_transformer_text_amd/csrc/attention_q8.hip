@@ -285,6 +285,10 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
     for (int i = 0; i < D / 32; ++i) o[i][e] = 0.f;
   }
   float m_run = -INFINITY;
+  constexpr int kBiasI = 0x4B400000;          // the float 1.5 * 2^23
+  constexpr float kBiasF = 12582912.0f;
+  const v16i bias = {kBiasI, kBiasI, kBiasI, kBiasI, kBiasI, kBiasI, kBiasI, kBiasI,
+                     kBiasI, kBiasI, kBiasI, kBiasI, kBiasI, kBiasI, kBiasI, kBiasI};
   const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                     0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
 
@@ -294,31 +298,33 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
     const uint8_t* tK = st;
     const uint8_t* tV = st + KB * D;
     // S^T = K Q^T on INT8 codes: 2 key blocks x 4 dim slices of 32
+    // The accumulators start at kBiasI (the first MFMA of each chain reads the constant registers
+    // `bias` as its C operand), so each ends as kBiasI + s for the integer score s; |s| <= 127^2 128 <
+    // 2^22 keeps that in the binade [2^23, 2^24), where its bit pattern read as a float is exactly
+    // 1.5 * 2^23 + s: no int-to-float conversion per score.
     v16i si[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) si[kb][e] = 0;
-#pragma unroll
       for (int ds = 0; ds < D / 32; ++ds) {
         const v4i kf = *reinterpret_cast<const v4i*>(tK + k_swz(32 * kb + fr, 2 * ds + fh));
-        si[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[ds], si[kb], 0, 0, 0);
+        si[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[ds], ds == 0 ? bias : si[kb], 0, 0, 0);
       }
     }
-    // scores in the exp2 domain are si * f (f >= 0, so the largest code gives the largest score); keys
-    // past the sequence are masked
+    // scores in the exp2 domain are s * f (f >= 0, so the largest code gives the largest score); keys
+    // past the sequence are masked (the biased scores are positive, so 0 stands below every key)
     const float f = qscale * s_ka[min(t, ntiles - 1)] * (1.0f / 127.f);
     const int k0 = t * KB;
-    int mi = INT_MIN;
+    int mi = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const bool dead = MASK && k0 + 32 * kb + 8 * (e >> 2) + 4 * fh + (e & 3) >= S;
-        mi = max(mi, dead ? INT_MIN : si[kb][e]);
+        mi = max(mi, dead ? 0 : si[kb][e]);
       }
     mi = max_xor32(mi);
-    const float mx = (float)mi * f;   // a wholly masked tile never moves the reference (tile 0 has a key)
+    const float mx = (float)(mi - kBiasI) * f;   // a wholly masked tile never moves the reference (tile 0 has a key)
     // lazy reference max: a query's reference moves to the tile's max only when that is more than one
     // log2 unit above it, so every probability stays <= 2; a move rescales that query's sums
     const bool move = mx - m_run > 1.0f;
@@ -334,7 +340,11 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
     }
     // P <= 2 as E4M3 codes of 224 p = exp2(s - m_run + log2 224) <= 448: byte b of the operand = key
     // 32 (b >> 4) + 8 ((b & 15) >> 2) + 4 fh + (b & 3)
+    // exp2 argument s f - m_b = (1.5 * 2^23 + s) f + c0 with c0 = -(1.5 * 2^23 f + m_b) rounded once per
+    // tile: one fma per score, off the exact argument by at most half an ulp of c0 (<= 0.75 f + 2^-24
+    // |m_b| log2 units; f is about 1e-4 for unit-variance q and k, 2e-3 for scores spread over +-60)
     const float m_b = m_run - kLog2PScale;
+    const float c0 = __builtin_fmaf(-kBiasF, f, -m_b);
     v8i pf;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
       float a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = __builtin_fmaf((float)si[kb][e0 + i], f, -m_b);
+        a[i] = __builtin_fmaf(__int_as_float(si[kb][e0 + i]), f, c0);
         if (MASK && k0 + 32 * kb + 8 * (e0 >> 2) + 4 * fh + i >= S) a[i] = -INFINITY;
       }
       // bytes 2-3 of the first conversion's third operand are overwritten by the second: the first
