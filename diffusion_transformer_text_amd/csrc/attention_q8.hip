@@ -299,9 +299,9 @@ __global__ __launch_bounds__(256, 2) void attention_q8_kernel(AttnQ8Args p) {
     const uint8_t* tV = st + KB * D;
     // S^T = K Q^T on INT8 codes: 2 key blocks x 4 dim slices of 32
     // The accumulators start at kBiasI (the first MFMA of each chain reads the constant registers
-    // `bias` as its C operand), so each ends as kBiasI + s for the integer score s; |s| <= 127^2 128 <
-    // 2^22 keeps that in the binade [2^23, 2^24), where its bit pattern read as a float is exactly
-    // 1.5 * 2^23 + s: no int-to-float conversion per score.
+    // `bias` as its C operand), so each ends as kBiasI + s for the integer score s; |s| <= 128^2 128 =
+    // 2^21 for any INT8 codes keeps that in the binade [2^23, 2^24), where its bit pattern read as a
+    // float is exactly 1.5 * 2^23 + s: no int-to-float conversion per score.
     v16i si[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
