@@ -8,6 +8,8 @@
   from the benchmark's seeded draw: the residual stream is dumped after every block and blocks
   0, 21, 22 and 41 are recomputed by the oracle on sampled rows from the GPU's input to that block;
   the embedding and the final layer + unpatchify are checked in full.
+* The largest batch (8 samples at 1024^2, each with its own sigma, prompt and skip set) equals eight
+  one-sample forwards bit for bit.
 * Whole sampling steps at the benchmark's shapes (the three-pass skip-layer guidance step at 1024^2,
   three rows; a step at 2048^2 with a 4096-token prompt): the step equals the guidance combine of the
   library's own batched forward (rows are computed independently, so the step's rows and the
@@ -192,6 +194,41 @@ def test_full_forward_1024_block_chain(mod_scale):
     if mod_scale != 1.0:       # literal init: the update is mostly bf16 rounding (see forward_block_chain)
         assert max(chain["update"]) <= REL_L2_BF16, chain["update"]
     assert max(mism["gated_res"]) <= 1e-3, mism
+
+
+@pytest.mark.timeout(600)
+def test_full_forward_batch_8_equals_single_samples():
+    """The largest batch: 8 samples at 1024^2 (M = 34816 rows per GEMM) with their own latents, prompts,
+    sigmas and skip sets equal eight one-sample forwards bit for bit, so the batched launches, the
+    per-sample modulation offsets and the runs of samples that a skip set cuts all hold at full size.
+    Every kernel computes a row the same whatever rows run beside it; the attention's key split is the
+    one batch-dependent choice, and with 816 query tiles per sample on 512 slots none is made in runs
+    of 1, 3, 5, 6 or 8 samples, the only run lengths these skip sets leave in any block."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the run lengths are chosen for 256 compute units (512 attention slots)")
+    D, B = 3072, 8
+    log("full forward 1024^2, batch 8 vs single samples")
+    w = synth.torch_weights(synth.FULL, seed=0, device="cuda")
+    model = dt.MossDiT(dt.moss_dit_config_init(), w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(21)
+    lat = torch.randn((B, 32, 128, 128), generator=g, device="cuda", dtype=torch.float32)
+    text = torch.randn((B, T, D), generator=g, device="cuda", dtype=torch.float32)
+    sig = [0.05 + 0.12 * b for b in range(B)]
+    # block 0: samples 1, 2 skip (runs of 1 and 5); block 10: 1, 7 (1 and 5); block 22: 1 (1 and 6);
+    # block 41: 6 (6 and 1); every other block: one run of 8
+    skips = [0, (1 << 22) | (1 << 10) | 1, 1, 0, 0, 0, 1 << 41, 1 << 10]
+    vel = torch.full_like(lat, float("nan"))
+    model.moss_dit_forward(lat, text, sig, vel, skip_mask=skips)
+    torch.cuda.synchronize()
+    assert torch.isfinite(vel).all().item()
+    for b in range(B):
+        v1 = torch.full_like(lat[b:b + 1], float("nan"))
+        model.moss_dit_forward(lat[b:b + 1].contiguous(), text[b:b + 1].contiguous(), [sig[b]], v1,
+                               skip_mask=[skips[b]])
+        torch.cuda.synchronize()
+        assert torch.equal(vel[b:b + 1], v1), b
+    model.close()
 
 
 def _step_vs_forward(model, T, side, step, slg_scale, seed):
