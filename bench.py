@@ -218,6 +218,8 @@ def main():
                     help="timed text-refiner calls per prompt length (256 and 4096 tokens; 0 = skip)")
     ap.add_argument("--fp8-steps", type=int, default=5,
                     help="steps timed with the FP8 tier (MXFP8 block projections, a second handle; 0 = skip)")
+    ap.add_argument("--library-gemm-reps", type=int, default=10,
+                    help="timed torch.matmul (hipBLASLt) calls on the gate/up shape, for reference (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="MiB of a plain device-to-device copy run once before the steps (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -338,6 +340,34 @@ def main():
                 "frac": kernels[dom]["frac_hbm_peak"], "traffic": measured_traffic(dom), "kernel": dom,
                 "bytes_per_launch": by / launches, "avg_launch_ms": kernels[dom]["ms_per_step"] / launches}
     log(f"[bench] per-kernel: {json.dumps(kernels)}")
+
+    # ---- the vendor GEMM (torch.matmul -> hipBLASLt) on the gate/up shape, for reference: the same
+    # M x N x K bf16 product without the SwiGLU epilogue, both operands contiguous ----
+    library_gemm = None
+    if args.library_gemm_reps > 0:
+        M_gu = 2 * S
+        glib = torch.Generator(device="cuda")
+        glib.manual_seed(7)
+        ga = torch.randn((M_gu, D), generator=glib, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        gb = (0.02 * torch.randn((D, 2 * F), generator=glib, device="cuda", dtype=torch.float32)).to(torch.bfloat16)
+        gc = torch.matmul(ga, gb)
+        for _ in range(3):
+            torch.matmul(ga, gb, out=gc)
+        lg0, lg1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        lg0.record()
+        for _ in range(args.library_gemm_reps):
+            torch.matmul(ga, gb, out=gc)
+        lg1.record()
+        lg1.synchronize()
+        ms_lib = lg0.elapsed_time(lg1) / args.library_gemm_reps
+        fl_lib = 2.0 * M_gu * (2 * F) * D
+        library_gemm = {"shape": f"{M_gu} x {2 * F} x {D}", "ms": round(ms_lib, 4),
+                        "tflops": round(fl_lib / (ms_lib * 1e-3) / 1e12, 1),
+                        "frac_mfma_peak": round(fl_lib / (ms_lib * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "ours_gate_up_tflops": kernels.get("gemm_gate_up_swiglu", {}).get("tflops")}
+        log(f"[bench] vendor GEMM on the gate/up shape: {json.dumps(library_gemm)}")
+        del ga, gb, gc
 
     # ---- one full 50-step image (step 0 runs full CFG, steps 1..49 skip block 22 in the negative pass) ----
     s_image = None
@@ -549,6 +579,7 @@ def main():
         "step_tflop": round(step_flops / 1e12, 2),
         "roofline": roof,
         "kernels": kernels,
+        "library_gemm": library_gemm,
         "step_cache": cached,
         "guidance_variants": variants,
         "sampling_2048": big,
