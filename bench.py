@@ -219,7 +219,8 @@ def main():
     ap.add_argument("--fp8-steps", type=int, default=5,
                     help="steps timed with the FP8 tier (MXFP8 block projections, a second handle; 0 = skip)")
     ap.add_argument("--library-gemm-reps", type=int, default=10,
-                    help="timed torch.matmul (hipBLASLt) calls on the gate/up shape, for reference (0 = skip)")
+                    help="timed vendor calls for reference: torch.matmul (hipBLASLt) on the gate/up shape and "
+                         "torch SDPA (flash backend) on the attention shape (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="MiB of a plain device-to-device copy run once before the steps (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -368,6 +369,38 @@ def main():
                         "ours_gate_up_tflops": kernels.get("gemm_gate_up_swiglu", {}).get("tflops")}
         log(f"[bench] vendor GEMM on the gate/up shape: {json.dumps(library_gemm)}")
         del ga, gb, gc
+
+    # ---- the vendor attention (torch SDPA restricted to its flash backend, which raises rather than
+    # fall back to the math path) on the step's attention shape, for reference ----
+    library_attention = None
+    if args.library_gemm_reps > 0:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        Hh = D // 128
+        glib = torch.Generator(device="cuda")
+        glib.manual_seed(8)
+        qa, ka, va = (torch.randn((2, Hh, S, 128), generator=glib, device="cuda", dtype=torch.float32)
+                      .to(torch.bfloat16) for _ in range(3))
+        try:
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                for _ in range(3):
+                    torch.nn.functional.scaled_dot_product_attention(qa, ka, va)
+                la0, la1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                la0.record()
+                for _ in range(args.library_gemm_reps):
+                    torch.nn.functional.scaled_dot_product_attention(qa, ka, va)
+                la1.record()
+                la1.synchronize()
+            ms_la = la0.elapsed_time(la1) / args.library_gemm_reps
+            fl_la = attention_flops(2, S, D)
+            library_attention = {"shape": f"B 2, {Hh} heads x 128, S {S}", "backend": "flash", "ms": round(ms_la, 4),
+                                 "tflops": round(fl_la / (ms_la * 1e-3) / 1e12, 1),
+                                 "frac_mfma_peak": round(fl_la / (ms_la * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                 "ours_attention_tflops": kernels.get("attention", {}).get("tflops")}
+        except RuntimeError as e:
+            library_attention = {"backend": "flash", "unavailable": str(e)[:200]}
+        log(f"[bench] vendor attention on the step's shape: {json.dumps(library_attention)}")
+        del qa, ka, va
 
     # ---- one full 50-step image (step 0 runs full CFG, steps 1..49 skip block 22 in the negative pass) ----
     s_image = None
@@ -580,6 +613,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "library_gemm": library_gemm,
+        "library_attention": library_attention,
         "step_cache": cached,
         "guidance_variants": variants,
         "sampling_2048": big,
