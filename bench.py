@@ -219,8 +219,8 @@ def main():
     ap.add_argument("--fp8-steps", type=int, default=5,
                     help="steps timed with the FP8 tier (MXFP8 block projections, a second handle; 0 = skip)")
     ap.add_argument("--library-gemm-reps", type=int, default=10,
-                    help="timed vendor calls for reference: torch.matmul (hipBLASLt) on the gate/up shape and "
-                         "torch SDPA (flash backend) on the attention shape (0 = skip)")
+                    help="timed vendor calls for reference: torch.matmul (hipBLASLt) and torch._scaled_mm (FP8) "
+                         "on the gate/up shape, torch SDPA (flash backend) on the attention shape (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="MiB of a plain device-to-device copy run once before the steps (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -401,6 +401,36 @@ def main():
             library_attention = {"backend": "flash", "unavailable": str(e)[:200]}
         log(f"[bench] vendor attention on the step's shape: {json.dumps(library_attention)}")
         del qa, ka, va
+
+    # ---- the vendor FP8 GEMM (torch._scaled_mm -> hipBLASLt, E4M3 with one scale per tensor, bf16 out) on
+    # the gate/up shape, for reference next to the FP8 tier's MXFP8 GEMM (block scales, fused epilogue) ----
+    library_fp8_gemm = None
+    if args.library_gemm_reps > 0:
+        M_gu = 2 * S
+        glib = torch.Generator(device="cuda")
+        glib.manual_seed(9)
+        try:
+            fa = torch.randn((M_gu, D), generator=glib, device="cuda").to(torch.float8_e4m3fn)
+            fb = (0.05 * torch.randn((2 * F, D), generator=glib, device="cuda")).to(torch.float8_e4m3fn)
+            one = torch.ones((), device="cuda", dtype=torch.float32)
+            for _ in range(3):
+                torch._scaled_mm(fa, fb.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            lf0, lf1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            lf0.record()
+            for _ in range(args.library_gemm_reps):
+                torch._scaled_mm(fa, fb.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            lf1.record()
+            lf1.synchronize()
+            ms_lf = lf0.elapsed_time(lf1) / args.library_gemm_reps
+            fl_lf = 2.0 * M_gu * (2 * F) * D
+            library_fp8_gemm = {"shape": f"{M_gu} x {2 * F} x {D}", "format": "E4M3, one scale per tensor",
+                                "ms": round(ms_lf, 4), "tflops": round(fl_lf / (ms_lf * 1e-3) / 1e12, 1),
+                                "frac_fp8_peak": round(fl_lf / (ms_lf * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+            del fa, fb
+        except (RuntimeError, TypeError, AttributeError) as e:
+            library_fp8_gemm = {"unavailable": str(e)[:200]}
+        log(f"[bench] vendor FP8 GEMM on the gate/up shape: {json.dumps(library_fp8_gemm)}")
 
     # ---- one full 50-step image (step 0 runs full CFG, steps 1..49 skip block 22 in the negative pass) ----
     s_image = None
@@ -614,6 +644,7 @@ def main():
         "kernels": kernels,
         "library_gemm": library_gemm,
         "library_attention": library_attention,
+        "library_fp8_gemm": library_fp8_gemm,
         "step_cache": cached,
         "guidance_variants": variants,
         "sampling_2048": big,
