@@ -1126,7 +1126,7 @@ int moss_attention_q8(const void* qkv, void* out, int32_t batch, int32_t seq, in
 
 int moss_gemm_bf16(const void* A, const void* W, float* out, int32_t M, int32_t N, int32_t K, void* stream) {
   if (!A || !W || !out || M < 1 || N < 1 || K < 1 || K % 64 != 0 || N % 128 != 0) {
-    thread_error() = "moss_gemm_bf16: need non-NULL pointers, K % 64 == 0, N % 128 == 0";
+    thread_error() = "moss_gemm_bf16: need non-NULL pointers, M, N, K >= 1, K % 64 == 0, N % 128 == 0";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   const hipError_t e = launch_gemm(gemm_args((const uint16_t*)A, (const uint16_t*)W, M, N, K, out, N), EPI_F32,
@@ -1143,7 +1143,7 @@ int moss_mx_quantize(const void* x, int32_t rows, int32_t K, void* codes, void* 
   if (!x || !codes || !scales || rows < 1 || K < 256 || K % 256 != 0 || ld_scale < rows ||
       (reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(codes) & 15) ||
       (reinterpret_cast<uintptr_t>(scales) & 3)) {
-    thread_error() = "moss_mx_quantize: need non-NULL 16-byte aligned x and codes, K % 256 == 0, ld_scale >= rows";
+    thread_error() = "moss_mx_quantize: need non-NULL 16-byte aligned x and codes, rows >= 1, K % 256 == 0, ld_scale >= rows";
     return MOSS_ERR_INVALID_ARGUMENT;
   }
   const hipError_t e = launch_mx_quant((const uint16_t*)x, K, rows, K, (uint8_t*)codes, (uint8_t*)scales, ld_scale,
@@ -1159,7 +1159,7 @@ int moss_gemm_mxfp8(const void* A, const void* A_scales, int64_t lds_a, const vo
                     int64_t lds_w, float* out, int32_t M, int32_t N, int32_t K, void* stream) {
   if (!A || !A_scales || !W || !W_scales || !out || M < 1 || N < 1 || K < 1 || N % 256 != 0 || K % 256 != 0 ||
       lds_a % 256 != 0 || lds_a < (M + 255) / 256 * 256 || lds_w % 256 != 0 || lds_w < N) {
-    thread_error() = "moss_gemm_mxfp8: need non-NULL pointers, N % 256 == 0, K % 256 == 0, lds_a >= M rounded up "
+    thread_error() = "moss_gemm_mxfp8: need non-NULL pointers, M, N, K >= 1, N % 256 == 0, K % 256 == 0, lds_a >= M rounded up "
                      "to 256, lds_w >= N, both multiples of 256";
     return MOSS_ERR_INVALID_ARGUMENT;
   }

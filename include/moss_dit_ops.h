@@ -89,7 +89,7 @@ int moss_attention_q8(const void* qkv, void* out, int32_t batch, int32_t seq, in
                       int64_t ws_bytes, void* stream);
 
 /* bf16 GEMM out = A W^T with an fp32 output (device A bf16 [M, K], W bf16 [N, K], out fp32 [M, N]);
- * K % 64 == 0, N % 128 == 0. */
+ * M, N, K >= 1, K % 64 == 0, N % 128 == 0; other values return MOSS_ERR_INVALID_ARGUMENT before any device work. */
 int moss_gemm_bf16(const void* A, const void* W, float* out, int32_t M, int32_t N, int32_t K, void* stream);
 
 /* Per-kernel-class timing with HIP events recorded on the call's stream around every launch of the
@@ -120,8 +120,9 @@ int moss_mx_quantize(const void* x, int32_t rows, int32_t K, void* codes, void* 
 
 /* MXFP8 GEMM with an fp32 output: out[m, n] = sum_k a(m, k) w(n, k), a and w the MXFP8 values of A
  * (codes [M, K], scale words with ld = lds_a) and W (codes [N, K], scale words with ld = lds_w), fp32
- * accumulation. N % 256 == 0, K % 256 == 0, lds_a >= M rounded up to 256 (the scale words of rows
- * M .. that bound are read, their products discarded), lds_w >= N, both multiples of 256. */
+ * accumulation. M, N, K >= 1, N % 256 == 0, K % 256 == 0, lds_a >= M rounded up to 256 (the scale
+ * words of rows M .. that bound are read, their products discarded), lds_w >= N, both multiples of
+ * 256; other values return MOSS_ERR_INVALID_ARGUMENT before any device work. */
 int moss_gemm_mxfp8(const void* A, const void* A_scales, int64_t lds_a, const void* W, const void* W_scales,
                     int64_t lds_w, float* out, int32_t M, int32_t N, int32_t K, void* stream);
 

@@ -228,3 +228,62 @@ def test_handleless_errors_set_thread_message():
     assert "config" in dt.moss_dit_last_error()
     assert dt._lib.moss_cfg_euler(None, None, None, 4, 3.0, 1.0, 0.5, None) == 1
     assert "moss_cfg_euler" in dt.moss_dit_last_error()
+
+
+# Placeholder device addresses (256-byte aligned, never dereferenced: every case below is refused on the
+# host before any device work).
+_P = 0x100000
+
+
+@pytest.mark.parametrize("name,args,needle", [
+    # exact attention (and its no-allocation twin): empty batch, empty sequence, no heads, more text
+    # rows than rows, NULL operands, image rows that are not whole rows of the RoPE grid
+    ("moss_attention", (_P, _P, 0, 128, 2, 0, 1, 0, None), "batch, seq and heads >= 1"),
+    ("moss_attention", (_P, _P, 1, 0, 2, 0, 1, 0, None), "batch, seq and heads >= 1"),
+    ("moss_attention", (_P, _P, 1, 128, 0, 0, 1, 0, None), "batch, seq and heads >= 1"),
+    ("moss_attention", (_P, _P, 1, 128, 2, 129, 1, 0, None), "text_len <= seq"),
+    ("moss_attention", (None, _P, 1, 128, 2, 0, 1, 0, None), "need qkv and out"),
+    ("moss_attention", (_P, None, 1, 128, 2, 0, 1, 0, None), "need qkv and out"),
+    ("moss_attention", (_P, _P, 1, 100, 2, 10, 7, 1, None), "grid"),
+    ("moss_attention_noalloc", (_P, _P, 1, 0, 2, 0, 1, 0, None), "batch, seq and heads >= 1"),
+    ("moss_attention_noalloc", (_P, _P, 1, 100, 2, 10, 7, 1, None), "grid"),
+    # 8-bit attention: empty shapes, a workspace one byte short or off its 256-byte alignment
+    ("moss_attention_q8", (_P, _P, 0, 128, 2, _P, 1 << 30, None), "bad arguments"),
+    ("moss_attention_q8", (_P, _P, 1, 128, 2, None, 1 << 30, None), "bad arguments"),
+    ("moss_attention_q8", (_P, _P, 1, 128, 2, _P, "short", None), "workspace"),
+    ("moss_attention_q8", (_P, _P, 1, 128, 2, _P + 16, "full", None), "workspace"),
+    # bf16 GEMM: empty M, N off the 128-wide tiles, K off the 64-deep k-tiles, NULL output
+    ("moss_gemm_bf16", (_P, _P, _P, 0, 128, 64, None), "M, N, K >= 1"),
+    ("moss_gemm_bf16", (_P, _P, _P, 16, 100, 64, None), "N % 128"),
+    ("moss_gemm_bf16", (_P, _P, _P, 16, 128, 48, None), "K % 64"),
+    ("moss_gemm_bf16", (_P, _P, None, 16, 128, 64, None), "non-NULL"),
+    # MXFP8 quantizer: no rows, K off the 256-element groups, scale rows fewer than rows, misaligned x
+    ("moss_mx_quantize", (_P, 0, 256, _P, _P, 1, None), "rows >= 1"),
+    ("moss_mx_quantize", (_P, 4, 192, _P, _P, 4, None), "K % 256"),
+    ("moss_mx_quantize", (_P, 4, 256, _P, _P, 3, None), "ld_scale >= rows"),
+    ("moss_mx_quantize", (_P + 8, 4, 256, _P, _P, 4, None), "16-byte aligned"),
+    # MXFP8 GEMM: empty M, N off 256, scale-word strides too short or off 256
+    ("moss_gemm_mxfp8", (_P, _P, 256, _P, _P, 256, _P, 0, 256, 256, None), "M, N, K >= 1"),
+    ("moss_gemm_mxfp8", (_P, _P, 256, _P, _P, 256, _P, 16, 200, 256, None), "N % 256"),
+    ("moss_gemm_mxfp8", (_P, _P, 256, _P, _P, 256, _P, 300, 256, 256, None), "lds_a >= M rounded up"),
+    ("moss_gemm_mxfp8", (_P, _P, 512, _P, _P, 128, _P, 300, 256, 256, None), "lds_w >= N"),
+    ("moss_gemm_mxfp8", (_P, _P, 300, _P, _P, 256, _P, 16, 256, 256, None), "multiples of 256"),
+])
+def test_ops_refuse_bad_arguments_on_the_host(name, args, needle):
+    """The standalone kernel entry points refuse what their declarations rule out -- empty and ragged
+    sizes, NULL pointers, short or misaligned workspaces -- with MOSS_ERR_INVALID_ARGUMENT and a message
+    naming the rule, before any device work (so this runs without a GPU)."""
+    if name == "moss_attention_q8":
+        ws = int(dt._lib.moss_attention_q8_workspace(1, 128, 2))
+        assert ws > 0
+        args = tuple(ws - 1 if a == "short" else ws if a == "full" else a for a in args)
+    st = getattr(dt._lib, name)(*args)
+    assert st == 1, (name, args, st)
+    msg = dt.moss_dit_last_error()
+    assert name in msg and needle in msg, msg
+
+
+def test_q8_workspace_of_empty_shapes_is_zero():
+    for b, s, h in [(0, 128, 2), (1, 0, 2), (1, 128, 0), (-1, 128, 2)]:
+        assert dt._lib.moss_attention_q8_workspace(b, s, h) == 0
+    assert dt._lib.moss_attention_q8_workspace(1, 128, 2) > 0
