@@ -47,10 +47,14 @@ def block_model(mod_scale, seed=3):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("mod_scale,T,GH,GW", [(1.0, T, GH, GW), (50.0, T, GH, GW), (50.0, 4096, 128, 128)])
+@pytest.mark.parametrize("mod_scale,T,GH,GW", [(1.0, T, GH, GW), (50.0, T, GH, GW), (50.0, 4096, 128, 128),
+                                               (50.0, 256, 64, 128)])
 def test_full_block_sampled_rows(mod_scale, T, GH, GW):
     """One joint block at full width, stage by stage and whole. The 2048^2 case (4096 text + 16384
-    image tokens, S = 20480, M = 40960 rows per GEMM) is the sampling benchmark's block shape."""
+    image tokens, S = 20480, M = 40960 rows per GEMM) is the sampling benchmark's block shape; the
+    1024 x 2048 case (a 64 x 128 patch grid, S = 8448) puts the rotary rows and columns on a
+    non-square grid at full width, with the attention's key-split tail on (2 x 24 x 66 query tiles
+    leave 96 for the last round)."""
     S = T + GH * GW
     log(f"full block: D=3072 F=8192 H=24, B=2, S={S}, mod_scale={mod_scale}")
     model, w, ocfg = block_model(mod_scale)
