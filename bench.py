@@ -10,7 +10,7 @@ twice", MOSS-Image: specs, settings, VRAM and text rendering tested -- "Recommen
 
 Prints ONE JSON line on stdout. Progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--image-steps 50] [--cpu-baseline-blocks 1]
+    python bench.py [--steps K] [--warmup W] [--image-steps 50] [--cpu-baseline-blocks 3]
 """
 from __future__ import annotations
 
@@ -202,7 +202,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--image-steps", type=int, default=50, help="steps of the full-image timing (0 = skip)")
-    ap.add_argument("--cpu-baseline-blocks", type=int, default=1, help="oracle blocks for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-baseline-blocks", type=int, default=3,
+                    help="oracle blocks of one sample for cpu_baseline, about 4 s each on 16 threads (0 = skip)")
     ap.add_argument("--profile-steps", type=int, default=3, help="steps of the per-kernel event pass")
     ap.add_argument("--text-len", type=int, default=256)
     ap.add_argument("--latent", type=int, default=128, help="latent side (1024 px / 8)")
