@@ -375,13 +375,13 @@ def main():
     # fall back to the math path) on the step's attention shape, for reference ----
     library_attention = None
     if args.library_gemm_reps > 0:
-        from torch.nn.attention import SDPBackend, sdpa_kernel
         Hh = D // 128
         glib = torch.Generator(device="cuda")
         glib.manual_seed(8)
         qa, ka, va = (torch.randn((2, Hh, S, 128), generator=glib, device="cuda", dtype=torch.float32)
                       .to(torch.bfloat16) for _ in range(3))
         try:
+            from torch.nn.attention import SDPBackend, sdpa_kernel
             with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
                 for _ in range(3):
                     torch.nn.functional.scaled_dot_product_attention(qa, ka, va)
@@ -398,7 +398,7 @@ def main():
                                  "tflops": round(fl_la / (ms_la * 1e-3) / 1e12, 1),
                                  "frac_mfma_peak": round(fl_la / (ms_la * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                  "ours_attention_tflops": kernels.get("attention", {}).get("tflops")}
-        except RuntimeError as e:
+        except (RuntimeError, ImportError) as e:
             library_attention = {"backend": "flash", "unavailable": str(e)[:200]}
         log(f"[bench] vendor attention on the step's shape: {json.dumps(library_attention)}")
         del qa, ka, va
