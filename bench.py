@@ -86,9 +86,10 @@ def measured_traffic(kernel_class):
 
 
 class ClockSampler:
-    """Shader clock of the GPU while it works: a thread reads the current frequency from the amdgpu kernel driver's
-    DPM table (sysfs pp_dpm_sclk of the card whose PCI address is torch's device 0; the line marked
-    '*') every `period` seconds between start() and stop(). Nothing is read from the GPU itself."""
+    """Shader clock of the GPU while it works: a thread reads the current frequency from the amdgpu
+    kernel driver's DPM table (sysfs pp_dpm_sclk of the card whose PCI address is torch's device 0; the
+    line marked '*') every `period` seconds between start() and stop(). Nothing is read from the GPU
+    itself."""
 
     def __init__(self, period=0.05):
         self.period = period
