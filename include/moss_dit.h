@@ -13,8 +13,8 @@
  * `hidden` (standing in for the text refiner's output) and latents of `latent_channels` channels.
  *
  * Conventions (modelled on the C API rules of the MossInfer integration guide):
- *   - Fill every struct with its *_init(&s, sizeof s) function before setting fields. struct_size
- *     must equal the size this header declares, else the call returns MOSS_ERR_ABI_MISMATCH.
+ *   - Each struct is prepared by its *_init(&s, sizeof s) call, and only then are its fields set.
+ *     A struct_size other than this header's size makes the call return MOSS_ERR_ABI_MISMATCH.
  *   - Device pointers are HIP device memory of the device current at moss_dit_create, allocated and
  *     owned by the caller (e.g. torch tensors); the library only borrows them for the call. The
  *     handle owns a copy of the weights and its workspace.
@@ -60,8 +60,9 @@ const char* moss_dit_last_error(const moss_dit* h);
  * Model configuration. Defaults (moss_dit_config_init) are MOSS-Image's: 42 layers, hidden 3072,
  * 24 heads of 128, FFN 8192, 32 latent channels, 2x2 patches ("Architecture and specs"), and the
  * readings where the pages are silent: time-embedding width 256, RoPE theta 1e4, LayerNorm eps 1e-6,
- * flow multiplier 1000 (t = 1000 * sigma), no QK-norm; for the text refiner (the text encoder's
- * final-layer states go through a projection and two text-only blocks, "Architecture and specs"):
+ * flow multiplier 1000 (t = 1000 * sigma), no QK-norm; for the text refiner (a projection and two
+ * blocks over the text rows alone, applied to the text encoder's last hidden states, "Architecture and
+ * specs"):
  * encoder state width 4096 and 2 refiner blocks.
  * Supported: head_dim == 128, hidden == num_heads * 128, hidden % 256 == 0, hidden <= 4096,
  * ffn_hidden % 64 == 0, temb_dim == 256, patch == 2, 1 <= num_layers <= 64, qk_norm == 0,
@@ -152,9 +153,9 @@ int moss_validate_forward_args(const moss_dit_config* cfg, const moss_forward_ar
 
 /* ---------------------------------------------------------------------------------------------
  * Text refiner: out = refine(enc), run once per prompt before the denoising loop; `out` is what
- * moss_dit_forward / moss_sample_step take as text states. The text encoder's final-layer states go
- * through a projection and two text-only blocks ("MOSS-Image: specs, settings, VRAM and text rendering
- * tested", "Architecture and specs"). Readings (the pages say no more): the projection has no bias;
+ * moss_dit_forward / moss_sample_step take as text states: a projection followed by two blocks over
+ * the text rows alone, applied to the text encoder's last hidden states ("MOSS-Image: specs, settings,
+ * VRAM and text rendering tested", "Architecture and specs"). Readings (the pages say no more): the projection has no bias;
  * the text-only blocks are joint blocks of the same widths run on the text rows alone, without
  * timestep modulation (unmodulated LayerNorm, gates 1: they depend on the prompt only) and without
  * RoPE. bf16 storage as in the DiT; the result is written as fp32 (exact bf16 values).
@@ -178,17 +179,18 @@ int moss_sigmas(int32_t num_steps, float shift, float* sigmas /* host [num_steps
  *   - The conditional pass always runs: v_c.
  *   - The negative (unconditional) pass runs when cfg_scale > 1 and step < cfg_truncation *
  *     num_steps, skipping uncond_skip_layers when slg_start <= step/num_steps <= slg_stop
- *     ("MOSS-Image" SGLang cookbook, "3. Guidance and precision"; CFG truncation drops the negative
- *     branch from step X*steps on: MossInfer integration guide, feature table "Lossy accelerators").
+ *     ("MOSS-Image" SGLang cookbook, "3. Guidance and precision"; CFG truncation leaves the negative
+ *     branch out of the last (1 - X) of the steps: MossInfer integration guide, feature table "Lossy
+ *     accelerators").
  *     Then v = v_u + cfg_scale * (v_c - v_u), else v = v_c.
  *   - Three-pass skip-layer guidance (slg_scale > 0; the cookbook's "adds a skipped conditional
  *     prediction"): inside the same window, a third pass runs the conditional input skipping the
  *     same uncond_skip_layers, v_s, and v += slg_scale * (v_c - v_s). The pages give no formula; this
  *     is the skip-layer guidance form. slg_scale = 0 (default) is the two-pass recipe.
  *   - Step cache (step_cache = 1, off by default; lossy: it changes the image): the First-Block Cache
- *     of the MossInfer integration guide ("Lossy accelerators"): blocks 1.. are reused from the last
- *     full call while block 0's output changed by less than step_cache_threshold (<= 0: 0.02, the
- *     base model's default). Readings: the change is sum|r - r_prev| / sum|r_prev| with r = the
+ *     of the MossInfer integration guide ("Lossy accelerators"): as long as block 0's output moves
+ *     less than step_cache_threshold between calls (<= 0: 0.02, the base model's default), blocks 1..
+ *     are taken from the last call that ran them. Readings: the change is sum|r - r_prev| / sum|r_prev| with r = the
  *     residual stream after block 0 minus the one before it (all rows of the call) and r_prev the same
  *     at the last full call; a reused call takes the stream after the last block as bf16(x after block
  *     0 + the difference of those two streams at the last full call). A call whose rows (batch, shapes,

@@ -461,8 +461,9 @@ def block(x: np.ndarray, m: np.ndarray, W: Dict, l: int, cfg: Config, text_len: 
 # ----------------------------------------------------------------------------------------------
 
 def text_refine(enc: np.ndarray, W: Dict, cfg: Config, mirror: bool = False) -> np.ndarray:
-    """The step before the DiT on the text side ([WP] "Architecture and specs": the encoder's
-    final-layer states go through a projection and two text-only blocks). enc [T, text_dim] -> [T, D].
+    """The step before the DiT on the text side ([WP] "Architecture and specs": a projection and two
+    blocks over the text rows alone turn the encoder's last hidden states into the DiT's text rows).
+    enc [T, text_dim] -> [T, D].
 
     Readings (the pages give no more): the projection is a linear map text_dim -> hidden without bias
     (no linear mentions one); the text-only blocks are joint blocks of the same widths applied to the
@@ -551,8 +552,8 @@ def euler_step(x: np.ndarray, v: np.ndarray, sigma: float, sigma_next: float) ->
 
 def negative_pass_runs(step: int, num_steps: int, cfg_scale: float, cfg_truncation: float = 1.0) -> bool:
     """Whether the negative (unconditional) branch runs at this step. CFG 1 runs none ([IV]
-    "Generation settings"). CFG truncation X in [0, 1] (default 1 = off) drops the negative branch
-    from step X*steps on ([MI] feature table, "Lossy accelerators", and its list of opt-in
+    "Generation settings"). CFG truncation X in [0, 1] (default 1 = off): the last (1 - X) of the steps
+    run without the negative branch ([MI] feature table, "Lossy accelerators", and its list of opt-in
     accelerators). Reading: with steps numbered from 0, the branch runs iff step < X*steps."""
     return cfg_scale > 1.0 and step < cfg_truncation * num_steps
 
@@ -629,9 +630,9 @@ class StepCache:
 
 def forward_cached(latents: np.ndarray, text: np.ndarray, sigma: Sequence[float], W: Dict, cfg: Config,
                    skip: Sequence[Set[int]], cache: StepCache, threshold: float, mirror: bool = False):
-    """DiT velocity with the step cache ([MI] opt-in accelerators: the step cache reuses DiT blocks
-    1..41 from the last full call while block 0's output changed by less than the threshold, default
-    0.02 on the base model). Readings: the change is the First-Block Cache measure of block 0's
+    """DiT velocity with the step cache ([MI] opt-in accelerators: as long as block 0's output moves
+    less than a threshold between calls, 0.02 for the base model, blocks 1..41 are taken from the last
+    call that ran them). Readings: the change is the First-Block Cache measure of block 0's
     residual r = x_after_block0 - x_before (first_block_change), one decision per call over all its
     rows; a reused call sets the stream after the last block to x_after_block0 + rest, rest = the
     difference of the same two streams at the last full call (a bf16 rounding, the residual being

@@ -67,8 +67,9 @@ def test_sigmas_endpoints_monotone_and_shift1_linear():
 
 
 def test_slg_window_first_step_full_cfg():
-    # "skips unconditional layer 22 inside the slg_start=0.01, slg_stop=1.0 window. It leaves the first
-    # step at full CFG"; "set slg_start=0.0 ... for the start-at-zero behavior" (SGLang cookbook, 3).
+    # The default window (0.01 to 1.0) makes the unconditional pass skip block 22 on every step but the
+    # first, which runs at full CFG; a window starting at 0.0 skips it from step 0 on (SGLang cookbook
+    # for MOSS-Image, section 3).
     g = golden()["defaults"]
     N = g["num_steps"]
     active = [i for i in range(N) if O.slg_active(i, N, g["slg_start"], g["slg_stop"])]
@@ -472,8 +473,9 @@ def test_sample_step_guidance_paths():
 
 
 def test_cfg_truncation_boundary_table():
-    # "drops the negative branch from step X * steps on" (MossInfer guide, lossy accelerators); steps
-    # are numbered from 0, X = 1 (the default) is off, and CFG 1 runs no negative branch at all.
+    # CFG truncation X leaves the negative branch out of the last (1 - X) of the steps (MossInfer
+    # guide, lossy accelerators); steps are numbered from 0, X = 1 (the default) is off, and CFG 1 runs
+    # no negative branch at all.
     runs = lambda X, N, cfg=3.0: [i for i in range(N) if O.negative_pass_runs(i, N, cfg, X)]
     assert runs(1.0, 50) == list(range(50))
     assert runs(0.0, 50) == []
